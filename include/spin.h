@@ -1,0 +1,243 @@
+/*
+ * spin.h -- C ABI of the SPIN (Shadow Predictive Indexer) decode-round library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * SPIN predicts which KV blocks matter before the sparse-attention indexer
+ * runs, so the indexer scores only the kept blocks (arXiv 2610.09025).  One
+ * decode round for one layer is
+ *
+ *     spin_predict_blocks  -> kept block list (predicted + explored)
+ *     spin_indexer_topk    -> indexer scores of the kept slots, per-row top-k
+ *     spin_update          -> EMA update from the observed slots (R == 1)
+ *     spin_mtp_replay      -> prefix-valid EMA replay once acceptance is known
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].
+ *   - Every call that takes a hipStream_t enqueues its kernels on that stream
+ *     and returns without synchronising.  No call allocates device memory; the
+ *     caller owns every buffer, including the state buffer.
+ *   - A state is used from one stream at a time: calls that overlap on one
+ *     state race on its workspace.
+ *   - Return value: SPIN_OK (0) or a negative SPIN_E* code; no C++ exception
+ *     crosses this boundary.  Arguments that live in host memory are checked
+ *     before anything is enqueued.  Values that live in device arrays (slot,
+ *     qpos, kept lists, block tables, accepted counts) cannot be checked on the
+ *     host without a synchronisation: the kernels check them, skip the
+ *     offending request or entry without touching memory out of bounds, and
+ *     set a bit in the state's device error word (spin_state_layout().error).
+ *   - Block size is 64 slots; slot i belongs to block i / 64.  Positions are
+ *     0-based; a query row at position q attends to slots 0..q (its own key
+ *     is in the cache before the indexer runs).
+ */
+#ifndef SPIN_H
+#define SPIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SPIN_OK = 0,
+  SPIN_EINVAL = -1,       /* null pointer, bad size, layer/rows out of range */
+  SPIN_EUNSUPPORTED = -2, /* valid configuration this library does not build */
+  SPIN_EHIP = -3,         /* a HIP launch failed; see spin_status_string */
+  SPIN_ESTATE = -4        /* state buffer too small or config mismatch */
+};
+
+/* Bits of the device error word. */
+enum {
+  SPIN_ERR_QPOS = 1,      /* qpos < 0 or qpos + R - 1 >= max_ctx, or too many blocks */
+  SPIN_ERR_SLOT = 2,      /* slot outside [0, max_slots) */
+  SPIN_ERR_KEPT = 4,      /* kept_count or a kept block index out of range */
+  SPIN_ERR_PAGE = 8,      /* block_table entry outside [0, pool_pages) */
+  SPIN_ERR_ACCEPT = 16    /* accepted outside [0, R-1] */
+};
+
+/* [host] Static configuration of one state buffer. */
+typedef struct spin_config {
+  int32_t num_layers;   /* layers, each with its own V/D state */
+  int32_t max_slots;    /* concurrent requests (state slots) */
+  int32_t max_ctx;      /* positions per request: qpos + R - 1 < max_ctx */
+  int32_t block_size;   /* must be 64 */
+  int32_t heads;        /* indexer heads H_I: 64 */
+  int32_t head_dim;     /* indexer head dim d_I: 128 */
+  int32_t topk;         /* K of the per-row top-k, 1..8192 */
+  int32_t max_rows;     /* 1 + MTP draft length, 1..4 */
+  int32_t warmup_steps; /* leading all-keep rounds of each (layer, request) */
+  int32_t explore_bp;   /* exploration share of the kept budget, basis points */
+  float alpha;          /* EMA history weight; beta = fp32(1 - alpha) */
+  uint32_t reserved;    /* must be 0 */
+  uint64_t seed;        /* Philox key word 0 for exploration */
+} spin_config;
+
+/* [host] One call's batch.  The [B][max_blocks] arrays of a call (block
+ * tables, kept lists, flags) all use the row stride max_blocks, which must be
+ * at least ceil((qpos + R) / 64) for every request and at most
+ * ceil(max_ctx / 64). */
+typedef struct spin_batch {
+  int32_t B;              /* requests in this call, 1..max_slots */
+  int32_t R;              /* query rows per request, 1..max_rows */
+  int32_t max_blocks;     /* row stride of the [B][max_blocks] arrays */
+  int32_t reserved;       /* must be 0 */
+  const int32_t* slot;    /* device [B]: state slot of each request */
+  const int32_t* qpos;    /* device [B]: position of row 0; row r is at qpos + r */
+} spin_batch;
+
+/* Byte offsets of the regions of a state buffer (for checkpoints, tests and
+ * debugging).  Arrays are dense, row-major, fp32 unless noted:
+ *   V   [num_layers][max_slots][max_ctx]     vertical EMA per slot (-inf = never observed)
+ *   D   [num_layers][max_slots][max_ctx]     diagonal EMA per relative offset q - i
+ *   VB  [num_layers][max_slots][max_blocks]  per-block max of V (a derived cache)
+ *   step [num_layers][max_slots] int32       completed rounds of each (layer, slot)
+ *   request_id [max_slots] uint64            Philox counter word 2
+ *   error int32                              SPIN_ERR_* bits, sticky until spin_state_init
+ *   q8  [max_slots][max_rows][heads][head_dim] uint8   workspace: e4m3fn query codes
+ *   wq  [max_slots][max_rows][heads]          workspace: w * 2^e
+ *   qexp [max_slots][max_rows][heads] int32   workspace: query exponents e
+ *   bscore [max_slots][max_rows][max_blocks]  workspace: block scores S
+ *   ukey [max_slots][max_blocks] uint64       workspace: exploration keys
+ * Workspace arrays are indexed by batch position b, not by slot. */
+typedef struct spin_state_layout {
+  size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, total;
+  int32_t max_blocks;     /* ceil(max_ctx / 64) */
+  int32_t reserved;
+} spin_state_layout;
+
+typedef struct spin_state spin_state; /* opaque host handle */
+
+/* Size in bytes of the state buffer for `cfg`.  Returns SPIN_EINVAL or
+ * SPIN_EUNSUPPORTED for a configuration the library does not accept. */
+int spin_state_bytes(const spin_config* cfg, size_t* bytes);
+
+/* [host] Region offsets of a state buffer for `cfg`. */
+int spin_state_layout_of(const spin_config* cfg, spin_state_layout* out);
+
+/* Bind a caller-owned device buffer of at least spin_state_bytes() bytes
+ * (256-byte aligned) and enqueue its initialisation: V, D, VB := -inf (never
+ * observed), step := 0, request_id := 0, error := 0.  *out receives a host
+ * handle; the buffer must outlive it.  READING of the pages (SPIN's AI Radio
+ * episode, "Title and authors" segment; ai4snews digest, "arXiv深度剖析"):
+ * V is one EMA per slot, D one EMA per relative offset; the pages leave the
+ * initial value open, and -inf marks "never observed". */
+int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes,
+                    hipStream_t stream, spin_state** out);
+
+/* [host] Free the host handle only; the caller frees state_mem. */
+int spin_state_destroy(spin_state* st);
+
+/* Start new requests in `n` slots: for every layer V, D, VB := -inf,
+ * step := 0, and request_id[slots[k]] := request_ids[k].
+ * slots: device int32 [n]; request_ids: device uint64 [n]. */
+int spin_reset_slots(spin_state* st, int n, const int32_t* slots,
+                     const uint64_t* request_ids, hipStream_t stream);
+
+/* Predict and select the kept KV blocks of one layer (AI Radio episode,
+ * "Title and authors": z_{t,i} = max(V_i, D_{q_t - i}), S_{t,j} = max of z over
+ * block j; "The paper's summary": a share gamma of the block budget is random
+ * exploration; ai4snews digest, "arXiv深度剖析": block-level sparsity, and for
+ * MTP the union of every verification row's mask).
+ * For each request and row r (position q_r = qpos + r, N_r = ceil((q_r+1)/64)
+ * blocks): K_b = ceil(keep_bp * N_r / 10^4), n_exp = floor(explore_bp * K_b /
+ * 10^4); the K_b - n_exp blocks with the largest S (ties: lower block) are
+ * predicted; among the other blocks the n_exp with the smallest Philox4x64-10
+ * word (key (seed, layer), counter (j/4, step, request_id, 0), word j%4; ties:
+ * lower block) are explored.  A row keeps every block when the (layer, slot)
+ * is within warmup_steps, keep_bp >= 10000 or K_b >= N_r.  The kept set is the
+ * union over rows.
+ * keep_bp: 0..10000 (= 10000 - target sparsity in basis points).
+ * Outputs: kept_blocks int32 [B][max_blocks] ascending block indices
+ * (entries past kept_count are left unspecified), kept_count int32 [B],
+ * block_flags uint8 [B][max_blocks] (0 skipped, 1 predicted by some row,
+ * 2 explored only; 0 for blocks past the last row's context). */
+int spin_predict_blocks(spin_state* st, int layer, const spin_batch* batch, int keep_bp,
+                        int32_t* kept_blocks, int32_t* kept_count, uint8_t* block_flags,
+                        hipStream_t stream);
+
+/* Quantise the queries into the state's workspace: per (request, row, head),
+ * e = the smallest integer with max|q| * 2^-e <= 448 (0 if q == 0), codes =
+ * round-to-nearest-even e4m3fn of q * 2^-e, and wq = w * 2^e, so the indexer
+ * score keeps its value (ReLU commutes with positive scales).
+ * q_bf16: bf16 [B][R][heads][head_dim]; w: fp32 [B][R][heads]. */
+int spin_quantize_q(spin_state* st, const spin_batch* batch, const void* q_bf16,
+                    const float* w, hipStream_t stream);
+
+/* Indexer on the kept blocks only, from the queries last quantised into the
+ * workspace by spin_quantize_q for this batch (v1 abstract: the indexer scores
+ * the KV cache each step; SPIN restricts it to the predicted blocks).  For
+ * kept block j (page p = block_table[b][j]) and slot i = 64 j + t <= q_r:
+ *   score_r(i) = k_scale[p] * sum_h wq[r][h] * max(0, sum_d q8[r][h][d] * k8[p][t][d])
+ * computed with fp8 e4m3fn MFMA and fp32 accumulation.
+ * k_pool: e4m3fn codes [pool_pages][64][head_dim]; k_scale: fp32 [pool_pages];
+ * block_table: int32 [B][max_blocks] (logical block -> page).
+ * scores: fp32 [B][R][max_blocks * 64] in kept order: element k*64 + t is slot
+ * 64*kept_blocks[b][k] + t; slots after the row's position get -inf. */
+int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* k_pool,
+                        const float* k_scale, int64_t pool_pages, const int32_t* block_table,
+                        const int32_t* kept_blocks, const int32_t* kept_count, float* scores,
+                        hipStream_t stream);
+
+/* Per-row top-k over kept-order scores (v1 abstract: a fixed top-k goes to
+ * core attention): the `topk` kept slots i <= q_r with the largest scores,
+ * ties to the lower slot, written ascending to topk_out int32 [B][R][topk],
+ * padded with -1.  -0.0 ranks equal to +0.0.  scores as spin_indexer_scores
+ * writes them (only slots <= q_r are read as candidates). */
+int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
+                     const int32_t* kept_blocks, const int32_t* kept_count, int32_t* topk_out,
+                     hipStream_t stream);
+
+/* spin_quantize_q + spin_indexer_scores + spin_topk_scores with the state's
+ * top-k K.  `scores` must stay alive until spin_update / spin_mtp_replay
+ * (the deferred update of the ai4snews digest, "arXiv深度剖析"). */
+int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf16,
+                      const float* w, const uint8_t* k_pool, const float* k_scale,
+                      int64_t pool_pages, const int32_t* block_table,
+                      const int32_t* kept_blocks, const int32_t* kept_count, float* scores,
+                      int32_t* topk_out, hipStream_t stream);
+
+/* EMA update from the observed slots of row 0 (AI Radio episode, "The paper's
+ * summary": blocks that were skipped get no update).  For every kept slot
+ * i <= qpos: V_i and D_{qpos - i} := s if never observed, else
+ * alpha * x + beta * s, beta = fp32(1 - alpha); VB of the kept blocks is
+ * refreshed and the (layer, slot) round counter is advanced.  Rows r > 0 of
+ * the scores are ignored (with R > 1 this is the row-0 update policy). */
+int spin_update(spin_state* st, int layer, const spin_batch* batch, const float* scores,
+                const int32_t* kept_blocks, const int32_t* kept_count, hipStream_t stream);
+
+/* Prefix-valid MTP replay (ai4snews digest, "arXiv深度剖析"; v1 Table 7,
+ * row-local union + prefix-valid update): with a = accepted[b] in 0..R-1,
+ * apply the update of rows 0..a in row order, row r observing the kept slots
+ * i <= qpos + r with offsets qpos + r - i; rows above a change nothing.  Then
+ * the round counter is advanced once.  accepted: device int32 [B]. */
+int spin_mtp_replay(spin_state* st, int layer, const spin_batch* batch, const int32_t* accepted,
+                    const float* scores, const int32_t* kept_blocks, const int32_t* kept_count,
+                    hipStream_t stream);
+
+/* Selection fidelity (v1, Table 5 caption: mean and p99 miss over eligible
+ * sparse decode rows): miss[b][r] = (number of entries of the all-keep top-k
+ * full_topk[b][r][:] that lie in blocks with block_flags == 0) / (number of
+ * non-negative entries), 0 when there are none.  full_topk: int32
+ * [B][R][topk]; block_flags: uint8 [B][max_blocks]; miss: fp32 [B][R]. */
+int spin_measure_miss(const spin_batch* batch, int topk, const int32_t* full_topk,
+                      const uint8_t* block_flags, float* miss, hipStream_t stream);
+
+/* [host] Per-layer keep budgets from measured miss rates (v3 abstract: the
+ * block budget is allocated across layers by their measured miss rates).
+ * READING: keep_l = clamp(c * (miss_l + 1e-3), mean/2, 10000) with the level
+ * c found by bisection so that sum keep_l = L * mean_keep_bp, rounded to
+ * integer basis points by largest remainder (ties to the lower layer).
+ * miss: [host] double [L]; keep_bp_out: [host] int32 [L]. */
+int spin_allocate_budgets(int L, const double* miss, int mean_keep_bp, int32_t* keep_bp_out);
+
+/* [host] Static text for a status code (and the last HIP error, if any). */
+const char* spin_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPIN_H */

@@ -1,0 +1,274 @@
+"""Python binding of libspin, the MI355X SPIN decode-round library.
+
+Argument marshalling only: every function forwards torch tensors' device
+pointers and the current HIP stream to the C ABI declared in include/spin.h,
+under the same names.  All computation runs in the library's HIP kernels; if
+libspin.so is missing, load() raises instead of falling back to anything.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "load", "SpinError", "SpinState", "make_config", "make_batch",
+    "spin_state_bytes", "spin_state_layout_of", "spin_state_init", "spin_state_destroy",
+    "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
+    "spin_topk_scores", "spin_indexer_topk", "spin_update", "spin_mtp_replay",
+    "spin_measure_miss", "spin_allocate_budgets", "spin_status_string", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so")
+
+EXPORTS = [
+    "spin_state_bytes", "spin_state_layout_of", "spin_state_init", "spin_state_destroy",
+    "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
+    "spin_topk_scores", "spin_indexer_topk", "spin_update", "spin_mtp_replay",
+    "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
+]
+
+SPIN_OK, SPIN_EINVAL, SPIN_EUNSUPPORTED, SPIN_EHIP, SPIN_ESTATE = 0, -1, -2, -3, -4
+ERR_QPOS, ERR_SLOT, ERR_KEPT, ERR_PAGE, ERR_ACCEPT = 1, 2, 4, 8, 16
+
+
+class SpinConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32), ("max_slots", ctypes.c_int32),
+        ("max_ctx", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("max_rows", ctypes.c_int32), ("warmup_steps", ctypes.c_int32),
+        ("explore_bp", ctypes.c_int32), ("alpha", ctypes.c_float),
+        ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64),
+    ]
+
+
+class SpinBatch(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("R", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("slot", ctypes.c_void_p), ("qpos", ctypes.c_void_p),
+    ]
+
+
+class SpinLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("V", "D", "VB", "step", "request_id", "error", "q8", "wq", "qexp",
+                 "bscore", "ukey", "total")] + [
+        ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SpinError(RuntimeError):
+    def __init__(self, status, text):
+        super().__init__(f"spin status {status}: {text}")
+        self.status = status
+
+
+_lib = None
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "spin_state_bytes": [ctypes.POINTER(SpinConfig), ctypes.POINTER(_sz)],
+    "spin_state_layout_of": [ctypes.POINTER(SpinConfig), ctypes.POINTER(SpinLayout)],
+    "spin_state_init": [ctypes.POINTER(SpinConfig), _vp, _sz, _vp, ctypes.POINTER(_vp)],
+    "spin_state_destroy": [_vp],
+    "spin_reset_slots": [_vp, _i32, _vp, _vp, _vp],
+    "spin_predict_blocks": [_vp, _i32, ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
+    "spin_quantize_q": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _vp],
+    "spin_indexer_scores": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
+    "spin_topk_scores": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp],
+    "spin_indexer_topk": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                          _vp, _vp, _vp],
+    "spin_update": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp],
+    "spin_mtp_replay": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp, _vp],
+    "spin_measure_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
+    "spin_allocate_budgets": [_i32, ctypes.POINTER(ctypes.c_double), _i32,
+                              ctypes.POINTER(ctypes.c_int32)],
+    "spin_status_string": [_i32],
+}
+
+
+def load(path=None):
+    """Load libspin.so (built by predictive_kv_block_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m predictive_kv_block_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "spin_status_string" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def spin_status_string(status):
+    return load().spin_status_string(int(status)).decode()
+
+
+def _check(rc):
+    if rc != SPIN_OK:
+        raise SpinError(rc, spin_status_string(rc))
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_config(num_layers, max_slots, max_ctx, topk, max_rows=1, heads=64, head_dim=128,
+                warmup_steps=1, explore_bp=500, alpha=0.9, seed=0x5350494E):
+    return SpinConfig(num_layers, max_slots, max_ctx, 64, heads, head_dim, topk, max_rows,
+                      warmup_steps, explore_bp, alpha, 0, seed)
+
+
+def make_batch(slot, qpos, R, max_blocks):
+    """A spin_batch over device int32 tensors slot [B] and qpos [B]."""
+    b = SpinBatch(int(qpos.numel()), int(R), int(max_blocks), 0, _p(slot), _p(qpos))
+    b._keep = (slot, qpos)
+    return b
+
+
+# ------------------------------------------------------------------ state
+def spin_state_bytes(cfg):
+    n = _sz()
+    _check(load().spin_state_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def spin_state_layout_of(cfg):
+    lay = SpinLayout()
+    _check(load().spin_state_layout_of(ctypes.byref(cfg), ctypes.byref(lay)))
+    return {f: getattr(lay, f) for f, _ in SpinLayout._fields_}
+
+
+def spin_state_init(cfg, state_mem, stream=None):
+    h = _vp()
+    _check(load().spin_state_init(ctypes.byref(cfg), _p(state_mem),
+                                  state_mem.numel() * state_mem.element_size(),
+                                  _stream(stream), ctypes.byref(h)))
+    return h
+
+
+def spin_state_destroy(h):
+    _check(load().spin_state_destroy(h))
+
+
+def spin_reset_slots(h, slots, request_ids, stream=None):
+    _check(load().spin_reset_slots(h, int(slots.numel()), _p(slots), _p(request_ids),
+                                   _stream(stream)))
+
+
+# --------------------------------------------------------------- decode round
+def spin_predict_blocks(h, layer, batch, keep_bp, kept_blocks, kept_count, block_flags,
+                        stream=None):
+    _check(load().spin_predict_blocks(h, int(layer), ctypes.byref(batch), int(keep_bp),
+                                      _p(kept_blocks), _p(kept_count), _p(block_flags),
+                                      _stream(stream)))
+
+
+def spin_quantize_q(h, batch, q_bf16, w, stream=None):
+    _check(load().spin_quantize_q(h, ctypes.byref(batch), _p(q_bf16), _p(w), _stream(stream)))
+
+
+def spin_indexer_scores(h, batch, k_pool, k_scale, block_table, kept_blocks, kept_count, scores,
+                        stream=None):
+    _check(load().spin_indexer_scores(h, ctypes.byref(batch), _p(k_pool), _p(k_scale),
+                                      int(k_scale.numel()), _p(block_table), _p(kept_blocks),
+                                      _p(kept_count), _p(scores), _stream(stream)))
+
+
+def spin_topk_scores(batch, topk, scores, kept_blocks, kept_count, topk_out, stream=None):
+    _check(load().spin_topk_scores(ctypes.byref(batch), int(topk), _p(scores), _p(kept_blocks),
+                                   _p(kept_count), _p(topk_out), _stream(stream)))
+
+
+def spin_indexer_topk(h, batch, q_bf16, w, k_pool, k_scale, block_table, kept_blocks,
+                      kept_count, scores, topk_out, stream=None):
+    _check(load().spin_indexer_topk(h, ctypes.byref(batch), _p(q_bf16), _p(w), _p(k_pool),
+                                    _p(k_scale), int(k_scale.numel()), _p(block_table),
+                                    _p(kept_blocks), _p(kept_count), _p(scores), _p(topk_out),
+                                    _stream(stream)))
+
+
+def spin_update(h, layer, batch, scores, kept_blocks, kept_count, stream=None):
+    _check(load().spin_update(h, int(layer), ctypes.byref(batch), _p(scores), _p(kept_blocks),
+                              _p(kept_count), _stream(stream)))
+
+
+def spin_mtp_replay(h, layer, batch, accepted, scores, kept_blocks, kept_count, stream=None):
+    _check(load().spin_mtp_replay(h, int(layer), ctypes.byref(batch), _p(accepted), _p(scores),
+                                  _p(kept_blocks), _p(kept_count), _stream(stream)))
+
+
+def spin_measure_miss(batch, topk, full_topk, block_flags, miss, stream=None):
+    _check(load().spin_measure_miss(ctypes.byref(batch), int(topk), _p(full_topk),
+                                    _p(block_flags), _p(miss), _stream(stream)))
+
+
+def spin_allocate_budgets(miss, mean_keep_bp):
+    L = len(miss)
+    arr = (ctypes.c_double * L)(*[float(m) for m in miss])
+    out = (ctypes.c_int32 * L)()
+    _check(load().spin_allocate_budgets(L, arr, int(mean_keep_bp), out))
+    return [int(x) for x in out]
+
+
+class SpinState:
+    """A state buffer allocated with torch on `device` and bound to the library."""
+
+    def __init__(self, cfg, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.layout = spin_state_layout_of(cfg)
+        self.mem = torch.empty(self.layout["total"], dtype=torch.uint8, device=device)
+        self.handle = spin_state_init(cfg, self.mem, stream)
+
+    def region(self, name, dtype, shape):
+        """A torch view of one state region (see spin_state_layout in spin.h)."""
+        import torch
+        off = self.layout[name]
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty(0, dtype=dtype).element_size()
+        return self.mem[off:off + nbytes].view(dtype).view(*shape)
+
+    def V(self):
+        c = self.cfg
+        import torch
+        return self.region("V", torch.float32, (c.num_layers, c.max_slots, c.max_ctx))
+
+    def D(self):
+        c = self.cfg
+        import torch
+        return self.region("D", torch.float32, (c.num_layers, c.max_slots, c.max_ctx))
+
+    def VB(self):
+        c = self.cfg
+        import torch
+        return self.region("VB", torch.float32, (c.num_layers, c.max_slots, self.layout["max_blocks"]))
+
+    def step(self):
+        c = self.cfg
+        import torch
+        return self.region("step", torch.int32, (c.num_layers, c.max_slots))
+
+    def error(self):
+        import torch
+        return int(self.region("error", torch.int32, (1,)).item())
+
+    def close(self):
+        if self.handle is not None:
+            spin_state_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

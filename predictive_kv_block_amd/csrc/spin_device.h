@@ -1,0 +1,92 @@
+// Device-side helpers of the SPIN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spin {
+
+constexpr int kBlock = 64;       // slots per logical KV block (= page)
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- float keys
+// Order-preserving map of fp32 to uint32 (larger float -> larger key), with
+// -0.0 folded onto +0.0 so that ReLU zeros of either sign compare equal.
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Number of set bits of a 64-lane ballot below this lane.
+__device__ __forceinline__ int ballot_rank(uint64_t ballot) {
+  const uint64_t below = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
+  return __popcll(ballot & below);
+}
+
+// ------------------------------------------------------------------- Philox
+// Philox4x64-10 counter-based generator, as published by Salmon, Moraes,
+// Dror and Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC'11):
+// ten rounds, each multiplying words 0 and 2 by fixed odd constants, mixing
+// the high halves with the key, and bumping the key by Weyl increments
+// between rounds.
+struct Philox4x64 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ Philox4x64 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2,
+                                                    uint64_t c3, uint64_t k0, uint64_t k1) {
+  const uint64_t m0 = 0xD2E7470EE14C6C93ull, m1 = 0xCA5A826395121157ull;
+  const uint64_t w0 = 0x9E3779B97F4A7C15ull, w1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round) {
+      k0 += w0;
+      k1 += w1;
+    }
+    const uint64_t lo0 = m0 * c0, hi0 = __umul64hi(m0, c0);
+    const uint64_t lo1 = m1 * c2, hi1 = __umul64hi(m1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0;
+    const uint64_t n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  Philox4x64 r;
+  r.w[0] = c0;
+  r.w[1] = c1;
+  r.w[2] = c2;
+  r.w[3] = c3;
+  return r;
+}
+
+// ---------------------------------------------------------------------- misc
+__device__ __forceinline__ int num_blocks_of(int qpos) { return (qpos + kBlock) / kBlock; }
+
+__device__ __forceinline__ void flag_error(int32_t* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// EMA observation: never-observed (-inf) takes the sample, else
+// alpha * x + beta * s in fp32.
+__device__ __forceinline__ float ema_observe(float x, float s, float alpha, float beta) {
+  return (x == -INFINITY) ? s : fmaf(alpha, x, beta * s);
+}
+
+}  // namespace spin

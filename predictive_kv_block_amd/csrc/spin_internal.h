@@ -1,0 +1,54 @@
+// Host-side internals shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/spin.h"
+
+// Device pointers and sizes of one bound state buffer.
+struct SpinView {
+  float* V;          // [L][S][max_ctx]
+  float* D;          // [L][S][max_ctx]
+  float* VB;         // [L][S][max_blocks]
+  int32_t* step;     // [L][S]
+  uint64_t* rid;     // [S]
+  int32_t* err;      // [1]
+  uint8_t* q8;       // [S][max_rows][H][d]
+  float* wq;         // [S][max_rows][H]
+  int32_t* qexp;     // [S][max_rows][H]
+  float* bscore;     // [S][max_rows][max_blocks]
+  uint64_t* ukey;    // [S][max_blocks]
+  int L, S, max_ctx, max_blocks, H, d, max_rows, topk, warmup, explore_bp;
+  float alpha;
+  uint64_t seed;
+};
+
+struct spin_state {
+  spin_config cfg;
+  spin_state_layout lay;
+  char* base;
+  SpinView view;
+};
+
+namespace spin {
+
+hipError_t launch_fill_state(const SpinView& v, hipStream_t s);
+hipError_t launch_reset_slots(const SpinView& v, int n, const int32_t* slots,
+                              const uint64_t* rids, hipStream_t s);
+hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, int keep_bp,
+                          int32_t* kept, int32_t* kept_count, uint8_t* flags, hipStream_t s);
+hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* q_bf16,
+                           const float* w, hipStream_t s);
+hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t* k_pool,
+                          const float* k_scale, int64_t pool_pages, const int32_t* table,
+                          const int32_t* kept, const int32_t* kept_count, float* scores,
+                          hipStream_t s);
+hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const int32_t* kept,
+                       const int32_t* kept_count, int32_t* out, hipStream_t s);
+hipError_t launch_update(const SpinView& v, int layer, const spin_batch& bt,
+                         const int32_t* accepted, const float* scores, const int32_t* kept,
+                         const int32_t* kept_count, hipStream_t s);
+hipError_t launch_miss(const spin_batch& bt, int topk, const int32_t* full_topk,
+                       const uint8_t* flags, float* miss, hipStream_t s);
+
+}  // namespace spin

@@ -1,0 +1,208 @@
+// SPIN block predictor: z = max(V, D), block max-pool, budgeted top-P block
+// selection, Philox exploration and the MTP row union.
+//
+// Two kernels per call:
+//   k_block_scores  (B x R x block-chunks workgroups, streams D and VB)
+//       S_j = max over existing slots i of block j of max(V_i, D_{q-i}).
+//       For a block wholly at or before q this equals max(VB_j, max of the
+//       D window), where VB_j (the block max of V) is kept exact by the update
+//       kernel; the partial last block reads V directly.
+//   k_select        (one 1024-thread workgroup per request)
+//       per row: budget, radix-select of the top-P blocks (ties -> lower j),
+//       radix-select of the n_exp explored blocks with the smallest Philox
+//       words among the rest; union over rows; ascending compaction.
+#include "spin_device.h"
+#include "spin_internal.h"
+#include "spin_select.h"
+
+namespace spin {
+namespace {
+
+constexpr int kScoreWaves = 4;        // waves per workgroup in k_block_scores
+constexpr int kScoreBlocksPerWave = 8;
+constexpr int kSelectThreads = 1024;
+
+__device__ __forceinline__ void budget(int keep_bp, int n, int explore_bp, int* kb, int* nexp) {
+  const int k = int((int64_t(keep_bp) * n + 9999) / 10000);
+  *kb = k;
+  *nexp = int((int64_t(explore_bp) * k) / 10000);
+}
+
+// True when the request's arguments are usable; otherwise the selection
+// kernel reports the error.
+__device__ __forceinline__ bool request_ok(const SpinView& v, const spin_batch& bt, int s, int q0) {
+  return s >= 0 && s < v.S && q0 >= 0 && q0 + bt.R - 1 < v.max_ctx &&
+         num_blocks_of(q0 + bt.R - 1) <= bt.max_blocks && bt.max_blocks <= v.max_blocks;
+}
+
+__global__ void __launch_bounds__(kScoreWaves * kWave)
+k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
+  const int b = blockIdx.y, r = blockIdx.z;
+  const int s = bt.slot[b];
+  const int q0 = bt.qpos[b];
+  if (!request_ok(v, bt, s, q0)) return;
+  const size_t row = size_t(layer) * v.S + s;
+  if (v.step[row] < v.warmup || keep_bp >= 10000) return;
+  const int q = q0 + r;
+  const int n = num_blocks_of(q);
+  int kb, nexp;
+  budget(keep_bp, n, v.explore_bp, &kb, &nexp);
+  if (kb >= n) return;
+
+  const float* V = v.V + row * v.max_ctx;
+  const float* D = v.D + row * v.max_ctx;
+  const float* VB = v.VB + row * v.max_blocks;
+  float* out = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
+  const int l = lane_id();
+  const int j0 = (blockIdx.x * kScoreWaves + threadIdx.x / kWave) * kScoreBlocksPerWave;
+
+  float d[kScoreBlocksPerWave], vv[kScoreBlocksPerWave];
+#pragma unroll
+  for (int m = 0; m < kScoreBlocksPerWave; ++m) {
+    const int j = j0 + m;
+    const int i = j * kBlock + l;
+    const bool in = (j < n) && (i <= q);
+    d[m] = in ? D[q - i] : -INFINITY;
+    const bool full = (j * kBlock + kBlock - 1) <= q;
+    vv[m] = (j < n) ? (full ? VB[j] : (in ? V[i] : -INFINITY)) : -INFINITY;
+  }
+#pragma unroll
+  for (int m = 0; m < kScoreBlocksPerWave; ++m) {
+    const int j = j0 + m;
+    const float sj = wave_max(fmaxf(d[m], vv[m]));
+    if (l == 0 && j < n) out[j] = sj;
+  }
+}
+
+struct BlockScoreSrc {
+  const float* S;
+  __device__ bool get(int j, uint32_t& key) const {
+    key = ord_key(S[j]);
+    return true;
+  }
+};
+
+struct ExploreSrc {
+  const uint64_t* u;
+  const uint8_t* flags;
+  __device__ bool get(int j, uint64_t& key) const {
+    if (flags[j] & 4) return false;      // predicted by this row
+    key = ~u[j];                         // smallest word first
+    return true;
+  }
+};
+
+struct KeptSrc {
+  const uint8_t* flags;
+  __device__ bool get(int j, uint32_t& key) const {
+    key = 0;
+    return (flags[j] & 3) != 0;
+  }
+};
+
+// Flags in LDS: bit 0 predicted by some row, bit 1 explored by some row,
+// bit 2 predicted by the current row.
+__global__ void __launch_bounds__(kSelectThreads)
+k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32_t* kept_count,
+         uint8_t* flags_out) {
+  extern __shared__ uint8_t s_flags[];
+  __shared__ int s_scr[kSelectScratchInts];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int s = bt.slot[b];
+  const int q0 = bt.qpos[b];
+  uint8_t* fo = flags_out + size_t(b) * bt.max_blocks;
+  int32_t* ko = kept + size_t(b) * bt.max_blocks;
+
+  if (!request_ok(v, bt, s, q0)) {
+    for (int j = tid; j < bt.max_blocks; j += kSelectThreads) fo[j] = 0;
+    if (tid == 0) {
+      kept_count[b] = 0;
+      flag_error(v.err, (s < 0 || s >= v.S) ? SPIN_ERR_SLOT : SPIN_ERR_QPOS);
+    }
+    return;
+  }
+  const size_t row = size_t(layer) * v.S + s;
+  const int step = v.step[row];
+  const uint64_t rid = v.rid[s];
+  const bool warm = step < v.warmup || keep_bp >= 10000;
+  const int n_last = num_blocks_of(q0 + bt.R - 1);
+
+  for (int j = tid; j < n_last; j += kSelectThreads) s_flags[j] = 0;
+
+  // Exploration words, shared by every row: u_j = Philox(counter (j/4, step,
+  // request id, 0), key (seed, layer)) word j%4.
+  uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
+  if (!warm && v.explore_bp > 0) {
+    for (int g = tid; g < (n_last + 3) / 4; g += kSelectThreads) {
+      const Philox4x64 p = philox4x64_10(uint64_t(g), uint64_t(step), rid, 0ull, v.seed,
+                                         uint64_t(layer));
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (4 * g + k < n_last) u[4 * g + k] = p.w[k];
+    }
+  }
+  __syncthreads();
+
+  for (int r = 0; r < bt.R; ++r) {
+    const int q = q0 + r;
+    const int n = num_blocks_of(q);
+    int kb, nexp;
+    budget(keep_bp, n, v.explore_bp, &kb, &nexp);
+    if (warm || kb >= n) {
+      for (int j = tid; j < n; j += kSelectThreads) s_flags[j] |= 1;
+      __syncthreads();
+      continue;
+    }
+    for (int j = tid; j < n; j += kSelectThreads) s_flags[j] &= 3;
+    __syncthreads();
+    const int pcount = kb - nexp;
+    if (pcount > 0) {
+      BlockScoreSrc src{v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks};
+      uint32_t thr;
+      int neq;
+      radix_threshold<kSelectThreads, 4, uint32_t>(src, n, pcount, &thr, &neq, s_scr);
+      ordered_emit<kSelectThreads, 2, uint32_t>(
+          src, n, thr, neq, [&](int j, int) { s_flags[j] |= 5; }, s_scr);
+    }
+    if (nexp > 0) {
+      ExploreSrc src{u, s_flags};
+      uint64_t thr;
+      int neq;
+      radix_threshold<kSelectThreads, 4, uint64_t>(src, n, nexp, &thr, &neq, s_scr);
+      ordered_emit<kSelectThreads, 2, uint64_t>(
+          src, n, thr, neq, [&](int j, int) { s_flags[j] |= 2; }, s_scr);
+    }
+    __syncthreads();
+  }
+
+  for (int j = tid; j < bt.max_blocks; j += kSelectThreads) {
+    uint8_t f = 0;
+    if (j < n_last) f = (s_flags[j] & 1) ? 1 : ((s_flags[j] & 2) ? 2 : 0);
+    fo[j] = f;
+  }
+  KeptSrc ksrc{s_flags};
+  const int total = ordered_emit<kSelectThreads, 2, uint32_t>(
+      ksrc, n_last, 0u, 0x7fffffff,
+      [&](int j, int rank) {
+        if (rank < bt.max_blocks) ko[rank] = j;
+      },
+      s_scr);
+  if (tid == 0) kept_count[b] = min(total, bt.max_blocks);
+}
+
+}  // namespace
+
+hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, int keep_bp,
+                          int32_t* kept, int32_t* kept_count, uint8_t* flags, hipStream_t s) {
+  const int per_wg = kScoreWaves * kScoreBlocksPerWave;
+  const unsigned chunks = unsigned((bt.max_blocks + per_wg - 1) / per_wg);
+  if (keep_bp < 10000)
+    hipLaunchKernelGGL(k_block_scores, dim3(chunks, bt.B, bt.R), dim3(kScoreWaves * kWave), 0, s,
+                       v, layer, bt, keep_bp);
+  hipLaunchKernelGGL(k_select, dim3(bt.B), dim3(kSelectThreads), size_t(bt.max_blocks), s, v,
+                     layer, bt, keep_bp, kept, kept_count, flags);
+  return hipGetLastError();
+}
+
+}  // namespace spin

@@ -1,0 +1,81 @@
+"""C-ABI checks that need no GPU: exports, configuration checks, layouts and
+the host-side budget allocator (against the oracle's statement of it)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import predictive_kv_block_amd as spin
+from oracle import spin_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spin.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(spin_\w+)\s*\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = spin.load()
+    names = _declared()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(spin.EXPORTS) == names
+
+
+def test_config_validation_and_layout():
+    cfg = spin.make_config(1, 96, 524288, 2048)
+    n = spin.spin_state_bytes(cfg)
+    lay = spin.spin_state_layout_of(cfg)
+    assert lay["total"] == n and lay["max_blocks"] == 8192
+    assert lay["D"] - lay["V"] >= 96 * 524288 * 4
+    for k in ("V", "D", "VB", "step", "request_id", "error", "q8", "wq", "qexp", "bscore", "ukey"):
+        assert lay[k] % 256 == 0
+    bad = spin.make_config(1, 4, 1024, 64)
+    bad.block_size = 32
+    with pytest.raises(spin.SpinError) as e:
+        spin.spin_state_bytes(bad)
+    assert e.value.status == spin.SPIN_EUNSUPPORTED
+    bad = spin.make_config(0, 4, 1024, 64)
+    with pytest.raises(spin.SpinError) as e:
+        spin.spin_state_bytes(bad)
+    assert e.value.status == spin.SPIN_EINVAL
+    bad = spin.make_config(1, 4, 1024, 64, max_rows=5)
+    with pytest.raises(spin.SpinError):
+        spin.spin_state_bytes(bad)
+    small = spin.make_config(1, 1, 4096, 256, heads=4, head_dim=32)      # predictor-only shape
+    assert spin.spin_state_bytes(small) > 0
+
+
+def test_null_and_range_arguments_rejected_before_any_launch():
+    lib = spin.load()
+    cfg = spin.make_config(1, 2, 1024, 64)
+    out = ctypes.c_void_p()
+    assert lib.spin_state_init(ctypes.byref(cfg), None, 0, None, ctypes.byref(out)) == spin.SPIN_EINVAL
+    assert lib.spin_state_destroy(None) == spin.SPIN_EINVAL
+    assert lib.spin_predict_blocks(None, 0, None, 5000, None, None, None, None) == spin.SPIN_EINVAL
+    assert lib.spin_update(None, 0, None, None, None, None, None) == spin.SPIN_EINVAL
+    b = spin.SpinBatch(1, 1, 16, 0, None, None)
+    assert lib.spin_topk_scores(ctypes.byref(b), 64, None, None, None, None, None) == spin.SPIN_EINVAL
+    assert lib.spin_measure_miss(ctypes.byref(b), 0, None, None, None, None) == spin.SPIN_EINVAL
+    assert "invalid" in spin.spin_status_string(spin.SPIN_EINVAL)
+
+
+@pytest.mark.parametrize("L,mean", [(4, 5000), (1, 6000), (7, 7000), (3, 9500)])
+def test_allocate_budgets_matches_oracle(L, mean):
+    rng = np.random.default_rng(L * 31 + mean)
+    for trial in range(20):
+        m = rng.random(L) * (0.5 if trial % 2 else 0.05)
+        if trial == 0:
+            m[:] = 0.0
+        got = spin.spin_allocate_budgets(list(m), mean)
+        exp = O.allocate_budgets(m, mean)
+        assert got == [int(x) for x in exp]
+        assert sum(got) == L * mean
+    with pytest.raises(spin.SpinError):
+        spin.spin_allocate_budgets([0.1, 1.5], 5000)

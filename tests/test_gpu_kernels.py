@@ -1,0 +1,292 @@
+"""Kernel-level parity of the HIP path against the oracle, through the C ABI.
+
+Every input comes from the seeded generator (or plain numpy/torch draws in the
+test); every expected value from oracle/.  Bars: q8 codes/exponents, masks,
+counts, exploration and top-k over identical scores bit-exact; indexer scores
+and EMA state within max(1e-3 |ref|, 1e-5 mag) (fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import predictive_kv_block_amd as spin
+from oracle import spin_oracle as O
+from tests.spin_harness import (NEG, Rig, assert_scores_close, assert_topk_tie_aware,
+                                nblocks, np_, oracle_fp8_operands, score_mag, score_tol)
+from workload import random_state
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# --------------------------------------------------------------- quantiser
+def test_quantize_codes_and_exponents_bit_exact(gpu_lib):
+    bits = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16)
+    vals = bits.view(torch.bfloat16)
+    vals = vals[torch.isfinite(vals.float())]
+    mag_order = torch.argsort(vals.float().abs())
+    n_heads = 8 * 2 * 64
+    need = n_heads * 128
+    rng = np.random.default_rng(0)
+    # layout 1: heads of similar magnitude (every value meets a nearby exponent);
+    # layout 2: random heads (small values under a large exponent round to 0)
+    lay1 = vals[mag_order].repeat(need // len(vals) + 1)[:need]
+    lay2 = vals[torch.as_tensor(rng.integers(0, len(vals), need))]
+    for name, q in (("sorted", lay1), ("random", lay2)):
+        q = q.view(8, 2, 64, 128).contiguous().to(DEV)
+        q[0, 0, 5] = 0                                              # an all-zero head
+        w = torch.rand(8, 2, 64, device=DEV) + 0.5
+        cfg = spin.make_config(1, 8, 4096, 64, max_rows=2)
+        rig = Rig(cfg, 8, 2, 64)
+        _say("quantize", name)
+        spin.spin_quantize_q(rig.h, rig.batch, q, w)
+        torch.cuda.synchronize()
+        lay = rig.state.layout
+        q8 = np_(rig.state.region("q8", torch.uint8, (8, 2, 64, 128)))
+        qe = np_(rig.state.region("qexp", torch.int32, (8, 2, 64)))
+        wq = np_(rig.state.region("wq", torch.float32, (8, 2, 64)))
+        qv, wv, codes, e = oracle_fp8_operands(q, w)
+        assert np.array_equal(qe, e), name
+        assert np.array_equal(q8, codes), f"{name}: {np.sum(q8 != codes)} codes differ"
+        # w * 2^e is exact in fp32 except where it lands below the normal range
+        # (heads of subnormal-sized bf16 values only)
+        sane = e > -100
+        assert np.array_equal(wq[sane], wv[sane].astype(np.float32)), name
+        assert lay["q8"] > 0
+
+
+# ------------------------------------------------------------------ indexer
+def _rand_pool(rng, pages, d=128):
+    k = torch.randn(pages, 64, d, generator=torch.Generator().manual_seed(int(rng.integers(1 << 30))))
+    amax = k.abs().amax(dim=(1, 2))
+    sc = amax / 448.0
+    codes = (k / sc[:, None, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, sc.float()
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_indexer_scores_parity(gpu_lib, R):
+    rng = np.random.default_rng(R)
+    B, mb, pages = 3, 40, 150
+    codes, sc = _rand_pool(rng, pages)
+    table = np.stack([rng.permutation(pages)[:mb] for _ in range(B)]).astype(np.int32)
+    qpos = np.array([64 * 37 + 20, 64 * 12 + 63, 64 * 39 - R], dtype=np.int64)
+    kept = []
+    for b in range(B):
+        n = nblocks(qpos[b] + R - 1)
+        sel = np.sort(rng.choice(n, size=max(1, n // 2), replace=False))
+        sel = np.union1d(sel, [n - 1])                            # ragged last block
+        kept.append(sel)
+    kept[2] = kept[2][:0]                                        # a request with nothing kept
+    q = (torch.randn(B, R, 64, 128) * 2).to(torch.bfloat16)
+    w = torch.rand(B, R, 64) + 0.5
+    cfg = spin.make_config(1, B, 64 * mb, 2048, max_rows=R)
+    rig = Rig(cfg, B, R, mb)
+    rig.set_qpos(qpos)
+    kt = np.full((B, mb), -1, dtype=np.int32)
+    for b in range(B):
+        kt[b, : len(kept[b])] = kept[b]
+    rig.kept.copy_(torch.as_tensor(kt))
+    rig.kept_count.copy_(torch.as_tensor([len(k) for k in kept], dtype=torch.int32))
+    rig.scores.fill_(12345.0)
+    _say("indexer R", R)
+    spin.spin_quantize_q(rig.h, rig.batch, q.to(DEV), w.to(DEV))
+    spin.spin_indexer_scores(rig.h, rig.batch, codes.to(DEV), sc.to(DEV),
+                             torch.as_tensor(table).to(DEV), rig.kept, rig.kept_count, rig.scores)
+    torch.cuda.synchronize()
+    kv = O.e4m3fn_decode(np_(codes))
+    scv = np_(sc).astype(np.float64)
+    got = np_(rig.scores)
+    for b in range(B):
+        qv, wv, _, _ = oracle_fp8_operands(q[b], w[b])
+        ref = O.indexer_scores(qv, wv, kv, scv, table[b], kept[b], int(qpos[b]))
+        mag = score_mag(qv, wv, kv, scv, table[b], kept[b])
+        n = len(kept[b]) * 64
+        assert_scores_close(got[b, :, :n], ref, mag, f"b{b}")
+        assert np.all(got[b, :, n:] == 12345.0)                  # nothing written past kept
+    assert rig.state.error() == 0
+
+
+# ------------------------------------------------------------------- top-k
+@pytest.mark.parametrize("case", ["random", "ties", "short", "zeros"])
+def test_topk_exact_on_identical_scores(gpu_lib, case):
+    rng = np.random.default_rng(["random", "ties", "short", "zeros"].index(case))
+    B, R, mb, K = 3, 2, 120, 512
+    qpos = np.array([64 * 110 + 5, 64 * 100 + 63, 64 * 5 + 3], dtype=np.int64)
+    kept = [np.sort(rng.choice(nblocks(q + R - 1), nblocks(q + R - 1) * 2 // 3, replace=False))
+            for q in qpos]
+    kept = [np.union1d(k, [nblocks(q + R - 1) - 1]) for k, q in zip(kept, qpos)]
+    if case == "short":
+        kept[0] = kept[0][:3]                                    # fewer candidates than K
+    sc = rng.random((B, R, mb * 64)).astype(np.float32)
+    if case == "ties":
+        sc = (np.round(sc * 16) / 16).astype(np.float32)
+    if case == "zeros":
+        sc[:] = 0.0
+        sc[:, :, ::7] = -0.0
+        sc[:, :, ::13] = 1.0
+    cfg_rows = []
+    batch_slot = torch.zeros(B, dtype=torch.int32, device=DEV)
+    qp = torch.as_tensor(qpos.astype(np.int32), device=DEV)
+    bt = spin.make_batch(batch_slot, qp, R, mb)
+    kt = np.full((B, mb), -1, dtype=np.int32)
+    for b in range(B):
+        kt[b, : len(kept[b])] = kept[b]
+    kept_d = torch.as_tensor(kt, device=DEV)
+    cnt_d = torch.as_tensor([len(k) for k in kept], dtype=torch.int32, device=DEV)
+    out = torch.zeros(B, R, K, dtype=torch.int32, device=DEV)
+    _say("topk", case)
+    spin.spin_topk_scores(bt, K, torch.as_tensor(sc, device=DEV), kept_d, cnt_d, out)
+    torch.cuda.synchronize()
+    got = np_(out)
+    for b in range(B):
+        for r in range(R):
+            ref = O.topk_positions(sc[b, r, : len(kept[b]) * 64].astype(np.float64), kept[b],
+                                   int(qpos[b]) + r, K)
+            assert np.array_equal(got[b, r], ref), (case, b, r)
+    del cfg_rows
+
+
+# --------------------------------------------------------------- predictor
+@pytest.mark.parametrize("R,keep_bp,explore_bp,step", [
+    (1, 6000, 500, 3), (1, 5000, 0, 1), (1, 8000, 2500, 7), (4, 5000, 1000, 2),
+    (4, 6000, 500, 0), (1, 10000, 500, 4), (1, 0, 500, 4), (2, 9990, 500, 5)])
+def test_predict_exact(gpu_lib, R, keep_bp, explore_bp, step):
+    rng = np.random.default_rng(keep_bp + R)
+    B, ctx = 4, 64 * 200
+    mb = nblocks(ctx - 1)
+    qpos = np.array([ctx - R, 64 * 150 + 63 - 1, 64 * 3 + 1, 40], dtype=np.int64)
+    cfg = spin.make_config(2, B, ctx, 256, max_rows=R, explore_bp=explore_bp, seed=0xABCDEF)
+    rig = Rig(cfg, B, R, mb)
+    rids = [1000 + 7 * b for b in range(B)]
+    rig.reset(rids)
+    layer = 1
+    states = []
+    for b in range(B):
+        V = np_(random_state(ctx, 0.15, seed=10 * b + 1)).astype(np.float64)
+        D = np_(random_state(ctx, 0.15, seed=10 * b + 2)).astype(np.float64)
+        V[qpos[b] + 1:] = NEG
+        rig.inject(layer, b, V.astype(np.float32), D.astype(np.float32), step)
+        states.append((V.astype(np.float32).astype(np.float64), D.astype(np.float32).astype(np.float64)))
+    rig.set_qpos(qpos)
+    _say("predict", R, keep_bp, explore_bp, step)
+    spin.spin_predict_blocks(rig.h, layer, rig.batch, keep_bp, rig.kept, rig.kept_count, rig.flags)
+    torch.cuda.synchronize()
+    for b in range(B):
+        V, D = states[b]
+        kept, flags = O.predict_blocks(V, D, int(qpos[b]), R, keep_bp, explore_bp, cfg.seed, layer,
+                                       step, rids[b], cfg.warmup_steps)
+        assert np.array_equal(rig.kept_list(b), kept), b
+        gf = np_(rig.flags[b])
+        assert np.array_equal(gf[: len(flags)], flags), b
+        assert np.all(gf[len(flags):] == 0)
+    assert rig.state.error() == 0
+
+
+# ------------------------------------------------------ update and replay
+@pytest.mark.parametrize("R", [1, 4])
+def test_update_and_replay_parity(gpu_lib, R):
+    rng = np.random.default_rng(40 + R)
+    B, ctx = 5, 64 * 60
+    mb = nblocks(ctx - 1)
+    cfg = spin.make_config(1, B, ctx, 256, max_rows=R, alpha=0.9)
+    rig = Rig(cfg, B, R, mb)
+    qpos = np.array([64 * 50 + 61, 64 * 50 + 63, 64 * 20, 64 * 55 + 2, 63], dtype=np.int64)
+    qpos = np.minimum(qpos, ctx - R)
+    acc = rng.integers(0, R, B).astype(np.int32)
+    states, kept = [], []
+    for b in range(B):
+        V = np_(random_state(ctx, 0.3, seed=b + 100)).astype(np.float32).astype(np.float64)
+        D = np_(random_state(ctx, 0.3, seed=b + 200)).astype(np.float32).astype(np.float64)
+        V[qpos[b] + 1:] = NEG
+        rig.inject(0, b, V, D, 3)
+        n = nblocks(qpos[b] + R - 1)
+        k = np.sort(rng.choice(n, size=max(1, (2 * n) // 3), replace=False))
+        k = np.union1d(k, [n - 1])
+        if b == 1:
+            k = np.arange(n)                                     # every block kept
+        kept.append(k)
+        states.append((V, D))
+    kt = np.full((B, mb), -1, dtype=np.int32)
+    for b in range(B):
+        kt[b, : len(kept[b])] = kept[b]
+    rig.kept.copy_(torch.as_tensor(kt))
+    rig.kept_count.copy_(torch.as_tensor([len(k) for k in kept], dtype=torch.int32))
+    sc = (rng.random((B, R, mb * 64)) * 20).astype(np.float32)
+    for b in range(B):
+        slot = (kept[b][:, None] * 64 + np.arange(64)).reshape(-1)
+        for r in range(R):
+            row = sc[b, r, : len(slot)]
+            row[slot > qpos[b] + r] = NEG
+    rig.scores.copy_(torch.as_tensor(sc))
+    rig.set_qpos(qpos)
+    _say("update R", R, "accepted", acc.tolist())
+    if R == 1:
+        spin.spin_update(rig.h, 0, rig.batch, rig.scores, rig.kept, rig.kept_count)
+        acc[:] = 0
+    else:
+        spin.spin_mtp_replay(rig.h, 0, rig.batch, torch.as_tensor(acc, device=DEV), rig.scores,
+                             rig.kept, rig.kept_count)
+    torch.cuda.synchronize()
+    for b in range(B):
+        V, D = states[b][0].copy(), states[b][1].copy()
+        O.ema_update(V, D, sc[b, :, : len(kept[b]) * 64].astype(np.float64), kept[b], int(qpos[b]),
+                     int(acc[b]), 0.9)
+        gV, gD, gVB, gstep = rig.read_state(0, b)
+        for name, g, r in (("V", gV, V), ("D", gD, D)):
+            fin = np.isfinite(r)
+            assert np.array_equal(fin, np.isfinite(g)), (name, b)
+            tol = 1e-3 * np.abs(r[fin]) + 1e-6
+            assert np.all(np.abs(g[fin] - r[fin]) <= tol), (name, b)
+        # unobserved entries are bit-unchanged
+        slot = (kept[b][:, None] * 64 + np.arange(64)).reshape(-1)
+        obs_v = np.zeros(ctx, dtype=bool)
+        obs_d = np.zeros(ctx, dtype=bool)
+        for r in range(int(acc[b]) + 1):
+            i = slot[slot <= qpos[b] + r]
+            obs_v[i] = True
+            obs_d[qpos[b] + r - i] = True
+        assert np.array_equal(gV[~obs_v], states[b][0][~obs_v]), b
+        assert np.array_equal(gD[~obs_d], states[b][1][~obs_d]), b
+        vb = np.concatenate([gV, np.full(mb * 64 - len(gV), NEG)]).reshape(mb, 64).max(1)
+        assert np.array_equal(gVB[kept[b]], vb[kept[b]]), b
+        assert gstep == 4
+    assert rig.state.error() == 0
+
+
+def test_measure_miss_parity(gpu_lib):
+    rng = np.random.default_rng(7)
+    B, R, mb, K = 3, 2, 50, 300
+    full = rng.integers(-1, mb * 64, (B, R, K)).astype(np.int32)
+    flags = rng.integers(0, 3, (B, mb)).astype(np.uint8)
+    bt = spin.make_batch(torch.zeros(B, dtype=torch.int32, device=DEV),
+                         torch.zeros(B, dtype=torch.int32, device=DEV), R, mb)
+    miss = torch.zeros(B, R, device=DEV)
+    spin.spin_measure_miss(bt, K, torch.as_tensor(full, device=DEV),
+                           torch.as_tensor(flags, device=DEV), miss)
+    got = np_(miss)
+    for b in range(B):
+        for r in range(R):
+            assert abs(got[b, r] - O.miss_rate(full[b, r], flags[b])) < 1e-6
+
+
+def test_device_errors_flagged_without_faults(gpu_lib):
+    cfg = spin.make_config(1, 2, 4096, 64)
+    rig = Rig(cfg, 2, 1, 64)
+    rig.slot.copy_(torch.tensor([0, 7], dtype=torch.int32))        # slot 7 >= max_slots
+    rig.set_qpos([100, 100])
+    spin.spin_predict_blocks(rig.h, 0, rig.batch, 5000, rig.kept, rig.kept_count, rig.flags)
+    torch.cuda.synchronize()
+    assert rig.state.error() & spin.ERR_SLOT
+    assert int(rig.kept_count[1]) == 0
+    rig.slot.copy_(torch.tensor([0, 1], dtype=torch.int32))
+    rig.set_qpos([100, 4096])                                      # past max_ctx
+    spin.spin_predict_blocks(rig.h, 0, rig.batch, 5000, rig.kept, rig.kept_count, rig.flags)
+    spin.spin_update(rig.h, 0, rig.batch, rig.scores, rig.kept, rig.kept_count)
+    torch.cuda.synchronize()
+    assert rig.state.error() & spin.ERR_QPOS
+    assert int(rig.kept_count[1]) == 0

@@ -256,7 +256,7 @@ def random_state(n, neg_inf_share, seed, device="cpu"):
     g = _gen(device, seed, 55)
     x = torch.randn(n, generator=g, device=device).abs() * 10.0
     dup = torch.randint(0, n, (max(1, n // 50),), generator=g, device=device)
-    x[dup] = x[dup[0]]
+    x[dup] = x[dup[0]].clone()
     ninf = torch.rand(n, generator=g, device=device) < neg_inf_share
     x[ninf] = float("-inf")
     return x
