@@ -24,9 +24,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 PAGE_BYTES = 64 * 128          # fp8 keys of one 64-token page
 # Algorithmic bytes the indexer kernel moves per kept page and row: the page's
-# keys, its scale, its block-table entry, its kept-list entry, 64 fp32 scores.
+# keys, its scale, its block-table entry, its kept-list entry, 64 fp32 scores
+# and the page's maximum score per row.
 IDX_BYTES_PER_PAGE = PAGE_BYTES + 4 + 4 + 4
-IDX_SCORE_BYTES_PER_PAGE_ROW = 64 * 4
+IDX_SCORE_BYTES_PER_PAGE_ROW = 64 * 4 + 4       # scores + the page maximum
 
 
 def _args():
@@ -67,6 +68,9 @@ def _setup(wl, device):
         scores=torch.empty(B, wl.rows, nb * 64, dtype=torch.float32, device=device),
         topk=torch.empty(B, wl.rows, wl.topk, dtype=torch.int32, device=device),
     )
+    bufs["pmax"] = torch.empty(B, wl.rows, nb, dtype=torch.float32, device=device)
+    bufs["topk_ws"] = torch.empty(max(256, spin.spin_topk_workspace_bytes(bufs["batch"], wl.topk)),
+                                  dtype=torch.uint8, device=device)
     return spin, pool, cfg, st, bufs, make_queries
 
 
@@ -82,10 +86,11 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, ev=None):
     if ev:
         ev[2].record()
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
-                             pool.block_table, b["kept"], b["cnt"], b["scores"])
+                             pool.block_table, b["kept"], b["cnt"], b["scores"], b["pmax"])
     if ev:
         ev[3].record()
-    spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"])
+    spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
+                          b["topk_ws"], b["pmax"])
     if ev:
         ev[4].record()
     spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"])

@@ -66,7 +66,7 @@ typedef struct spin_config {
   int32_t block_size;   /* must be 64 */
   int32_t heads;        /* indexer heads H_I: 64 */
   int32_t head_dim;     /* indexer head dim d_I: 128 */
-  int32_t topk;         /* K of the per-row top-k, 1..8192 */
+  int32_t topk;         /* K of the per-row top-k, 4..4096, a multiple of 4 */
   int32_t max_rows;     /* 1 + MTP draft length, 1..4 */
   int32_t warmup_steps; /* leading all-keep rounds of each (layer, request) */
   int32_t explore_bp;   /* exploration share of the kept budget, basis points */
@@ -101,9 +101,13 @@ typedef struct spin_batch {
  *   qexp [max_slots][max_rows][heads] int32   workspace: query exponents e
  *   bscore [max_slots][max_rows][max_blocks]  workspace: block scores S
  *   ukey [max_slots][max_blocks] uint64       workspace: exploration keys
+ *   page_max [max_slots][max_rows][max_blocks] workspace: page maxima for the top-k
+ *   topk_ws                                   workspace: top-k survivor buffers for
+ *                                             max_slots * max_rows rows (to `total`)
  * Workspace arrays are indexed by batch position b, not by slot. */
 typedef struct spin_state_layout {
-  size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, total;
+  size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, page_max, topk_ws,
+      total;
   int32_t max_blocks;     /* ceil(max_ctx / 64) */
   int32_t reserved;
 } spin_state_layout;
@@ -175,23 +179,39 @@ int spin_quantize_q(spin_state* st, const spin_batch* batch, const void* q_bf16,
  * k_pool: e4m3fn codes [pool_pages][64][head_dim]; k_scale: fp32 [pool_pages];
  * block_table: int32 [B][max_blocks] (logical block -> page).
  * scores: fp32 [B][R][max_blocks * 64] in kept order: element k*64 + t is slot
- * 64*kept_blocks[b][k] + t; slots after the row's position get -inf. */
+ * 64*kept_blocks[b][k] + t; slots after the row's position get -inf.
+ * page_max (may be NULL): fp32 [B][R][max_blocks], element k = the largest of
+ * the 64 scores of kept page k for that row (-inf if all are masked); it is
+ * the optional top-k prefilter input of spin_topk_scores. */
 int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* k_pool,
                         const float* k_scale, int64_t pool_pages, const int32_t* block_table,
                         const int32_t* kept_blocks, const int32_t* kept_count, float* scores,
-                        hipStream_t stream);
+                        float* page_max, hipStream_t stream);
+
+/* Bytes of caller-owned device workspace spin_topk_scores needs for this
+ * batch shape and K (0 when every row fits one 16384-candidate chunk). */
+int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
 
 /* Per-row top-k over kept-order scores (v1 abstract: a fixed top-k goes to
  * core attention): the `topk` kept slots i <= q_r with the largest scores,
  * ties to the lower slot, written ascending to topk_out int32 [B][R][topk],
  * padded with -1.  -0.0 ranks equal to +0.0.  scores as spin_indexer_scores
- * writes them (only slots <= q_r are read as candidates). */
+ * writes them (only slots <= q_r are read as candidates).  topk: 4..4096, a
+ * multiple of 4.  page_max (may be NULL): the per-page maxima written by
+ * spin_indexer_scores for these scores; with at least `topk` valid pages its
+ * topk-th largest value is a lower bound of the answer's smallest score, so
+ * scores below it are dropped before ranking (the result is the same).
+ * workspace: 256-byte aligned device memory of at least
+ * spin_topk_workspace_bytes() bytes (may be NULL only when page_max is NULL
+ * and the rows fit one 16384-candidate chunk); its contents need no
+ * initialisation and are clobbered.  batch->slot is not read. */
 int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
-                     const int32_t* kept_blocks, const int32_t* kept_count, int32_t* topk_out,
+                     const float* page_max, const int32_t* kept_blocks, const int32_t* kept_count,
+                     int32_t* topk_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
 /* spin_quantize_q + spin_indexer_scores + spin_topk_scores with the state's
- * top-k K.  `scores` must stay alive until spin_update / spin_mtp_replay
+ * top-k K, the state's page-max and top-k workspaces.  `scores` must stay alive until spin_update / spin_mtp_replay
  * (the deferred update of the ai4snews digest, "arXiv深度剖析"). */
 int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf16,
                       const float* w, const uint8_t* k_pool, const float* k_scale,

@@ -12,8 +12,9 @@ __all__ = [
     "load", "SpinError", "SpinState", "make_config", "make_batch",
     "spin_state_bytes", "spin_state_layout_of", "spin_state_init", "spin_state_destroy",
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
-    "spin_topk_scores", "spin_indexer_topk", "spin_update", "spin_mtp_replay",
-    "spin_measure_miss", "spin_allocate_budgets", "spin_status_string", "EXPORTS",
+    "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
+    "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so")
@@ -21,8 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so"
 EXPORTS = [
     "spin_state_bytes", "spin_state_layout_of", "spin_state_init", "spin_state_destroy",
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
-    "spin_topk_scores", "spin_indexer_topk", "spin_update", "spin_mtp_replay",
-    "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
+    "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
+    "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
 ]
 
 SPIN_OK, SPIN_EINVAL, SPIN_EUNSUPPORTED, SPIN_EHIP, SPIN_ESTATE = 0, -1, -2, -3, -4
@@ -50,7 +51,7 @@ class SpinBatch(ctypes.Structure):
 class SpinLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("V", "D", "VB", "step", "request_id", "error", "q8", "wq", "qexp",
-                 "bscore", "ukey", "total")] + [
+                 "bscore", "ukey", "page_max", "topk_ws", "total")] + [
         ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
@@ -70,8 +71,10 @@ _SIGS = {
     "spin_reset_slots": [_vp, _i32, _vp, _vp, _vp],
     "spin_predict_blocks": [_vp, _i32, ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
     "spin_quantize_q": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _vp],
-    "spin_indexer_scores": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp],
-    "spin_topk_scores": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp],
+    "spin_indexer_scores": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                            _vp],
+    "spin_topk_scores": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "spin_topk_workspace_bytes": [ctypes.POINTER(SpinBatch), _i32, ctypes.POINTER(_sz)],
     "spin_indexer_topk": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                           _vp, _vp, _vp],
     "spin_update": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp],
@@ -176,15 +179,26 @@ def spin_quantize_q(h, batch, q_bf16, w, stream=None):
 
 
 def spin_indexer_scores(h, batch, k_pool, k_scale, block_table, kept_blocks, kept_count, scores,
-                        stream=None):
+                        page_max=None, stream=None):
     _check(load().spin_indexer_scores(h, ctypes.byref(batch), _p(k_pool), _p(k_scale),
                                       int(k_scale.numel()), _p(block_table), _p(kept_blocks),
-                                      _p(kept_count), _p(scores), _stream(stream)))
+                                      _p(kept_count), _p(scores), _p(page_max), _stream(stream)))
 
 
-def spin_topk_scores(batch, topk, scores, kept_blocks, kept_count, topk_out, stream=None):
-    _check(load().spin_topk_scores(ctypes.byref(batch), int(topk), _p(scores), _p(kept_blocks),
-                                   _p(kept_count), _p(topk_out), _stream(stream)))
+def spin_topk_workspace_bytes(batch, topk):
+    n = _sz()
+    _check(load().spin_topk_workspace_bytes(ctypes.byref(batch), int(topk), ctypes.byref(n)))
+    return n.value
+
+
+def spin_topk_scores(batch, topk, scores, kept_blocks, kept_count, topk_out, workspace=None,
+                     page_max=None, stream=None):
+    """workspace: a uint8 device tensor of >= spin_topk_workspace_bytes bytes;
+    page_max: the optional page maxima from spin_indexer_scores."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().spin_topk_scores(ctypes.byref(batch), int(topk), _p(scores), _p(page_max),
+                                   _p(kept_blocks), _p(kept_count), _p(topk_out), _p(workspace),
+                                   nbytes, _stream(stream)))
 
 
 def spin_indexer_topk(h, batch, q_bf16, w, k_pool, k_scale, block_table, kept_blocks,

@@ -31,9 +31,9 @@ SOURCES = ["spin_abi.cpp", "spin_state.hip", "spin_predict.hip", "spin_indexer.h
            "spin_topk.hip", "spin_update.hip"]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, build_dir=BUILD, extra=()):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines()
                      if "packed-fp32-ops" not in ln and "ignoring feature" not in ln)
@@ -42,25 +42,27 @@ def _compile(src):
     return obj, errs.strip()
 
 
-def build(jobs=None, verbose=False):
-    """Compile every HIP source and link libspin.so; returns the library path."""
+def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, defines=()):
+    """Compile every HIP source and link the library (default: libspin.so next to
+    this file); `defines` are extra -D macros for tuning experiments."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
     for obj, msg in results:
         if msg and verbose:
             print(msg, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *[o for o, _ in results],
            "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

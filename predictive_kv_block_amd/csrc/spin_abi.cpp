@@ -20,7 +20,8 @@ int check_config(const spin_config* c) {
       c->explore_bp < 0 || c->explore_bp > 10000 || c->reserved != 0 ||
       !(c->alpha >= 0.0f && c->alpha <= 1.0f))
     return SPIN_EINVAL;
-  if (c->block_size != 64 || c->max_rows > 4 || c->topk > 8192 || c->max_ctx > (1 << 22) ||
+  if (c->block_size != 64 || c->max_rows > 4 || c->topk > 4096 || c->topk % 4 != 0 ||
+      c->max_ctx > (1 << 22) ||
       c->num_layers > 1024 || c->max_slots > 65535 || c->heads > 1024 || c->head_dim > 1024)
     return SPIN_EUNSUPPORTED;
   return SPIN_OK;
@@ -49,6 +50,9 @@ spin_state_layout make_layout(const spin_config* c) {
   l.qexp = off;       off = align_up(off + S * R * H * 4);
   l.bscore = off;     off = align_up(off + S * R * MB * 4);
   l.ukey = off;       off = align_up(off + S * MB * 8);
+  l.page_max = off;   off = align_up(off + S * R * MB * 4);
+  l.topk_ws = off;
+  off = align_up(off + spin::topk_plan(int(S * R), int(MB), c->topk).bytes);
   l.total = off;
   l.max_blocks = int32_t(MB);
   return l;
@@ -71,7 +75,7 @@ int check_batch(const spin_state* st, const spin_batch* bt) {
 int check_plain_batch(const spin_batch* bt) {
   if (!bt || !bt->qpos) return SPIN_EINVAL;
   if (bt->B < 1 || bt->B > 65535 || bt->R < 1 || bt->R > 4 || bt->max_blocks < 1 ||
-      bt->max_blocks > (1 << 20) || bt->reserved != 0)
+      bt->max_blocks > (1 << 16) || bt->B * bt->R > 65535 || bt->reserved != 0)
     return SPIN_EINVAL;
   return SPIN_OK;
 }
@@ -121,6 +125,9 @@ int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes, hipSt
   v.qexp = reinterpret_cast<int32_t*>(st->base + lay.qexp);
   v.bscore = reinterpret_cast<float*>(st->base + lay.bscore);
   v.ukey = reinterpret_cast<uint64_t*>(st->base + lay.ukey);
+  v.pmax = reinterpret_cast<float*>(st->base + lay.page_max);
+  v.topk_ws = st->base + lay.topk_ws;
+  v.topk_ws_bytes = lay.total - lay.topk_ws;
   v.L = cfg->num_layers;
   v.S = cfg->max_slots;
   v.max_ctx = cfg->max_ctx;
@@ -178,7 +185,7 @@ int spin_quantize_q(spin_state* st, const spin_batch* batch, const void* q_bf16,
 int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* k_pool,
                         const float* k_scale, int64_t pool_pages, const int32_t* block_table,
                         const int32_t* kept_blocks, const int32_t* kept_count, float* scores,
-                        hipStream_t stream) {
+                        float* page_max, hipStream_t stream) {
   int rc = check_batch(st, batch);
   if (rc) return rc;
   if (!k_pool || !k_scale || pool_pages < 1 || pool_pages > (int64_t(1) << 31) || !block_table ||
@@ -186,18 +193,33 @@ int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* 
     return SPIN_EINVAL;
   if (!indexer_shape_ok(st)) return SPIN_EUNSUPPORTED;
   return hip_status(spin::launch_indexer(st->view, *batch, k_pool, k_scale, pool_pages,
-                                         block_table, kept_blocks, kept_count, scores, stream));
+                                         block_table, kept_blocks, kept_count, scores, page_max,
+                                         stream));
+}
+
+int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes) {
+  int rc = check_plain_batch(batch);
+  if (rc) return rc;
+  if (!bytes || topk < 1 || topk > 4096 || topk % 4 != 0) return SPIN_EINVAL;
+  *bytes = spin::topk_plan(batch->B * batch->R, batch->max_blocks, topk).bytes;
+  return SPIN_OK;
 }
 
 int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
-                     const int32_t* kept_blocks, const int32_t* kept_count, int32_t* topk_out,
+                     const float* page_max, const int32_t* kept_blocks, const int32_t* kept_count,
+                     int32_t* topk_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
   int rc = check_plain_batch(batch);
   if (rc) return rc;
-  if (topk < 1 || topk > 65536 || !scores || !kept_blocks || !kept_count || !topk_out)
+  if (topk < 1 || topk > 4096 || topk % 4 != 0 || !scores || !kept_blocks || !kept_count ||
+      !topk_out)
     return SPIN_EINVAL;
-  return hip_status(
-      spin::launch_topk(*batch, topk, scores, kept_blocks, kept_count, topk_out, stream));
+  const spin::TopkPlan p = spin::topk_plan(batch->B * batch->R, batch->max_blocks, topk);
+  if ((p.levels > 1 || page_max) && (!workspace || workspace_bytes < p.bytes))
+    return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPIN_EINVAL;
+  return hip_status(spin::launch_topk(*batch, topk, scores, page_max, kept_blocks, kept_count,
+                                      topk_out, workspace, stream));
 }
 
 int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf16, const float* w,
@@ -212,9 +234,10 @@ int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf1
   rc = spin_quantize_q(st, batch, q_bf16, w, stream);
   if (rc) return rc;
   rc = spin_indexer_scores(st, batch, k_pool, k_scale, pool_pages, block_table, kept_blocks,
-                           kept_count, scores, stream);
+                           kept_count, scores, st->view.pmax, stream);
   if (rc) return rc;
-  return spin_topk_scores(batch, st->cfg.topk, scores, kept_blocks, kept_count, topk_out, stream);
+  return spin_topk_scores(batch, st->cfg.topk, scores, st->view.pmax, kept_blocks, kept_count,
+                          topk_out, st->view.topk_ws, st->view.topk_ws_bytes, stream);
 }
 
 int spin_update(spin_state* st, int layer, const spin_batch* batch, const float* scores,

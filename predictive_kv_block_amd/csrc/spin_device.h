@@ -33,10 +33,10 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// Number of set bits of a 64-lane ballot below this lane.
+// Number of set bits of a 64-lane ballot below this lane (v_mbcnt).
 __device__ __forceinline__ int ballot_rank(uint64_t ballot) {
-  const uint64_t below = (lane_id() == 0) ? 0ull : (~0ull >> (64 - lane_id()));
-  return __popcll(ballot & below);
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(ballot >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(uint32_t(ballot), 0u));
 }
 
 // ------------------------------------------------------------------- Philox
@@ -74,6 +74,21 @@ __device__ __forceinline__ Philox4x64 philox4x64_10(uint64_t c0, uint64_t c1, ui
   r.w[2] = c2;
   r.w[3] = c3;
   return r;
+}
+
+// Histogram increment for a wave: every lane with `on` adds 1 to hist[digit].
+// When every active lane has the same digit (keys concentrated in one bin),
+// one lane adds the whole count; otherwise each lane issues its own LDS atomic.
+__device__ __forceinline__ void hist_add(int* hist, int digit, bool on) {
+  const uint64_t act = __ballot(on);
+  if (act == 0) return;
+  const int d0 = __builtin_amdgcn_readlane(digit, __ffsll(static_cast<unsigned long long>(act)) - 1);
+  const uint64_t other = __ballot(on && digit != d0);
+  if (other == 0) {
+    if (lane_id() == __ffsll(static_cast<unsigned long long>(act)) - 1) atomicAdd(&hist[d0], __popcll(act));
+  } else if (on) {
+    atomicAdd(&hist[digit], 1);
+  }
 }
 
 // ---------------------------------------------------------------------- misc

@@ -5,7 +5,8 @@
 //   wq = w * 2^e, so sum_h wq_h ReLU(q8_h . k) equals the bf16-query score up
 //   to the rounding of q to e4m3fn.
 // k_indexer: one wave per kept page (64 tokens x 128 fp8 = 8 KB, contiguous in
-//   the pool).  Heads form the M side of v_mfma_scale_f32_16x16x128_f8f6f4 and
+//   the pool); optionally also the page's maximum score per row, which lets
+//   the top-k discard most candidates before ranking them.  Heads form the M side of v_mfma_scale_f32_16x16x128_f8f6f4 and
 //   tokens the N side, so one MFMA does 16 heads x 16 tokens over the whole
 //   head dim; a page is 4 head tiles x 4 token tiles per row.  ReLU, the head
 //   weights and the head sum run on the accumulator registers, the 4 lane
@@ -22,8 +23,17 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
-constexpr int kIdxWaves = 4;
-constexpr int kPagesPerWave = 8;
+#ifndef SPIN_IDX_PAGES_PER_WAVE
+#define SPIN_IDX_PAGES_PER_WAVE 16
+#endif
+#ifndef SPIN_IDX_WAVES
+#define SPIN_IDX_WAVES 4
+#endif
+#ifndef SPIN_IDX_NONTEMPORAL
+#define SPIN_IDX_NONTEMPORAL 0
+#endif
+constexpr int kIdxWaves = SPIN_IDX_WAVES;
+constexpr int kPagesPerWave = SPIN_IDX_PAGES_PER_WAVE;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -61,22 +71,25 @@ k_quantize(SpinView v, spin_batch bt, const uint16_t* q, const float* w) {
   }
 }
 
+// 32 contiguous key bytes; keys are streamed once, so optionally non-temporal.
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 c = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r;
-  r[0] = int(a.x); r[1] = int(a.y); r[2] = int(a.z); r[3] = int(a.w);
-  r[4] = int(c.x); r[5] = int(c.y); r[6] = int(c.z); r[7] = int(c.w);
-  return r;
+#if SPIN_IDX_NONTEMPORAL
+  return __builtin_nontemporal_load(reinterpret_cast<const v8i*>(p));
+#else
+  return *reinterpret_cast<const v8i*>(p);
+#endif
 }
 
 // grid (ceil(max_blocks / (4 * kPagesPerWave)), B), 256 threads.
-// Wave w of workgroup x handles kept pages x*32 + w + 4m, m < kPagesPerWave.
+// Wave w of workgroup x handles kept pages x*4*P + w + 4m, m < P = kPagesPerWave.
+// The page metadata chain (kept entry -> block table -> scale) is issued first
+// and overlaps the staging of the queries in LDS; the keys of page m+1 are in
+// flight while page m runs on the MFMAs.
 template <int R>
 __global__ void __launch_bounds__(kIdxWaves * kWave)
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
-          const int32_t* kept, const int32_t* kept_count, float* scores) {
+          const int32_t* kept, const int32_t* kept_count, float* scores, float* page_max) {
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kDim];
   __shared__ float s_w[R * kHeads];
   const int b = blockIdx.y;
@@ -88,17 +101,8 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   const int first = blockIdx.x * (kIdxWaves * kPagesPerWave);
   if (first >= cnt) return;
 
-  // Stage this request's quantised queries and head weights in LDS.
-  const uint8_t* q8 = v.q8 + size_t(b) * v.max_rows * kHeads * kDim;
-  const float* wq = v.wq + size_t(b) * v.max_rows * kHeads;
-  for (int i = threadIdx.x; i < R * kHeads * kDim / 16; i += blockDim.x)
-    reinterpret_cast<uint4*>(s_q)[i] = reinterpret_cast<const uint4*>(q8)[i];
-  for (int i = threadIdx.x; i < R * kHeads; i += blockDim.x) s_w[i] = wq[i];
-  __syncthreads();
-
   const int l = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int q0 = bt.qpos[b];
   const size_t mb = size_t(bt.max_blocks);
 
   // Page metadata for this wave's pages, lane m holding page m.
@@ -123,29 +127,49 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
     }
   }
 
+  // Stage this request's quantised queries and head weights in LDS.
+  const uint8_t* q8 = v.q8 + size_t(b) * v.max_rows * kHeads * kDim;
+  const float* wq = v.wq + size_t(b) * v.max_rows * kHeads;
+  for (int i = threadIdx.x; i < R * kHeads * kDim / 16; i += kIdxWaves * kWave)
+    reinterpret_cast<uint4*>(s_q)[i] = reinterpret_cast<const uint4*>(q8)[i];
+  for (int i = threadIdx.x; i < R * kHeads; i += kIdxWaves * kWave) s_w[i] = wq[i];
+
+  const int q0 = bt.qpos[b];
   const int g = l >> 4;       // lane group: K chunk of the operands, M rows of the result
   const int n16 = l & 15;     // M row of A / N column of B
-  v8i kb[4];
-  auto load_page = [&](int p) {
+  const int npages = min(kPagesPerWave, (cnt - first - wave + kIdxWaves - 1) / kIdxWaves);
+
+  v8i kb[4], kn[4];
+  auto load_page = [&](v8i* dst, int p) {
     const uint8_t* base = k_pool + size_t(p) * (kBlock * kDim) + g * 32;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) kb[tt] = load32(base + (tt * 16 + n16) * kDim);
+    for (int tt = 0; tt < 4; ++tt) dst[tt] = load32(base + (tt * 16 + n16) * kDim);
   };
+  {
+    const int p0 = __shfl(my_p, 0, kWave);
+    if (npages > 0 && p0 >= 0) load_page(kn, p0);
+  }
+  __syncthreads();
 
 #pragma unroll 1
-  for (int m = 0; m < kPagesPerWave; ++m) {
+  for (int m = 0; m < npages; ++m) {
     const int k = first + wave + kIdxWaves * m;
-    if (k >= cnt) break;
     const int j = __shfl(my_j, m, kWave);
-    const int p = __shfl(my_p, m, kWave);
     const float sc = __shfl(my_sc, m, kWave);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) kb[tt] = kn[tt];
+    if (m + 1 < npages) {
+      const int pn = __shfl(my_p, m + 1, kWave);
+      if (pn >= 0) load_page(kn, pn);
+    }
     if (j < 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r) {
         scores[(size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l] = -INFINITY;
+        if (page_max && l == 0) page_max[(size_t(b) * R + r) * mb + k] = -INFINITY;
+      }
       continue;
     }
-    load_page(p);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -168,8 +192,12 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
       }
       const float val = g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
       const int slot = j * kBlock + l;
-      scores[(size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l] =
-          (slot <= q0 + r) ? val * sc : -INFINITY;
+      const float out = (slot <= q0 + r) ? val * sc : -INFINITY;
+      scores[(size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l] = out;
+      if (page_max) {
+        const float m = wave_max(out);
+        if (l == 0) page_max[(size_t(b) * R + r) * mb + k] = m;
+      }
     }
   }
 }
@@ -186,26 +214,26 @@ hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* 
 hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t* k_pool,
                           const float* k_scale, int64_t pool_pages, const int32_t* table,
                           const int32_t* kept, const int32_t* kept_count, float* scores,
-                          hipStream_t s) {
+                          float* page_max, hipStream_t s) {
   const int per_wg = kIdxWaves * kPagesPerWave;
   const dim3 grid(unsigned((bt.max_blocks + per_wg - 1) / per_wg), unsigned(bt.B));
   const dim3 block(kIdxWaves * kWave);
   switch (bt.R) {
     case 1:
       hipLaunchKernelGGL(k_indexer<1>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores);
+                         table, kept, kept_count, scores, page_max);
       break;
     case 2:
       hipLaunchKernelGGL(k_indexer<2>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores);
+                         table, kept, kept_count, scores, page_max);
       break;
     case 3:
       hipLaunchKernelGGL(k_indexer<3>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores);
+                         table, kept, kept_count, scores, page_max);
       break;
     case 4:
       hipLaunchKernelGGL(k_indexer<4>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores);
+                         table, kept, kept_count, scores, page_max);
       break;
     default:
       return hipErrorInvalidValue;

@@ -18,6 +18,9 @@ struct SpinView {
   int32_t* qexp;     // [S][max_rows][H]
   float* bscore;     // [S][max_rows][max_blocks]
   uint64_t* ukey;    // [S][max_blocks]
+  float* pmax;       // [S][max_rows][max_blocks] page maxima of the last indexer call
+  void* topk_ws;     // top-k level buffers for max_slots * max_rows rows
+  size_t topk_ws_bytes;
   int L, S, max_ctx, max_blocks, H, d, max_rows, topk, warmup, explore_bp;
   float alpha;
   uint64_t seed;
@@ -32,6 +35,18 @@ struct spin_state {
 
 namespace spin {
 
+// Candidates per top-k chunk (staged in LDS as uint32 keys).
+constexpr int kChunk = 16384;
+
+// Levels of the chunked top-k for `rows` rows of up to max_blocks * 64
+// candidates, and the workspace they need (two ping-pong survivor buffers).
+struct TopkPlan {
+  int rows, K, levels;
+  int chunks[16];
+  size_t buf_elems, count_elems, bytes;
+};
+TopkPlan topk_plan(int rows, int max_blocks, int K);
+
 hipError_t launch_fill_state(const SpinView& v, hipStream_t s);
 hipError_t launch_reset_slots(const SpinView& v, int n, const int32_t* slots,
                               const uint64_t* rids, hipStream_t s);
@@ -42,9 +57,10 @@ hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* 
 hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t* k_pool,
                           const float* k_scale, int64_t pool_pages, const int32_t* table,
                           const int32_t* kept, const int32_t* kept_count, float* scores,
-                          hipStream_t s);
-hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const int32_t* kept,
-                       const int32_t* kept_count, int32_t* out, hipStream_t s);
+                          float* page_max, hipStream_t s);
+hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_max,
+                       const int32_t* kept, const int32_t* kept_count, int32_t* out, void* ws,
+                       hipStream_t s);
 hipError_t launch_update(const SpinView& v, int layer, const spin_batch& bt,
                          const int32_t* accepted, const float* scores, const int32_t* kept,
                          const int32_t* kept_count, hipStream_t s);

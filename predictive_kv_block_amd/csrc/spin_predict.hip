@@ -19,8 +19,9 @@ namespace spin {
 namespace {
 
 constexpr int kScoreWaves = 4;        // waves per workgroup in k_block_scores
-constexpr int kScoreBlocksPerWave = 8;
+constexpr int kScoreBlocksPerWave = 16;
 constexpr int kSelectThreads = 1024;
+constexpr size_t kResidentLdsMax = 150 * 1024;   // dynamic LDS for the resident selection
 
 __device__ __forceinline__ void budget(int keep_bp, int n, int explore_bp, int* kb, int* nexp) {
   const int k = int((int64_t(keep_bp) * n + 9999) / 10000);
@@ -101,12 +102,18 @@ struct KeptSrc {
 };
 
 // Flags in LDS: bit 0 predicted by some row, bit 1 explored by some row,
-// bit 2 predicted by the current row.
+// bit 2 predicted by the current row.  With RESIDENT, the row's block scores
+// and the exploration words also live in LDS (dynamic LDS = 13 B per block);
+// otherwise the selection reads them from the state's workspace.
+template <bool RESIDENT>
 __global__ void __launch_bounds__(kSelectThreads)
 k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32_t* kept_count,
          uint8_t* flags_out) {
-  extern __shared__ uint8_t s_flags[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
   __shared__ int s_scr[kSelectScratchInts];
+  uint64_t* s_u = reinterpret_cast<uint64_t*>(s_dyn);
+  float* s_S = reinterpret_cast<float*>(s_dyn + size_t(bt.max_blocks) * 8);
+  uint8_t* s_flags = RESIDENT ? s_dyn + size_t(bt.max_blocks) * 12 : s_dyn;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int s = bt.slot[b];
@@ -132,7 +139,7 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
 
   // Exploration words, shared by every row: u_j = Philox(counter (j/4, step,
   // request id, 0), key (seed, layer)) word j%4.
-  uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
+  uint64_t* u = RESIDENT ? s_u : v.ukey + size_t(b) * v.max_blocks;
   if (!warm && v.explore_bp > 0) {
     for (int g = tid; g < (n_last + 3) / 4; g += kSelectThreads) {
       const Philox4x64 p = philox4x64_10(uint64_t(g), uint64_t(step), rid, 0ull, v.seed,
@@ -157,8 +164,13 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
     for (int j = tid; j < n; j += kSelectThreads) s_flags[j] &= 3;
     __syncthreads();
     const int pcount = kb - nexp;
+    const float* S_row = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
+    if (RESIDENT && pcount > 0) {
+      for (int j = tid; j < n; j += kSelectThreads) s_S[j] = S_row[j];
+      __syncthreads();
+    }
     if (pcount > 0) {
-      BlockScoreSrc src{v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks};
+      BlockScoreSrc src{RESIDENT ? s_S : S_row};
       uint32_t thr;
       int neq;
       radix_threshold<kSelectThreads, 4, uint32_t>(src, n, pcount, &thr, &neq, s_scr);
@@ -200,8 +212,18 @@ hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, in
   if (keep_bp < 10000)
     hipLaunchKernelGGL(k_block_scores, dim3(chunks, bt.B, bt.R), dim3(kScoreWaves * kWave), 0, s,
                        v, layer, bt, keep_bp);
-  hipLaunchKernelGGL(k_select, dim3(bt.B), dim3(kSelectThreads), size_t(bt.max_blocks), s, v,
-                     layer, bt, keep_bp, kept, kept_count, flags);
+  const size_t resident_lds = size_t(bt.max_blocks) * 13;
+  // Opt in to dynamic LDS beyond 64 KB for the resident variant (once).
+  static const hipError_t lds_opt_in = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&k_select<true>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(kResidentLdsMax));
+  if (resident_lds > 64 * 1024 && lds_opt_in != hipSuccess) return lds_opt_in;
+  if (resident_lds <= kResidentLdsMax)
+    hipLaunchKernelGGL(k_select<true>, dim3(bt.B), dim3(kSelectThreads), resident_lds, s, v,
+                       layer, bt, keep_bp, kept, kept_count, flags);
+  else
+    hipLaunchKernelGGL(k_select<false>, dim3(bt.B), dim3(kSelectThreads), size_t(bt.max_blocks),
+                       s, v, layer, bt, keep_bp, kept, kept_count, flags);
   return hipGetLastError();
 }
 

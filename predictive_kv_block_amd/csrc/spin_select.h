@@ -14,7 +14,8 @@
 
 namespace spin {
 
-// LDS scratch needed by the helpers below (ints).
+// LDS scratch needed by the helpers below (ints): histogram, broadcast words,
+// per-wave counts and prefixes.
 constexpr int kSelectScratchInts = 256 + 8 + 4 * 32;
 
 template <int NT, int U, typename K, typename Src>
@@ -26,7 +27,8 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
   const int tid = threadIdx.x;
   K prefix = 0, mask = 0;
   int remaining = want;
-  for (int shift = int(sizeof(K)) * 8 - 8; shift >= 0; shift -= 8) {
+  bool done = false;
+  for (int shift = int(sizeof(K)) * 8 - 8; shift >= 0 && !done; shift -= 8) {
     for (int i = tid; i < 256; i += NT) s_hist[i] = 0;
     __syncthreads();
     for (int base = 0; base < n; base += NT * U) {
@@ -39,7 +41,7 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (ok[u] && (key[u] & mask) == prefix) atomicAdd(&s_hist[int(key[u] >> shift) & 255], 1);
+        hist_add(s_hist, int(key[u] >> shift) & 255, ok[u] && (key[u] & mask) == prefix);
     }
     __syncthreads();
     if (tid < kWave) {
@@ -47,6 +49,7 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
       if (l == 0) {
         s_bc[0] = 0;
         s_bc[1] = 0;
+        s_bc[2] = 0;
       }
       const int c0 = s_hist[4 * l], c1 = s_hist[4 * l + 1], c2 = s_hist[4 * l + 2],
                 c3 = s_hist[4 * l + 3];
@@ -65,6 +68,7 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
           if (cum + c[b] >= remaining) {
             digit = 4 * l + b;
             at = cum;
+            s_bc[2] = c[b];
             break;
           }
           cum += c[b];
@@ -76,13 +80,17 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
     __syncthreads();
     const int digit = s_bc[0];
     const int at = s_bc[1];
+    const int bucket = s_bc[2];
     prefix |= K(digit) << shift;
     mask |= K(255) << shift;
     remaining -= at;
+    done = bucket == remaining;        // the whole bucket is taken: stop early
     __syncthreads();
   }
+  // With an early stop, thr is the bucket's lowest key and every key of the
+  // bucket (>= thr) is taken.
   *thr_out = prefix;
-  *neq_out = remaining;
+  *neq_out = done ? 0x7fffffff : remaining;
 }
 
 // Ordered emission: calls emit(j, rank) for every selected j, rank being its

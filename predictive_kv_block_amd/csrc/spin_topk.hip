@@ -1,65 +1,571 @@
 // Per-row top-k over the kept-order indexer scores, and the miss measurement.
 //
-// k_topk: one 1024-thread workgroup per (request, row).  Candidates are the
-//   kept slots at or before the row's position.  The K-th largest key is found
-//   by MSB-first 8-bit radix passes over an LDS histogram; the selected slots
-//   (key above the threshold, or equal to it and among the first n_eq such
-//   slots) are emitted by a per-wave ordered ballot pass.  Kept order is
-//   ascending in position, so the output comes out sorted and ties go to the
-//   lower position.
+// Candidates of a row are the kept slots at or before its position, in kept
+// order (= ascending position).  The selection is exact, with ties to the
+// lower position.
+//
+// 1. k_topk_fused (one workgroup per row, when the indexer's per-page maxima
+//    are given): t1 = the K-th largest page maximum.  Each page whose maximum
+//    is >= t1 holds at least one score >= t1, so with at least K valid pages
+//    the row's K-th largest score is >= t1 and every score < t1 can be
+//    dropped.  Only pages with maximum >= t1 are read; their scores >= t1 are
+//    gathered in position order and ranked exactly, and the row is done.  Rows
+//    that do not fit its buffers fall through to step 2 with t1 as a filter.
+// 2. k_topk_level, level 0: the row is cut into chunks of kChunk; each chunk's
+//    surviving candidates are held in registers (wave w owns a contiguous
+//    segment, lane l every 64th element of it).  If at most K survive, all of
+//    them pass on; otherwise the chunk's local top-K is found by an MSB-first
+//    radix select over LDS histograms.  Every element of the row's top-K is in
+//    its chunk's local top-K, so nothing of the answer is lost.  Survivors are
+//    written in position order, K slots per chunk.
+// 3. Further levels repeat step 2 over the survivors until one chunk remains;
+//    that level writes the answer ascending, padded with -1.  Rows answered by
+//    step 1 are skipped by every level.
+//
 // k_miss: share of an all-keep top-k that falls in skipped blocks.
 #include "spin_device.h"
 #include "spin_internal.h"
-#include "spin_select.h"
 
 namespace spin {
 namespace {
 
-constexpr int kTopkThreads = 1024;
+constexpr int kTopkThreads = 512;
+constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kHistCopies = 4;                       // LDS histograms, shared by waves
+constexpr int kSeg = kChunk / kTopkWaves;            // 2048 keys per wave
+constexpr int kPerLane = kSeg / kWave;               // 32 keys per lane
 
-struct ScoreRowSrc {
-  const float* s;
+struct LevelArgs {
+  spin_batch bt;
+  int K;
+  // level 0 input
+  const float* scores;
   const int32_t* kept;
-  int qr;
-  int max_blocks;
-  __device__ bool get(int x, uint32_t& key) const {
-    const int j = kept[x >> 6];
-    const int slot = j * kBlock + (x & 63);
-    if (j < 0 || j >= max_blocks || slot > qr) return false;
-    key = ord_key(s[x]);
-    return true;
-  }
+  const int32_t* kept_count;
+  const uint32_t* thr_key;    // [rows] key lower bound from the page maxima, or null
+  const int32_t* done;        // [rows] 1 = answered by the fused kernel, or null
+  // later levels' input: survivors of the previous level
+  const uint32_t* in_keys;    // [rows][in_chunks * K]
+  const int32_t* in_pos;      // [rows][in_chunks * K]
+  const int32_t* in_counts;   // [rows][in_chunks]
+  int in_chunks;
+  // output
+  uint32_t* out_keys;         // [rows][out_chunks * K]
+  int32_t* out_pos;
+  int32_t* out_counts;        // [rows][out_chunks]
+  int out_chunks;
+  int32_t* topk_out;          // final level: [rows][K]
 };
 
-__global__ void __launch_bounds__(kTopkThreads)
-k_topk(spin_batch bt, int K, const float* scores, const int32_t* kept,
-       const int32_t* kept_count, int32_t* out) {
-  __shared__ int s_scr[kSelectScratchInts];
-  const int b = blockIdx.x / bt.R, r = blockIdx.x % bt.R;
+constexpr int kMaxWaves = 16;
+
+struct TopkShared {
+  int hist[kHistCopies][256];
+  int wave_a[kMaxWaves], wave_b[kMaxWaves];
+  uint32_t wave_min[kMaxWaves], wave_max[kMaxWaves];
+  int bc[4];
+};
+
+// Workgroup totals over register-held keys (0 = not a candidate): the number
+// of candidates and their smallest and largest key.  NT threads, NPL keys each.
+template <int NT, int NPL>
+__device__ void block_key_stats(const uint32_t* key, TopkShared& sh, int* total, uint32_t* kmin,
+                                uint32_t* kmax) {
+  constexpr int NW = NT / kWave;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  int n = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    n += key[i] != 0u;
+    if (key[i] != 0u) {
+      lo = min(lo, key[i]);
+      hi = max(hi, key[i]);
+    }
+  }
+  n = wave_sum(n);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, uint32_t(__shfl_xor(int(lo), o, kWave)));
+    hi = max(hi, uint32_t(__shfl_xor(int(hi), o, kWave)));
+  }
+  __syncthreads();
+  if (l == 0) {
+    sh.wave_a[w] = n;
+    sh.wave_min[w] = lo;
+    sh.wave_max[w] = hi;
+  }
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    t += sh.wave_a[i];
+    lo = min(lo, sh.wave_min[i]);
+    hi = max(hi, sh.wave_max[i]);
+  }
+  *total = t;
+  *kmin = lo;
+  *kmax = hi;
+}
+
+// Threshold of the `want` largest register-held keys (0 < want < total):
+// selected = key > thr, or key == thr for the first n_eq in index order.
+// Radix windows start below the bits common to kmin and kmax; the search stops
+// early when the whole threshold bucket is taken (then thr is the bucket's
+// lowest key and n_eq is unbounded).
+template <int NT, int NPL>
+__device__ void radix_select_regs(const uint32_t* key, int want, uint32_t kmin, uint32_t kmax,
+                                  TopkShared& sh, uint32_t* thr_out, int* n_eq_out) {
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  if (kmin == kmax) {
+    *thr_out = kmin;                       // all equal: the lowest-index `want`
+    *n_eq_out = want;
+    return;
+  }
+  const int hb = 31 - __clz(int(kmin ^ kmax));
+  uint32_t mask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmin & mask;
+  int remaining = want;
+  int top = hb;                            // highest bit of the current window
+  bool done = false;
+  while (top >= 0 && !done) {
+    const int width = min(8, top + 1);
+    const int shift = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    __syncthreads();
+    for (int i = tid; i < kHistCopies * 256; i += NT) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      hist_add(sh.hist[w % kHistCopies], int((key[i] >> shift) & dmask),
+               key[i] != 0u && (key[i] & mask) == prefix);
+    __syncthreads();
+    if (w == 0) {
+      int c4[4], tot = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        int sum = 0;
+#pragma unroll
+        for (int hc = 0; hc < kHistCopies; ++hc) sum += sh.hist[hc][4 * l + k];
+        c4[k] = sum;
+        tot += sum;
+      }
+      int sfx = tot;  // inclusive suffix sum over lanes l..63
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_down(sfx, o, kWave);
+        if (l + o < kWave) sfx += t;
+      }
+      const int above = sfx - tot;
+      if (l == 0) {
+        sh.bc[0] = 0;
+        sh.bc[1] = 0;
+        sh.bc[2] = 0;
+      }
+      if (above < remaining && remaining <= sfx) {
+        int cum = above;
+        for (int k = 3; k >= 0; --k) {
+          if (cum + c4[k] >= remaining) {
+            sh.bc[0] = 4 * l + k;
+            sh.bc[1] = cum;
+            sh.bc[2] = c4[k];
+            break;
+          }
+          cum += c4[k];
+        }
+      }
+    }
+    __syncthreads();
+    const int digit = sh.bc[0];
+    remaining -= sh.bc[1];
+    prefix |= uint32_t(digit) << shift;
+    mask |= dmask << shift;
+    done = sh.bc[2] == remaining;
+    top = shift - 1;
+  }
+  *thr_out = prefix;
+  *n_eq_out = done ? 0x7fffffff : remaining;
+}
+
+// ---------------------------------------------------------------- fused row
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedPageLanes = 16;                          // page maxima per lane
+constexpr int kFusedMaxPages = kFusedThreads * kFusedPageLanes;   // 16384
+constexpr int kFusedCandPages = 4096;                        // listed candidate pages
+constexpr int kFusedCap = 8192;                              // survivors held in LDS
+constexpr int kFusedPerLane = kFusedCap / kFusedThreads;     // 8
+
+constexpr int kFusedBatch = 16;                              // pages per wave step
+
+struct FusedShared {
+  TopkShared t;
+  int pages[kFusedCandPages];     // kept index of each candidate page, ascending
+  int pagej[kFusedCandPages];     // its block index (kept entry)
+  int pcount[kFusedCandPages];    // survivors per candidate page, then their offsets
+  uint32_t skey[kFusedCap];       // survivors in position order
+  int spos[kFusedCap];
+  int scan[kFusedWaves];
+};
+
+// Exclusive prefix sum over n <= kFusedCandPages ints in LDS; returns the total.
+__device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
+  constexpr int per = kFusedCandPages / kFusedThreads;         // 4
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  int loc[per], sum = 0;
+#pragma unroll
+  for (int k = 0; k < per; ++k) {
+    const int i = tid * per + k;
+    loc[k] = (i < n) ? v[i] : 0;
+    sum += loc[k];
+  }
+  int inc = sum;                                               // inclusive scan in the wave
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (l >= o) inc += t;
+  }
+  __syncthreads();
+  if (l == kWave - 1) wave_tot[w] = inc;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedWaves; ++i) {
+    before += (i < w) ? wave_tot[i] : 0;
+    total += wave_tot[i];
+  }
+  int run = before + inc - sum;
+#pragma unroll
+  for (int k = 0; k < per; ++k) {
+    const int i = tid * per + k;
+    if (i < n) v[i] = run;
+    run += loc[k];
+  }
+  __syncthreads();
+  return total;
+}
+
+// grid (rows).  The whole top-k of a row in one workgroup when the page maxima
+// allow it: t1 = K-th largest page maximum; only pages whose maximum is >= t1
+// can hold scores >= t1; those scores (at least K of them) are collected in
+// position order and ranked exactly.  Rows that do not fit (fewer than K valid
+// pages, more than kFusedCandPages candidate pages or kFusedCap survivors)
+// leave done = 0 and thr_key = t1 (or 0) for the chunked levels.
+__global__ void __launch_bounds__(kFusedThreads)
+k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
+             const int32_t* kept, const int32_t* kept_count, int32_t* topk_out,
+             uint32_t* thr_key, int32_t* done) {
+  __shared__ FusedShared sh;
+  const int row = blockIdx.x;
+  const int b = row / bt.R, r = row % bt.R;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   const size_t mb = size_t(bt.max_blocks);
   int cnt = kept_count[b];
   cnt = cnt < 0 ? 0 : (cnt > bt.max_blocks ? bt.max_blocks : cnt);
-  const int n = cnt * kBlock;
+  if (cnt > kFusedMaxPages || cnt < K) {
+    if (tid == 0) {
+      thr_key[row] = 0u;
+      done[row] = 0;
+    }
+    return;
+  }
+  const int qr = bt.qpos[b] + r;
+  const float* pm = page_max + size_t(row) * mb;
+  const float* sc = scores + size_t(row) * mb * kBlock;
   const int32_t* kb = kept + size_t(b) * mb;
-  ScoreRowSrc src{scores + (size_t(b) * bt.R + r) * mb * kBlock, kb, bt.qpos[b] + r,
-                  bt.max_blocks};
-  int32_t* o = out + (size_t(b) * bt.R + r) * K;
 
-  const int nvalid = count_valid<kTopkThreads, 8, uint32_t>(src, n, s_scr);
-  const int want = min(K, nvalid);
-  uint32_t thr = 0;
-  int neq = 0x7fffffff;
-  if (want > 0 && want < nvalid)
-    radix_threshold<kTopkThreads, 8, uint32_t>(src, n, want, &thr, &neq, s_scr);
-  int total = 0;
-  if (want > 0)
-    total = ordered_emit<kTopkThreads, 4, uint32_t>(
-        src, n, thr, neq,
-        [&](int x, int rank) {
-          if (rank < K) o[rank] = kb[x >> 6] * kBlock + (x & 63);
-        },
-        s_scr);
-  for (int i = min(total, K) + threadIdx.x; i < K; i += kTopkThreads) o[i] = -1;
+  // 1. t1 over the page maxima (page p = w*1024 + i*64 + l held by lane l)
+  uint32_t pk[kFusedPageLanes];
+#pragma unroll
+  for (int i = 0; i < kFusedPageLanes; ++i) {
+    const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
+    const float v = (p < cnt) ? pm[p] : -INFINITY;
+    pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
+  }
+  int npages;
+  uint32_t kmin, kmax;
+  block_key_stats<kFusedThreads, kFusedPageLanes>(pk, sh.t, &npages, &kmin, &kmax);
+  if (npages < K) {
+    if (tid == 0) {
+      thr_key[row] = 0u;
+      done[row] = 0;
+    }
+    return;
+  }
+  uint32_t t1 = kmin;
+  if (npages > K) {
+    int n_eq;
+    radix_select_regs<kFusedThreads, kFusedPageLanes>(pk, K, kmin, kmax, sh.t, &t1, &n_eq);
+  }
+  if (tid == 0) thr_key[row] = t1;
+
+  // 2. candidate pages (maximum >= t1), listed in ascending kept order
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedPageLanes; ++i) mine += (pk[i] != 0u && pk[i] >= t1) ? 1 : 0;
+  mine = wave_sum(mine);
+  __syncthreads();
+  if (l == 0) sh.scan[w] = mine;
+  __syncthreads();
+  int before = 0, ncand = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedWaves; ++i) {
+    before += (i < w) ? sh.scan[i] : 0;
+    ncand += sh.scan[i];
+  }
+  if (ncand > kFusedCandPages) {
+    if (tid == 0) done[row] = 0;
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < kFusedPageLanes; ++i) {
+    const bool sel = pk[i] != 0u && pk[i] >= t1;
+    const uint64_t bal = __ballot(sel);
+    if (sel) sh.pages[before + ballot_rank(bal)] = w * (kFusedPageLanes * kWave) + i * kWave + l;
+    before += __popcll(bal);
+  }
+  __syncthreads();
+
+  // kept entries of the candidate pages, looked up in parallel
+  for (int c = tid; c < ncand; c += kFusedThreads) sh.pagej[c] = kb[sh.pages[c]];
+  __syncthreads();
+
+  // 3. survivors per candidate page.  Wave w scans the contiguous candidate
+  // range [c_lo, c_hi), kFusedBatch pages per step with all loads in flight;
+  // lane l looks at slot l of each page.
+  const int per_wave = (ncand + kFusedWaves - 1) / kFusedWaves;
+  const int c_lo = min(ncand, w * per_wave), c_hi = min(ncand, c_lo + per_wave);
+  auto survivor_key = [&](int c, float v, uint32_t* key_out) {
+    const int j = sh.pagej[c];
+    const uint32_t key = ord_key(v);
+    *key_out = key;
+    return j >= 0 && j < bt.max_blocks && j * kBlock + l <= qr && key >= t1;
+  };
+  for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
+    float v[kFusedBatch];
+#pragma unroll
+    for (int u = 0; u < kFusedBatch; ++u) {
+      const int c = c0 + u;
+      v[u] = (c < c_hi) ? sc[size_t(sh.pages[c]) * kBlock + l] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kFusedBatch; ++u) {
+      const int c = c0 + u;
+      uint32_t key;
+      const bool ok = (c < c_hi) && survivor_key(c, v[u], &key);
+      const uint64_t bal = __ballot(ok);
+      if (c < c_hi && l == 0) sh.pcount[c] = __popcll(bal);
+    }
+  }
+  __syncthreads();
+  const int nsurv = block_exclusive_scan(sh.pcount, ncand, sh.scan);
+  if (nsurv > kFusedCap || nsurv < K) {
+    if (tid == 0) done[row] = 0;
+    return;
+  }
+  // 4. collect them in position order
+  for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
+    float v[kFusedBatch];
+#pragma unroll
+    for (int u = 0; u < kFusedBatch; ++u) {
+      const int c = c0 + u;
+      v[u] = (c < c_hi) ? sc[size_t(sh.pages[c]) * kBlock + l] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kFusedBatch; ++u) {
+      const int c = c0 + u;
+      uint32_t key;
+      const bool ok = (c < c_hi) && survivor_key(c, v[u], &key);
+      const uint64_t bal = __ballot(ok);
+      if (ok) {
+        const int o = sh.pcount[c] + ballot_rank(bal);
+        sh.skey[o] = key;
+        sh.spos[o] = sh.pagej[c] * kBlock + l;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 5. exact top-K of the survivors (element s = w*512 + i*64 + l held by lane l)
+  uint32_t key[kFusedPerLane];
+#pragma unroll
+  for (int i = 0; i < kFusedPerLane; ++i) {
+    const int s = w * (kFusedPerLane * kWave) + i * kWave + l;
+    key[i] = (s < nsurv) ? sh.skey[s] : 0u;
+  }
+  uint32_t thr = 0;                       // exactly K survivors: take them all
+  int n_eq = 0;
+  if (nsurv > K) {
+    uint32_t smin, smax;
+    int tot;
+    block_key_stats<kFusedThreads, kFusedPerLane>(key, sh.t, &tot, &smin, &smax);
+    radix_select_regs<kFusedThreads, kFusedPerLane>(key, K, smin, smax, sh.t, &thr, &n_eq);
+  }
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedPerLane; ++i) {
+    gt += (key[i] != 0u && key[i] > thr) ? 1 : 0;
+    eq += (key[i] != 0u && key[i] == thr) ? 1 : 0;
+  }
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  __syncthreads();
+  if (l == 0) {
+    sh.t.wave_a[w] = gt;
+    sh.t.wave_b[w] = eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int i = 0; i < kFusedWaves; ++i) {
+    gt_before += (i < w) ? sh.t.wave_a[i] : 0;
+    eq_before += (i < w) ? sh.t.wave_b[i] : 0;
+  }
+  int eq_base = eq_before;
+  int out_base = gt_before + min(n_eq, eq_before);
+  int32_t* o = topk_out + size_t(row) * K;
+#pragma unroll
+  for (int i = 0; i < kFusedPerLane; ++i) {
+    const bool is_eq = key[i] != 0u && key[i] == thr;
+    const uint64_t eqb = __ballot(is_eq);
+    const bool sel = (key[i] != 0u && key[i] > thr) || (is_eq && eq_base + ballot_rank(eqb) < n_eq);
+    const uint64_t selb = __ballot(sel);
+    const int rank = out_base + ballot_rank(selb);
+    if (sel && rank < K) o[rank] = sh.spos[w * (kFusedPerLane * kWave) + i * kWave + l];
+    eq_base += __popcll(eqb);
+    out_base += __popcll(selb);
+  }
+  if (tid == 0) done[row] = 1;
+}
+
+// grid (rows, chunks of this level).
+template <bool FIRST, bool FINAL>
+__global__ void __launch_bounds__(kTopkThreads) k_topk_level(LevelArgs a) {
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x;           // b * R + r
+  const int c = blockIdx.y;             // chunk of this level
+  const int b = row / a.bt.R, r = row % a.bt.R;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  const int K = a.K;
+  const size_t mb = size_t(a.bt.max_blocks);
+  const int seg = c * kChunk + w * kSeg;  // first candidate of this wave
+  if (a.done && a.done[row]) return;      // the fused kernel already answered this row
+
+  uint32_t key[kPerLane];
+  int my_kept = -1;                       // level 0: kept entry of block i (lane i)
+  if (FIRST) {
+    int cnt = a.kept_count[b];
+    cnt = cnt < 0 ? 0 : (cnt > a.bt.max_blocks ? a.bt.max_blocks : cnt);
+    const int n = cnt * kBlock;
+    if (c * kChunk >= n) {                // the whole chunk is past the kept list
+      if (!FINAL && tid == 0) a.out_counts[size_t(row) * a.out_chunks + c] = 0;
+      if (FINAL)
+        for (int i = tid; i < K; i += kTopkThreads) a.topk_out[size_t(row) * K + i] = -1;
+      return;
+    }
+    const int qr = a.bt.qpos[b] + r;
+    const uint32_t lowest = a.thr_key ? max(a.thr_key[row], 1u) : 1u;
+    const float* s = a.scores + size_t(row) * mb * kBlock;
+    if (l < kPerLane && seg + l * kBlock < n) my_kept = a.kept[size_t(b) * mb + seg / kBlock + l];
+    float v[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int x = seg + i * kBlock + l;
+      v[i] = (x < n) ? s[x] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int j = __builtin_amdgcn_readlane(my_kept, i);
+      const bool ok = j >= 0 && j < a.bt.max_blocks && j * kBlock + l <= qr;
+      const uint32_t kk = ord_key(v[i]);
+      key[i] = (ok && kk >= lowest) ? kk : 0u;
+    }
+  } else {
+    const uint32_t* ik = a.in_keys + size_t(row) * a.in_chunks * K;
+    const int32_t* ic = a.in_counts + size_t(row) * a.in_chunks;
+    // survivor slot sidx = g * K + within, advanced by 64 per step (no division)
+    int g = (seg + l) / K, within = (seg + l) - g * K;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int sidx = seg + i * kBlock + l;
+      const int cnt = (g < a.in_chunks) ? ic[g] : 0;
+      key[i] = (within < cnt) ? ik[sidx] : 0u;
+      within += kBlock;
+      while (within >= K) {
+        within -= K;
+        ++g;
+      }
+    }
+  }
+
+  int total_valid;
+  uint32_t kmin, kmax;
+  block_key_stats<kTopkThreads, kPerLane>(key, sh, &total_valid, &kmin, &kmax);
+  const int want = min(K, total_valid);
+  uint32_t thr = 0;                       // select-all: every key > 0
+  int n_eq = 0;
+  if (want > 0 && want < total_valid)
+    radix_select_regs<kTopkThreads, kPerLane>(key, want, kmin, kmax, sh, &thr, &n_eq);
+
+  // ---- ordered emission ----
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    gt += (key[i] != 0u && key[i] > thr) ? 1 : 0;
+    eq += (key[i] != 0u && key[i] == thr) ? 1 : 0;
+  }
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  __syncthreads();
+  if (l == 0) {
+    sh.wave_a[w] = gt;
+    sh.wave_b[w] = eq;
+  }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0, gt_all = 0, eq_all = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) {
+    gt_before += (i < w) ? sh.wave_a[i] : 0;
+    eq_before += (i < w) ? sh.wave_b[i] : 0;
+    gt_all += sh.wave_a[i];
+    eq_all += sh.wave_b[i];
+  }
+  const int total = want > 0 ? gt_all + min(n_eq, eq_all) : 0;
+  int eq_base = eq_before;
+  int out_base = gt_before + min(n_eq, eq_before);
+  int rk[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const bool is_eq = key[i] != 0u && key[i] == thr;
+    const uint64_t eqb = __ballot(is_eq);
+    const bool sel = want > 0 &&
+        ((key[i] != 0u && key[i] > thr) || (is_eq && eq_base + ballot_rank(eqb) < n_eq));
+    const uint64_t selb = __ballot(sel);
+    rk[i] = sel ? out_base + ballot_rank(selb) : -1;
+    eq_base += __popcll(eqb);
+    out_base += __popcll(selb);
+  }
+  const int32_t* ip = FIRST ? nullptr : a.in_pos + size_t(row) * a.in_chunks * K;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int rank = rk[i];
+    if (rank >= 0 && rank < K) {
+      const int pos = FIRST ? __builtin_amdgcn_readlane(my_kept, i) * kBlock + l
+                            : ip[seg + i * kBlock + l];
+      if (FINAL) {
+        a.topk_out[size_t(row) * K + rank] = pos;
+      } else {
+        const size_t o = size_t(row) * a.out_chunks * K + size_t(c) * K + rank;
+        a.out_keys[o] = key[i];
+        a.out_pos[o] = pos;
+      }
+    }
+  }
+  if (FINAL) {
+    for (int i = min(total, K) + tid; i < K; i += kTopkThreads) a.topk_out[size_t(row) * K + i] = -1;
+  } else if (tid == 0) {
+    a.out_counts[size_t(row) * a.out_chunks + c] = min(total, K);
+  }
 }
 
 __global__ void __launch_bounds__(256)
@@ -91,12 +597,90 @@ k_miss(spin_batch bt, int K, const int32_t* full, const uint8_t* flags, float* m
   }
 }
 
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 }  // namespace
 
-hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const int32_t* kept,
-                       const int32_t* kept_count, int32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(bt.B * bt.R), dim3(kTopkThreads), 0, s, bt, topk, scores, kept,
-                     kept_count, out);
+TopkPlan topk_plan(int rows, int max_blocks, int K) {
+  TopkPlan p;
+  p.rows = rows;
+  p.K = K;
+  p.levels = 0;
+  int64_t n = int64_t(max_blocks) * kBlock;
+  int64_t widest = 0;
+  while (true) {
+    const int64_t chunks = (n + kChunk - 1) / kChunk;
+    p.chunks[p.levels++] = int(chunks);
+    if (chunks <= 1) break;
+    if (chunks > widest) widest = chunks;
+    n = chunks * K;
+  }
+  p.buf_elems = size_t(rows) * size_t(widest) * size_t(K);
+  p.count_elems = size_t(rows) * size_t(widest);
+  p.bytes = 2 * (align256(p.buf_elems * 4) * 2 + align256(p.count_elems * 4)) +
+            2 * align256(size_t(rows) * 4) + 256;
+  return p;
+}
+
+hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_max,
+                       const int32_t* kept, const int32_t* kept_count, int32_t* out, void* ws,
+                       hipStream_t s) {
+  const int rows = bt.B * bt.R;
+  const TopkPlan p = topk_plan(rows, bt.max_blocks, topk);
+  char* base = static_cast<char*>(ws);
+  uint32_t* keys[2] = {nullptr, nullptr};
+  int32_t* pos[2] = {nullptr, nullptr};
+  int32_t* cnts[2] = {nullptr, nullptr};
+  uint32_t* thr = nullptr;
+  int32_t* done = nullptr;
+  if (base) {
+    size_t off = 0;
+    for (int i = 0; i < 2; ++i) {
+      keys[i] = reinterpret_cast<uint32_t*>(base + off);
+      off += align256(p.buf_elems * 4);
+      pos[i] = reinterpret_cast<int32_t*>(base + off);
+      off += align256(p.buf_elems * 4);
+      cnts[i] = reinterpret_cast<int32_t*>(base + off);
+      off += align256(p.count_elems * 4);
+    }
+    if (page_max) {
+      thr = reinterpret_cast<uint32_t*>(base + off);
+      off += align256(size_t(rows) * 4);
+      done = reinterpret_cast<int32_t*>(base + off);
+    }
+  }
+  if (thr)
+    hipLaunchKernelGGL(k_topk_fused, dim3(rows), dim3(kFusedThreads), 0, s, bt, topk, scores,
+                       page_max, kept, kept_count, out, thr, done);
+  LevelArgs a;
+  a.bt = bt;
+  a.K = topk;
+  a.scores = scores;
+  a.kept = kept;
+  a.kept_count = kept_count;
+  a.thr_key = thr;
+  a.done = done;
+  a.topk_out = out;
+  for (int lv = 0; lv < p.levels; ++lv) {
+    const bool first = lv == 0, final = lv == p.levels - 1;
+    a.in_keys = first ? nullptr : keys[(lv - 1) & 1];
+    a.in_pos = first ? nullptr : pos[(lv - 1) & 1];
+    a.in_counts = first ? nullptr : cnts[(lv - 1) & 1];
+    a.in_chunks = first ? 0 : p.chunks[lv - 1];
+    a.out_keys = keys[lv & 1];
+    a.out_pos = pos[lv & 1];
+    a.out_counts = cnts[lv & 1];
+    a.out_chunks = p.chunks[lv];
+    const dim3 grid(unsigned(rows), unsigned(p.chunks[lv]));
+    if (first && final)
+      hipLaunchKernelGGL((k_topk_level<true, true>), grid, dim3(kTopkThreads), 0, s, a);
+    else if (first)
+      hipLaunchKernelGGL((k_topk_level<true, false>), grid, dim3(kTopkThreads), 0, s, a);
+    else if (final)
+      hipLaunchKernelGGL((k_topk_level<false, true>), grid, dim3(kTopkThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_topk_level<false, false>), grid, dim3(kTopkThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -1,16 +1,17 @@
 // EMA update from the observed slots, with prefix-valid MTP replay.
 //
-// One wave per kept block j (kept index k).  With a accepted drafts, rows
-// 0..a are applied in row order; row r observes kept slots i <= q + r and
-// updates V_i and D_{q+r-i}.
-//   V: lane t owns slot 64j + t and folds the rows in order; the block's new
-//      maximum refreshes VB_j.
+// Each wave takes kUpdBlocks consecutive entries of the kept list.  With a
+// accepted drafts, rows 0..a are applied in row order; row r observes kept
+// slots i <= q + r and updates V_i and D_{q+r-i}.
+//   V: lane t owns slot 64j + t of kept block j and folds the rows in order;
+//      the block's new maximum refreshes VB_j.
 //   D: offset o is owned by the wave of the block holding i0 = q - o (the slot
 //      row 0 sees at that offset); the rows reach i0 + r, which can spill into
-//      block j + 1 (read from kept index k + 1 when that block is kept).  When
-//      block j - 1 is not kept, the wave of block j also owns the offsets with
-//      i0 in 64j - a .. 64j - 1, whose later rows land in block j.  Each offset
-//      therefore has exactly one writer and sees its rows in order.
+//      block j + 1 (its scores are the next kept entry when that block is
+//      kept).  When block j - 1 is not kept, block j's owner also takes the
+//      offsets with i0 in 64j - a .. 64j - 1, whose later rows land in block j.
+//      Each offset therefore has exactly one writer and sees its rows in order.
+// All loads of a wave's blocks are issued before any is used.
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -18,6 +19,7 @@ namespace spin {
 namespace {
 
 constexpr int kUpdWaves = 4;
+constexpr int kUpdBlocks = 4;     // kept entries per wave
 
 __global__ void __launch_bounds__(kUpdWaves * kWave)
 k_update(SpinView v, int layer, spin_batch bt, const int32_t* accepted, const float* scores,
@@ -47,65 +49,99 @@ k_update(SpinView v, int layer, spin_batch bt, const int32_t* accepted, const fl
   const size_t row = size_t(layer) * v.S + s;
   if (lead) v.step[row] += 1;
 
-  const int k = blockIdx.x * kUpdWaves + threadIdx.x / kWave;
-  if (k >= cnt) return;
+  const int k0 = (blockIdx.x * kUpdWaves + threadIdx.x / kWave) * kUpdBlocks;
+  if (k0 >= cnt) return;
+  const int l = lane_id();
   const size_t mb = size_t(bt.max_blocks);
   const int32_t* kb = kept + size_t(b) * mb;
-  const int j = kb[k];
-  if (j < 0 || j >= bt.max_blocks) {
-    if (lane_id() == 0) flag_error(v.err, SPIN_ERR_KEPT);
-    return;
+
+  // kept entries k0-1 .. k0+kUpdBlocks (lane m holds entry k0 - 1 + m)
+  int e = -2;
+  if (l < kUpdBlocks + 2) {
+    const int k = k0 - 1 + l;
+    if (k >= 0 && k < cnt) e = kb[k];
   }
-  const bool next_kept = (k + 1 < cnt) && kb[k + 1] == j + 1;
-  const bool prev_kept = (k > 0) && kb[k - 1] == j - 1;
+  int jj[kUpdBlocks + 2];
+#pragma unroll
+  for (int m = 0; m < kUpdBlocks + 2; ++m) jj[m] = __shfl(e, m, kWave);
 
   const float alpha = v.alpha, beta = 1.0f - v.alpha;
   float* V = v.V + row * v.max_ctx;
   float* D = v.D + row * v.max_ctx;
-  const int l = lane_id();
-  const float* sc = scores + size_t(b) * bt.R * mb * kBlock;   // row r at + r * mb * 64
+  float* VB = v.VB + row * v.max_blocks;
   const size_t rstride = mb * kBlock;
-  const size_t here = size_t(k) * kBlock;
+  const float* sc = scores + size_t(b) * bt.R * rstride;
 
-  // V of slot i = 64j + l.
-  const int i = j * kBlock + l;
-  float x = (i < v.max_ctx) ? V[i] : -INFINITY;
-  bool changed = false;
-  for (int r = 0; r <= a; ++r) {
-    if (i <= q + r) {
-      x = ema_observe(x, sc[r * rstride + here + l], alpha, beta);
+  // Issue the loads of every block first.
+  float x[kUpdBlocks], y[kUpdBlocks], s0[kUpdBlocks];
+  bool okb[kUpdBlocks];
+#pragma unroll
+  for (int m = 0; m < kUpdBlocks; ++m) {
+    const int j = jj[m + 1];
+    const int k = k0 + m;
+    okb[m] = k < cnt && j >= 0 && j < bt.max_blocks;
+    const int i = j * kBlock + l;
+    x[m] = (okb[m] && i < v.max_ctx) ? V[i] : -INFINITY;
+    y[m] = (okb[m] && i <= q) ? D[q - i] : 0.0f;
+    s0[m] = okb[m] ? sc[size_t(k) * kBlock + l] : 0.0f;
+  }
+#pragma unroll
+  for (int m = 0; m < kUpdBlocks; ++m) {
+    const int k = k0 + m;
+    if (k < cnt && !okb[m] && l == 0) flag_error(v.err, SPIN_ERR_KEPT);
+  }
+
+#pragma unroll
+  for (int m = 0; m < kUpdBlocks; ++m) {
+    if (!okb[m]) continue;
+    const int j = jj[m + 1];
+    const int k = k0 + m;
+    const bool next_kept = jj[m + 2] == j + 1 && k + 1 < cnt;
+    const bool prev_kept = jj[m] == j - 1 && k > 0;
+    const size_t here = size_t(k) * kBlock;
+    const int i = j * kBlock + l;
+
+    // V of slot i, rows 0..a in order (row 0's score is already loaded)
+    float xv = x[m];
+    bool changed = false;
+    if (i <= q) {
+      xv = ema_observe(xv, s0[m], alpha, beta);
       changed = true;
     }
-  }
-  if (changed) V[i] = x;
-  const float bmax = wave_max(x);
-  if (l == 0) v.VB[row * v.max_blocks + j] = bmax;
-
-  // D at offset q - i0 for i0 = 64j + l.
-  if (i <= q) {
-    const int o = q - i;
-    float y = D[o];
-    for (int r = 0; r <= a; ++r) {
-      const int t = l + r;                       // slot i + r, relative to block j
-      if (t < kBlock) {
-        y = ema_observe(y, sc[r * rstride + here + t], alpha, beta);
-      } else if (next_kept) {
-        y = ema_observe(y, sc[r * rstride + here + kBlock + (t - kBlock)], alpha, beta);
+    for (int r = 1; r <= a; ++r) {
+      if (i <= q + r) {
+        xv = ema_observe(xv, sc[r * rstride + here + l], alpha, beta);
+        changed = true;
       }
     }
-    D[o] = y;
-  }
-  // Offsets whose row-0 slot lies just before block j, in a block not kept.
-  if (!prev_kept && l < a) {
-    const int i0 = j * kBlock - 1 - l;
-    if (i0 <= q) {
-      const int o = q - i0;
-      float y = D[o];
-      for (int r = 0; r <= a; ++r) {
-        const int t = i0 + r - j * kBlock;       // slot i0 + r, relative to block j
-        if (t >= 0) y = ema_observe(y, sc[r * rstride + here + t], alpha, beta);
+    if (changed && i < v.max_ctx) V[i] = xv;
+    const float bmax = wave_max(i < v.max_ctx ? xv : -INFINITY);
+    if (l == 0) VB[j] = bmax;
+
+    // D at offset q - i for row-0 slot i (rows reach i + r)
+    if (i <= q) {
+      float yv = ema_observe(y[m], s0[m], alpha, beta);
+      for (int r = 1; r <= a; ++r) {
+        const int t = l + r;
+        if (t < kBlock)
+          yv = ema_observe(yv, sc[r * rstride + here + t], alpha, beta);
+        else if (next_kept)
+          yv = ema_observe(yv, sc[r * rstride + here + t], alpha, beta);
       }
-      D[o] = y;
+      D[q - i] = yv;
+    }
+    // offsets whose row-0 slot lies just before block j, in a block not kept
+    if (!prev_kept && l < a) {
+      const int i0 = j * kBlock - 1 - l;
+      if (i0 <= q) {
+        const int o = q - i0;
+        float yv = D[o];
+        for (int r = 0; r <= a; ++r) {
+          const int t = i0 + r - j * kBlock;
+          if (t >= 0) yv = ema_observe(yv, sc[r * rstride + here + t], alpha, beta);
+        }
+        D[o] = yv;
+      }
     }
   }
 }
@@ -115,7 +151,8 @@ k_update(SpinView v, int layer, spin_batch bt, const int32_t* accepted, const fl
 hipError_t launch_update(const SpinView& v, int layer, const spin_batch& bt,
                          const int32_t* accepted, const float* scores, const int32_t* kept,
                          const int32_t* kept_count, hipStream_t s) {
-  const dim3 grid(unsigned((bt.max_blocks + kUpdWaves - 1) / kUpdWaves), unsigned(bt.B));
+  const int per_wg = kUpdWaves * kUpdBlocks;
+  const dim3 grid(unsigned((bt.max_blocks + per_wg - 1) / per_wg), unsigned(bt.B));
   hipLaunchKernelGGL(k_update, grid, dim3(kUpdWaves * kWave), 0, s, v, layer, bt, accepted,
                      scores, kept, kept_count);
   return hipGetLastError();

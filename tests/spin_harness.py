@@ -83,6 +83,8 @@ class Rig:
         self.scores = torch.zeros(B, R, max_blocks * BLOCK, dtype=torch.float32, device=dev)
         self.topk = torch.zeros(B, R, cfg.topk, dtype=torch.int32, device=dev)
         self.batch = spin.make_batch(self.slot, self.qpos, R, max_blocks)
+        self.topk_ws = torch.empty(max(256, spin.spin_topk_workspace_bytes(self.batch, cfg.topk)),
+                                   dtype=torch.uint8, device=dev)
 
     @property
     def h(self):

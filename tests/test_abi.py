@@ -61,7 +61,17 @@ def test_null_and_range_arguments_rejected_before_any_launch():
     assert lib.spin_predict_blocks(None, 0, None, 5000, None, None, None, None) == spin.SPIN_EINVAL
     assert lib.spin_update(None, 0, None, None, None, None, None) == spin.SPIN_EINVAL
     b = spin.SpinBatch(1, 1, 16, 0, None, None)
-    assert lib.spin_topk_scores(ctypes.byref(b), 64, None, None, None, None, None) == spin.SPIN_EINVAL
+    assert lib.spin_topk_scores(ctypes.byref(b), 64, None, None, None, None, None, None, 0,
+                                None) == spin.SPIN_EINVAL
+    # a row long enough for several top-k levels needs a workspace
+    big = spin.SpinBatch(2, 1, 8192, 0, None, ctypes.c_void_p(16))
+    n = ctypes.c_size_t()
+    assert lib.spin_topk_workspace_bytes(ctypes.byref(big), 2048, ctypes.byref(n)) == spin.SPIN_OK
+    assert n.value >= 2 * 32 * 2048 * 8
+    assert lib.spin_topk_scores(ctypes.byref(big), 2048, ctypes.c_void_p(256), None,
+                                ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                                None, 0, None) == spin.SPIN_EINVAL
+    assert lib.spin_topk_workspace_bytes(ctypes.byref(big), 2050, ctypes.byref(n)) == spin.SPIN_EINVAL
     assert lib.spin_measure_miss(ctypes.byref(b), 0, None, None, None, None) == spin.SPIN_EINVAL
     assert "invalid" in spin.spin_status_string(spin.SPIN_EINVAL)
 

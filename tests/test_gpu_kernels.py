@@ -93,11 +93,14 @@ def test_indexer_scores_parity(gpu_lib, R):
     rig.kept.copy_(torch.as_tensor(kt))
     rig.kept_count.copy_(torch.as_tensor([len(k) for k in kept], dtype=torch.int32))
     rig.scores.fill_(12345.0)
+    pmax = torch.full((B, R, mb), 777.0, device=DEV)
     _say("indexer R", R)
     spin.spin_quantize_q(rig.h, rig.batch, q.to(DEV), w.to(DEV))
     spin.spin_indexer_scores(rig.h, rig.batch, codes.to(DEV), sc.to(DEV),
-                             torch.as_tensor(table).to(DEV), rig.kept, rig.kept_count, rig.scores)
+                             torch.as_tensor(table).to(DEV), rig.kept, rig.kept_count, rig.scores,
+                             pmax)
     torch.cuda.synchronize()
+    gpm = np_(pmax)
     kv = O.e4m3fn_decode(np_(codes))
     scv = np_(sc).astype(np.float64)
     got = np_(rig.scores)
@@ -108,39 +111,80 @@ def test_indexer_scores_parity(gpu_lib, R):
         n = len(kept[b]) * 64
         assert_scores_close(got[b, :, :n], ref, mag, f"b{b}")
         assert np.all(got[b, :, n:] == 12345.0)                  # nothing written past kept
+        # page maxima: exactly the max of the GPU's own page scores
+        nk = len(kept[b])
+        if nk:
+            own = got[b, :, :n].reshape(R, nk, 64).max(axis=2)
+            assert np.array_equal(gpm[b, :, :nk], own)
+        assert np.all(gpm[b, :, nk:] == 777.0)
     assert rig.state.error() == 0
 
 
 # ------------------------------------------------------------------- top-k
-@pytest.mark.parametrize("case", ["random", "ties", "short", "zeros"])
+TOPK_CASES = {
+    # name: (rows R, max_blocks, K, pattern); "+pm" cases pass page maxima
+    "random": (2, 120, 512, "random"),
+    "ties": (2, 120, 512, "ties"),
+    "short": (2, 120, 512, "short"),
+    "zeros": (2, 120, 512, "zeros"),
+    "two-levels": (1, 2048, 2048, "random"),
+    "three-levels-ties": (2, 8192, 2048, "ties"),
+    "k-equals-chunk-quarter": (1, 1500, 4096, "random"),
+    "pm-random": (1, 8192, 2048, "random"),
+    "pm-clustered": (2, 8192, 2048, "clustered"),
+    "pm-equal-maxima": (1, 4096, 2048, "plateau"),
+    "pm-few-pages": (2, 1000, 2048, "random"),
+}
+
+
+@pytest.mark.parametrize("case", list(TOPK_CASES))
 def test_topk_exact_on_identical_scores(gpu_lib, case):
-    rng = np.random.default_rng(["random", "ties", "short", "zeros"].index(case))
-    B, R, mb, K = 3, 2, 120, 512
-    qpos = np.array([64 * 110 + 5, 64 * 100 + 63, 64 * 5 + 3], dtype=np.int64)
+    R, mb, K, pattern = TOPK_CASES[case]
+    rng = np.random.default_rng(list(TOPK_CASES).index(case))
+    B = 3
+    qpos = np.array([64 * (mb - 10) + 5, 64 * (mb - 20) + 63, 64 * 5 + 3], dtype=np.int64)
     kept = [np.sort(rng.choice(nblocks(q + R - 1), nblocks(q + R - 1) * 2 // 3, replace=False))
             for q in qpos]
     kept = [np.union1d(k, [nblocks(q + R - 1) - 1]) for k, q in zip(kept, qpos)]
-    if case == "short":
+    if pattern == "short":
         kept[0] = kept[0][:3]                                    # fewer candidates than K
+    if case == "two-levels":
+        kept[1] = np.arange(nblocks(qpos[1]))                    # a whole row kept
     sc = rng.random((B, R, mb * 64)).astype(np.float32)
-    if case == "ties":
+    if pattern == "ties":
         sc = (np.round(sc * 16) / 16).astype(np.float32)
-    if case == "zeros":
+    if pattern == "zeros":
         sc[:] = 0.0
         sc[:, :, ::7] = -0.0
         sc[:, :, ::13] = 1.0
-    cfg_rows = []
-    batch_slot = torch.zeros(B, dtype=torch.int32, device=DEV)
+    if pattern == "clustered":                                   # every large score in 40 pages
+        sc *= 0.5
+        sc[:, :, 64 * 100: 64 * 140] += 10.0
+    if pattern == "plateau":                                     # every page has the same maximum
+        sc = np.minimum(sc, np.float32(0.75))
     qp = torch.as_tensor(qpos.astype(np.int32), device=DEV)
-    bt = spin.make_batch(batch_slot, qp, R, mb)
+    bt = spin.make_batch(torch.zeros(B, dtype=torch.int32, device=DEV), qp, R, mb)
     kt = np.full((B, mb), -1, dtype=np.int32)
     for b in range(B):
         kt[b, : len(kept[b])] = kept[b]
     kept_d = torch.as_tensor(kt, device=DEV)
     cnt_d = torch.as_tensor([len(k) for k in kept], dtype=torch.int32, device=DEV)
     out = torch.zeros(B, R, K, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(256, spin.spin_topk_workspace_bytes(bt, K)), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)                                               # stale contents must not matter
+    pm = None
+    if case.startswith("pm-"):
+        # page maxima over each row's valid slots, in kept order (as the indexer writes them)
+        pmh = np.full((B, R, mb), -np.inf, dtype=np.float32)
+        for b in range(B):
+            for r in range(R):
+                nk = len(kept[b])
+                slot = (kept[b][:, None] * 64 + np.arange(64)).reshape(nk, 64)
+                v = np.where(slot <= qpos[b] + r, sc[b, r, : nk * 64].reshape(nk, 64), -np.inf)
+                pmh[b, r, :nk] = v.max(axis=1)
+        pm = torch.as_tensor(pmh, device=DEV)
     _say("topk", case)
-    spin.spin_topk_scores(bt, K, torch.as_tensor(sc, device=DEV), kept_d, cnt_d, out)
+    spin.spin_topk_scores(bt, K, torch.as_tensor(sc, device=DEV), kept_d, cnt_d, out, ws, pm)
     torch.cuda.synchronize()
     got = np_(out)
     for b in range(B):
@@ -148,18 +192,19 @@ def test_topk_exact_on_identical_scores(gpu_lib, case):
             ref = O.topk_positions(sc[b, r, : len(kept[b]) * 64].astype(np.float64), kept[b],
                                    int(qpos[b]) + r, K)
             assert np.array_equal(got[b, r], ref), (case, b, r)
-    del cfg_rows
 
 
 # --------------------------------------------------------------- predictor
-@pytest.mark.parametrize("R,keep_bp,explore_bp,step", [
-    (1, 6000, 500, 3), (1, 5000, 0, 1), (1, 8000, 2500, 7), (4, 5000, 1000, 2),
-    (4, 6000, 500, 0), (1, 10000, 500, 4), (1, 0, 500, 4), (2, 9990, 500, 5)])
-def test_predict_exact(gpu_lib, R, keep_bp, explore_bp, step):
+@pytest.mark.parametrize("R,keep_bp,explore_bp,step,blocks", [
+    (1, 6000, 500, 3, 200), (1, 5000, 0, 1, 200), (1, 8000, 2500, 7, 200), (4, 5000, 1000, 2, 200),
+    (4, 6000, 500, 0, 200), (1, 10000, 500, 4, 200), (1, 0, 500, 4, 200), (2, 9990, 500, 5, 200),
+    # past the LDS-resident limit of the selection kernel: the workspace path
+    (1, 5000, 500, 3, 12000), (4, 6000, 1000, 2, 12000)])
+def test_predict_exact(gpu_lib, R, keep_bp, explore_bp, step, blocks):
     rng = np.random.default_rng(keep_bp + R)
-    B, ctx = 4, 64 * 200
+    B, ctx = 4, 64 * blocks
     mb = nblocks(ctx - 1)
-    qpos = np.array([ctx - R, 64 * 150 + 63 - 1, 64 * 3 + 1, 40], dtype=np.int64)
+    qpos = np.array([ctx - R, 64 * (blocks * 3 // 4) + 63 - 1, 64 * 3 + 1, 40], dtype=np.int64)
     cfg = spin.make_config(2, B, ctx, 256, max_rows=R, explore_bp=explore_bp, seed=0xABCDEF)
     rig = Rig(cfg, B, R, mb)
     rids = [1000 + 7 * b for b in range(B)]

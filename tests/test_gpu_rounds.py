@@ -89,7 +89,8 @@ def test_tiny4k_trajectory_with_oracle_scores(gpu_lib):
         sc = np.full((1, 1, wl.blocks * 64), NEG, dtype=np.float32)
         sc[0, 0, : len(gk) * 64] = ref["scores"][0].astype(np.float32)
         rig.scores.copy_(torch.as_tensor(sc))
-        spin.spin_topk_scores(rig.batch, wl.topk, rig.scores, rig.kept, rig.kept_count, rig.topk)
+        spin.spin_topk_scores(rig.batch, wl.topk, rig.scores, rig.kept, rig.kept_count, rig.topk,
+                              rig.topk_ws)
         spin.spin_update(rig.h, 0, rig.batch, rig.scores, rig.kept, rig.kept_count)
         torch.cuda.synchronize()
         s32 = {int(x): float(v) for x, v in zip(
