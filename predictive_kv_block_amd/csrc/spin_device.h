@@ -19,16 +19,39 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
 }
 
 // ------------------------------------------------------------ wave reductions
+// DPP data movement within a wave64: quad permutes, row mirrors and the row
+// broadcasts of lanes 15 and 31 fold all 64 lanes into lane 63, which is then
+// read back as a scalar (no LDS round trips).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;            // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;            // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<kDppXor1, 0xF>(x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<kDppXor2, 0xF>(x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<kDppRowHalfMirror, 0xF>(x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<kDppRowMirror, 0xF>(x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<kDppRowBcast15, 0xA>(x))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(dpp<kDppRowBcast31, 0xC>(x))));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp<kDppXor1, 0xF>(v);
+  v += dpp<kDppXor2, 0xF>(v);
+  v += dpp<kDppRowHalfMirror, 0xF>(v);
+  v += dpp<kDppRowMirror, 0xF>(v);
+  v += dpp<kDppRowBcast15, 0xA>(v);
+  v += dpp<kDppRowBcast31, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }

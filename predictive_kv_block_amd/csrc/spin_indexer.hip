@@ -32,6 +32,20 @@ constexpr int kDim = 128;
 #ifndef SPIN_IDX_NONTEMPORAL
 #define SPIN_IDX_NONTEMPORAL 0
 #endif
+#ifndef SPIN_IDX_PREFETCH
+#define SPIN_IDX_PREFETCH 1            // pages in flight ahead of the one on the MFMAs
+#endif
+#ifndef SPIN_IDX_NT_STORE
+#define SPIN_IDX_NT_STORE 0            // streaming (non-temporal) score stores
+#endif
+#ifndef SPIN_IDX_WAVES_PER_EU
+#define SPIN_IDX_WAVES_PER_EU 0        // occupancy target for the register allocator (0: none)
+#endif
+#if SPIN_IDX_WAVES_PER_EU > 0
+#define SPIN_IDX_OCCUPANCY __attribute__((amdgpu_waves_per_eu(SPIN_IDX_WAVES_PER_EU)))
+#else
+#define SPIN_IDX_OCCUPANCY
+#endif
 constexpr int kIdxWaves = SPIN_IDX_WAVES;
 constexpr int kPagesPerWave = SPIN_IDX_PAGES_PER_WAVE;
 
@@ -46,15 +60,16 @@ __device__ __forceinline__ int q_exponent(float amax) {
   return x - (f <= 0.875f ? 9 : 8);
 }
 
-// grid (B, R), 256 threads; wave w handles heads w, w+4, ...; lane l the
-// elements 2l and 2l+1 of a head.
+// grid (B, R, 16), 256 threads; wave w handles head 4z + w; lane l the
+// elements 2l and 2l+1 of the head.
 __global__ void __launch_bounds__(256)
 k_quantize(SpinView v, spin_batch bt, const uint16_t* q, const float* w) {
   const int b = blockIdx.x, r = blockIdx.y;
   const int l = lane_id();
   const size_t in_row = size_t(b) * bt.R + r;
   const size_t ws_row = size_t(b) * v.max_rows + r;
-  for (int h = threadIdx.x / kWave; h < kHeads; h += 4) {
+  {
+    const int h = blockIdx.z * 4 + threadIdx.x / kWave;
     const uint32_t pair =
         *reinterpret_cast<const uint32_t*>(q + (in_row * kHeads + h) * kDim + 2 * l);
     const float x0 = bf16_bits_to_f32(pair & 0xFFFFu), x1 = bf16_bits_to_f32(pair >> 16);
@@ -86,7 +101,7 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
 // and overlaps the staging of the queries in LDS; the keys of page m+1 are in
 // flight while page m runs on the MFMAs.
 template <int R>
-__global__ void __launch_bounds__(kIdxWaves * kWave)
+__global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
           const int32_t* kept, const int32_t* kept_count, float* scores, float* page_max) {
@@ -139,15 +154,20 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   const int n16 = l & 15;     // M row of A / N column of B
   const int npages = min(kPagesPerWave, (cnt - first - wave + kIdxWaves - 1) / kIdxWaves);
 
-  v8i kb[4], kn[4];
+  constexpr int PF = SPIN_IDX_PREFETCH > 0 ? SPIN_IDX_PREFETCH : 1;
+  constexpr bool kPrefetch = SPIN_IDX_PREFETCH > 0;
+  v8i kb[4], kn[PF][4];
   auto load_page = [&](v8i* dst, int p) {
     const uint8_t* base = k_pool + size_t(p) * (kBlock * kDim) + g * 32;
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) dst[tt] = load32(base + (tt * 16 + n16) * kDim);
   };
-  {
-    const int p0 = __shfl(my_p, 0, kWave);
-    if (npages > 0 && p0 >= 0) load_page(kn, p0);
+  if (kPrefetch) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+      const int pf = __builtin_amdgcn_readlane(my_p, f);
+      if (f < npages && pf >= 0) load_page(kn[f], pf);
+    }
   }
   __syncthreads();
 
@@ -156,11 +176,20 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
     const int k = first + wave + kIdxWaves * m;
     const int j = __shfl(my_j, m, kWave);
     const float sc = __shfl(my_sc, m, kWave);
+    if (kPrefetch) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) kb[tt] = kn[tt];
-    if (m + 1 < npages) {
-      const int pn = __shfl(my_p, m + 1, kWave);
-      if (pn >= 0) load_page(kn, pn);
+      for (int tt = 0; tt < 4; ++tt) kb[tt] = kn[0][tt];
+#pragma unroll
+      for (int f = 0; f + 1 < PF; ++f)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) kn[f][tt] = kn[f + 1][tt];
+      if (m + PF < npages) {
+        const int pn = __shfl(my_p, m + PF, kWave);
+        if (pn >= 0) load_page(kn[PF - 1], pn);
+      }
+    } else {
+      const int pc = __shfl(my_p, m, kWave);
+      if (pc >= 0) load_page(kb, pc);
     }
     if (j < 0) {
 #pragma unroll
@@ -193,7 +222,12 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
       const float val = g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
       const int slot = j * kBlock + l;
       const float out = (slot <= q0 + r) ? val * sc : -INFINITY;
-      scores[(size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l] = out;
+      float* dst = scores + (size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l;
+#if SPIN_IDX_NT_STORE
+      __builtin_nontemporal_store(out, dst);
+#else
+      *dst = out;
+#endif
       if (page_max) {
         const float m = wave_max(out);
         if (l == 0) page_max[(size_t(b) * R + r) * mb + k] = m;
@@ -206,7 +240,7 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
 
 hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* q_bf16,
                            const float* w, hipStream_t s) {
-  hipLaunchKernelGGL(k_quantize, dim3(bt.B, bt.R), dim3(256), 0, s, v, bt,
+  hipLaunchKernelGGL(k_quantize, dim3(bt.B, bt.R, kHeads / 4), dim3(256), 0, s, v, bt,
                      reinterpret_cast<const uint16_t*>(q_bf16), w);
   return hipGetLastError();
 }
