@@ -24,6 +24,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed fp32 instructions (v_pk_*_f32) anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the epilogues read them with plain VALU
+    # operands instead of copying each accumulator register out first
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-warning-option",
     "-I", os.path.join(ROOT, "include"),
 ]

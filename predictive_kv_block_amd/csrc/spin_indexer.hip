@@ -11,7 +11,7 @@
 //   head dim; a page is 4 head tiles x 4 token tiles per row.  ReLU, the head
 //   weights and the head sum run on the accumulator registers, the 4 lane
 //   groups are folded with two cross-lane adds, and every lane then holds the
-//   score of token `lane`, stored as one coalesced 256-byte row.
+//   score of token `lane`; rows are staged in LDS and written in bursts.
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -24,7 +24,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 #ifndef SPIN_IDX_PAGES_PER_WAVE
-#define SPIN_IDX_PAGES_PER_WAVE 16
+#define SPIN_IDX_PAGES_PER_WAVE 32
 #endif
 #ifndef SPIN_IDX_WAVES
 #define SPIN_IDX_WAVES 4
@@ -32,11 +32,11 @@ constexpr int kDim = 128;
 #ifndef SPIN_IDX_NONTEMPORAL
 #define SPIN_IDX_NONTEMPORAL 0
 #endif
-#ifndef SPIN_IDX_PREFETCH
-#define SPIN_IDX_PREFETCH 1            // pages in flight ahead of the one on the MFMAs
+#ifndef SPIN_IDX_STAGES
+#define SPIN_IDX_STAGES 3              // key ring depth: pages in flight + the one on the MFMAs
 #endif
 #ifndef SPIN_IDX_NT_STORE
-#define SPIN_IDX_NT_STORE 0            // streaming (non-temporal) score stores
+#define SPIN_IDX_NT_STORE 1            // streaming (non-temporal) score stores
 #endif
 #ifndef SPIN_IDX_WAVES_PER_EU
 #define SPIN_IDX_WAVES_PER_EU 0        // occupancy target for the register allocator (0: none)
@@ -48,6 +48,12 @@ constexpr int kDim = 128;
 #endif
 constexpr int kIdxWaves = SPIN_IDX_WAVES;
 constexpr int kPagesPerWave = SPIN_IDX_PAGES_PER_WAVE;
+constexpr int kStages = SPIN_IDX_STAGES;
+#ifndef SPIN_IDX_FLUSH_ROWS
+#define SPIN_IDX_FLUSH_ROWS 32         // page-rows of scores staged per wave before a burst write
+#endif
+constexpr int kFlushRows = SPIN_IDX_FLUSH_ROWS;
+static_assert(kStages >= 2 && kPagesPerWave + kStages <= kWave, "indexer pipeline shape");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -95,18 +101,82 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
 #endif
 }
 
-// grid (ceil(max_blocks / (4 * kPagesPerWave)), B), 256 threads.
-// Wave w of workgroup x handles kept pages x*4*P + w + 4m, m < P = kPagesPerWave.
-// The page metadata chain (kept entry -> block table -> scale) is issued first
-// and overlaps the staging of the queries in LDS; the keys of page m+1 are in
-// flight while page m runs on the MFMAs.
+// One page of keys in MFMA B-operand layout: tile tt holds tokens 16tt..16tt+15,
+// lane (g, n16) the 32 bytes g*32.. of token 16tt + n16.
+struct PageRegs {
+  v8i t[4];
+};
+
+// Issues the 8 loads of page p, or, when `live` is false, 8 loads that all hit
+// the pool's first 32 bytes: the ring then issues the same number of loads on
+// every path, so the waits before the MFMAs stay partial (a conditional load
+// would force a full drain of the load queue).
+__device__ __forceinline__ void load_page(PageRegs& dst, const uint8_t* k_pool, int p, bool live,
+                                          int lane_off) {
+  const uint8_t* base = k_pool + (live ? size_t(p) * (kBlock * kDim) + lane_off : 0);
+  const int step = live ? 16 * kDim : 0;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) dst.t[tt] = load32(base + tt * step);
+}
+
+// 2 max(x, 0) as x + |x|: one add with an abs source modifier, exact for finite
+// x (fmaxf would cost a second, NaN-quieting max in IEEE mode).  The head
+// weights are staged halved, so (w/2)(x + |x|) is bit-identical to w max(x, 0).
+__device__ __forceinline__ float relu2(float x) { return x + fabsf(x); }
+
+// Scores of one page for query row r: 16 MFMAs (4 head tiles x 4 token tiles),
+// ReLU and head weights on the accumulators (one add and one FMA per head and
+// token), lane groups folded; returns the raw (unscaled) score of token `lane`.
+// s_w holds the halved head weights.
+template <int R>
+__device__ __forceinline__ float page_row_score(const PageRegs& kb, const uint8_t* s_q,
+                                                const float* s_w, int r, int g, int n16) {
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const v8i qa = *reinterpret_cast<const v8i*>(s_q + ((r * kHeads + ht * 16 + n16) * kDim) + g * 32);
+    const float4 wv = *reinterpret_cast<const float4*>(s_w + r * kHeads + ht * 16 + g * 4);
+    v4f acc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb.t[tt], zero, 0, 0, 0, 127, 0, 127);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      part[tt] = fmaf(wv.x, relu2(acc[tt][0]), part[tt]);
+      part[tt] = fmaf(wv.y, relu2(acc[tt][1]), part[tt]);
+      part[tt] = fmaf(wv.z, relu2(acc[tt][2]), part[tt]);
+      part[tt] = fmaf(wv.w, relu2(acc[tt][3]), part[tt]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    part[tt] += __shfl_xor(part[tt], 16, kWave);
+    part[tt] += __shfl_xor(part[tt], 32, kWave);
+  }
+  return g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
+}
+
+// grid (ceil(max_blocks / (W * P)), B), W waves of 64 threads, P = pages per wave.
+// Wave w of workgroup x handles the P consecutive kept positions starting at
+// x*W*P + w*P.  Page metadata (kept entry -> block table -> scale) sits in
+// lanes 0..P-1 and is read back with scalar lane reads, so every branch on it
+// is wave-uniform.  Keys stream through a ring of kStages register buffers:
+// while page m is on the MFMAs, pages m+1 .. m+kStages-1 are in flight.
+// Score rows are staged in LDS and written kFlushRows/R pages at a time as one
+// contiguous burst per row: single 256-byte rows, each written long after its
+// neighbours, reach HBM as scattered partial-row writes that stall the key
+// stream far more than their share of the bytes.
 template <int R>
 __global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
           const int32_t* kept, const int32_t* kept_count, float* scores, float* page_max) {
+  constexpr int F = kFlushRows / R > 0 ? kFlushRows / R : 1;   // pages per flush
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kDim];
   __shared__ float s_w[R * kHeads];
+  __shared__ __attribute__((aligned(16))) float s_out[kIdxWaves * R * F * kBlock];
   const int b = blockIdx.y;
   int cnt = kept_count[b];
   if (cnt < 0 || cnt > bt.max_blocks) {
@@ -117,120 +187,100 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   if (first >= cnt) return;
 
   const int l = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const size_t mb = size_t(bt.max_blocks);
+  const int kw = first + wave * kPagesPerWave;           // this wave's first kept position
+  const int npages = max(0, min(kPagesPerWave, cnt - kw));
 
-  // Page metadata for this wave's pages, lane m holding page m.
-  int my_j = -1, my_p = -1;
+  // Page metadata for this wave's pages, lane m holding page m (j = -1: invalid).
+  int my_j = -1, my_p = 0;
   float my_sc = 0.0f;
-  if (l < kPagesPerWave) {
-    const int k = first + wave + kIdxWaves * l;
-    if (k < cnt) {
-      const int j = kept[size_t(b) * mb + k];
-      if (j < 0 || j >= bt.max_blocks) {
-        flag_error(v.err, SPIN_ERR_KEPT);
+  if (l < npages) {
+    const int j = kept[size_t(b) * mb + kw + l];
+    if (j < 0 || j >= bt.max_blocks) {
+      flag_error(v.err, SPIN_ERR_KEPT);
+    } else {
+      const int p = table[size_t(b) * mb + j];
+      if (p < 0 || int64_t(p) >= pool_pages) {
+        flag_error(v.err, SPIN_ERR_PAGE);
       } else {
-        const int p = table[size_t(b) * mb + j];
-        if (p < 0 || int64_t(p) >= pool_pages) {
-          flag_error(v.err, SPIN_ERR_PAGE);
-        } else {
-          my_j = j;
-          my_p = p;
-          my_sc = k_scale[p];
-        }
+        my_j = j;
+        my_p = p;
+        my_sc = k_scale[p];
       }
     }
   }
 
-  // Stage this request's quantised queries and head weights in LDS.
+  // Stage this request's quantised queries and halved head weights in LDS.
   const uint8_t* q8 = v.q8 + size_t(b) * v.max_rows * kHeads * kDim;
   const float* wq = v.wq + size_t(b) * v.max_rows * kHeads;
   for (int i = threadIdx.x; i < R * kHeads * kDim / 16; i += kIdxWaves * kWave)
     reinterpret_cast<uint4*>(s_q)[i] = reinterpret_cast<const uint4*>(q8)[i];
-  for (int i = threadIdx.x; i < R * kHeads; i += kIdxWaves * kWave) s_w[i] = wq[i];
+  for (int i = threadIdx.x; i < R * kHeads; i += kIdxWaves * kWave) s_w[i] = 0.5f * wq[i];
 
   const int q0 = bt.qpos[b];
   const int g = l >> 4;       // lane group: K chunk of the operands, M rows of the result
   const int n16 = l & 15;     // M row of A / N column of B
-  const int npages = min(kPagesPerWave, (cnt - first - wave + kIdxWaves - 1) / kIdxWaves);
+  float* my_out = s_out + wave * (R * F * kBlock);
 
-  constexpr int PF = SPIN_IDX_PREFETCH > 0 ? SPIN_IDX_PREFETCH : 1;
-  constexpr bool kPrefetch = SPIN_IDX_PREFETCH > 0;
-  v8i kb[4], kn[PF][4];
-  auto load_page = [&](v8i* dst, int p) {
-    const uint8_t* base = k_pool + size_t(p) * (kBlock * kDim) + g * 32;
+  // Invalid pages (flagged above) read page 0 and are written as -inf.
+  const int lane_off = n16 * kDim + g * 32;
+  PageRegs ring[kStages];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) dst[tt] = load32(base + (tt * 16 + n16) * kDim);
-  };
-  if (kPrefetch) {
-#pragma unroll
-    for (int f = 0; f < PF; ++f) {
-      const int pf = __builtin_amdgcn_readlane(my_p, f);
-      if (f < npages && pf >= 0) load_page(kn[f], pf);
-    }
-  }
+  for (int f = 0; f + 1 < kStages; ++f)
+    load_page(ring[f], k_pool, __builtin_amdgcn_readlane(my_p, f), f < npages, lane_off);
   __syncthreads();
 
-#pragma unroll 1
-  for (int m = 0; m < npages; ++m) {
-    const int k = first + wave + kIdxWaves * m;
-    const int j = __shfl(my_j, m, kWave);
-    const float sc = __shfl(my_sc, m, kWave);
-    if (kPrefetch) {
+  for (int m0 = 0; m0 < npages; m0 += kStages) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) kb[tt] = kn[0][tt];
-#pragma unroll
-      for (int f = 0; f + 1 < PF; ++f)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) kn[f][tt] = kn[f + 1][tt];
-      if (m + PF < npages) {
-        const int pn = __shfl(my_p, m + PF, kWave);
-        if (pn >= 0) load_page(kn[PF - 1], pn);
-      }
-    } else {
-      const int pc = __shfl(my_p, m, kWave);
-      if (pc >= 0) load_page(kb, pc);
-    }
-    if (j < 0) {
+    for (int u = 0; u < kStages; ++u) {
+      const int m = m0 + u;
+      if (m >= npages) break;
+      load_page(ring[(u + kStages - 1) % kStages], k_pool,
+                __builtin_amdgcn_readlane(my_p, m + kStages - 1), m + kStages - 1 < npages,
+                lane_off);
+      const int j = __builtin_amdgcn_readlane(my_j, m);
+      const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_sc), m));
+      const int mf = m % F;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        scores[(size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l] = -INFINITY;
-        if (page_max && l == 0) page_max[(size_t(b) * R + r) * mb + k] = -INFINITY;
-      }
-      continue;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ht = 0; ht < 4; ++ht) {
-        const v8i qa = *reinterpret_cast<const v8i*>(s_q + ((r * kHeads + ht * 16 + n16) * kDim) + g * 32);
-        const float4 wv = *reinterpret_cast<const float4*>(s_w + r * kHeads + ht * 16 + g * 4);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          v4f acc = {0.f, 0.f, 0.f, 0.f};
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb[tt], acc, 0, 0, 0, 127, 0, 127);
-          part[tt] += wv.x * fmaxf(acc[0], 0.f) + wv.y * fmaxf(acc[1], 0.f) +
-                      wv.z * fmaxf(acc[2], 0.f) + wv.w * fmaxf(acc[3], 0.f);
+        float out = -INFINITY;
+        if (j >= 0) {
+          const float val = page_row_score<R>(ring[u], s_q, s_w, r, g, n16);
+          out = (j * kBlock + l <= q0 + r) ? val * sc : -INFINITY;
+        }
+        my_out[(r * F + mf) * kBlock + l] = out;
+        if (page_max) {   // every lane writes the same word (no divergent store)
+          const float pm = wave_max(out);
+          page_max[(size_t(b) * R + r) * mb + kw + m] = pm;
         }
       }
+      if (mf == F - 1 || m + 1 == npages) {
+        // Flush pages m-mf .. m of every row: LDS -> one contiguous burst.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int n4 = (mf + 1) * (kBlock / 4);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        part[tt] += __shfl_xor(part[tt], 16, kWave);
-        part[tt] += __shfl_xor(part[tt], 32, kWave);
-      }
-      const float val = g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
-      const int slot = j * kBlock + l;
-      const float out = (slot <= q0 + r) ? val * sc : -INFINITY;
-      float* dst = scores + (size_t(b) * R + r) * mb * kBlock + size_t(k) * kBlock + l;
+        for (int r = 0; r < R; ++r) {
+          v4f* dst = reinterpret_cast<v4f*>(scores + (size_t(b) * R + r) * mb * kBlock +
+                                            size_t(kw + m - mf) * kBlock);
+          const v4f* src = reinterpret_cast<const v4f*>(my_out + r * F * kBlock);
+#pragma unroll
+          for (int i0 = 0; i0 < F * (kBlock / 4); i0 += kWave) {
+            const int i = i0 + l;
+            if (i < n4) {
 #if SPIN_IDX_NT_STORE
-      __builtin_nontemporal_store(out, dst);
+              __builtin_nontemporal_store(src[i], dst + i);
 #else
-      *dst = out;
+              dst[i] = src[i];
 #endif
-      if (page_max) {
-        const float m = wave_max(out);
-        if (l == 0) page_max[(size_t(b) * R + r) * mb + k] = m;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
   }
