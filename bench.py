@@ -30,6 +30,34 @@ IDX_BYTES_PER_PAGE = PAGE_BYTES + 4 + 4 + 4
 IDX_SCORE_BYTES_PER_PAGE_ROW = 64 * 4 + 4       # scores + the page maximum
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_indexer_ctx512k-b96_hbm_traffic.md")
+INDEXER_BUILD_FILES = ["predictive_kv_block_amd/csrc/spin_indexer.hip",
+                       "predictive_kv_block_amd/csrc/spin_device.h",
+                       "predictive_kv_block_amd/csrc/spin_internal.h",
+                       "predictive_kv_block_amd/build.py"]
+
+
+def _measured_traffic(workload, sparsity_bp):
+    """HBM bytes per indexer launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when that summary is for another workload or
+    the indexer has been rebuilt from different sources since."""
+    import hashlib
+    import re
+
+    if workload != "ctx512k-b96" or sparsity_bp != 5000 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    t = re.search(r"^traffic_bytes_per_launch = (\d+)$", text, re.M)
+    d = re.search(r"^indexer_build_sha256 = ([0-9a-f]{64})$", text, re.M)
+    if not t or not d:
+        return None
+    h = hashlib.sha256()
+    for f in INDEXER_BUILD_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return int(t.group(1)) if h.hexdigest() == d.group(1) else None
+
+
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -39,7 +67,7 @@ def _args():
     ap.add_argument("--sparsity-bp", type=int, default=5000)
     ap.add_argument("--sweep", default="0,4000", help="extra sparsities (bp) timed for scaling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-requests", type=int, default=4)
+    ap.add_argument("--cpu-requests", type=int, default=160)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     return ap.parse_args()
@@ -74,28 +102,48 @@ def _setup(wl, device):
     return spin, pool, cfg, st, bufs, make_queries
 
 
-def _round(spin, st, bufs, pool, q, w, keep_bp, ev=None):
-    """One SPIN round; `ev` = list of 6 events bracketing the 5 calls, or None."""
+def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
+    """One SPIN round.
+
+    Main stream: predict -> quantise -> indexer -> top-k.  The EMA update runs
+    on `side` once the indexer is done, concurrently with the top-k: both only
+    read the scores and kept lists, and they write disjoint outputs.  The top-k
+    goes first on the stream that ran the indexer, so its workgroups are
+    resident before the update's fill the GPU.  The round starts after the
+    previous round's update (`prev_update`): the predictor reads the EMAs it
+    writes, and this round overwrites the kept lists and scores it reads.
+    `ev` = 7 timing events (5 on the main stream around predict, quantise,
+    indexer and top-k; 2 on `side` around the update), or None.  Returns the
+    event that marks this round's update as done.
+    """
+    import torch
+
     b = bufs
-    if ev:
-        ev[0].record()
+    main = torch.cuda.current_stream()
+    if prev_update is not None:
+        main.wait_event(prev_update)
+    ev = ev or [None] * 7
+    rec = lambda e, s: e.record(s) if e is not None else None
+    rec(ev[0], main)
     spin.spin_predict_blocks(st.handle, 0, b["batch"], keep_bp, b["kept"], b["cnt"], b["flags"])
-    if ev:
-        ev[1].record()
+    rec(ev[1], main)
     spin.spin_quantize_q(st.handle, b["batch"], q, w)
-    if ev:
-        ev[2].record()
+    rec(ev[2], main)
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
                              pool.block_table, b["kept"], b["cnt"], b["scores"], b["pmax"])
-    if ev:
-        ev[3].record()
+    idx_done = torch.cuda.Event()
+    idx_done.record(main)
+    rec(ev[3], main)
     spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
                           b["topk_ws"], b["pmax"])
-    if ev:
-        ev[4].record()
-    spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"])
-    if ev:
-        ev[5].record()
+    rec(ev[4], main)
+    side.wait_event(idx_done)
+    rec(ev[5], side)
+    spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"], stream=side)
+    rec(ev[6], side)
+    upd_done = torch.cuda.Event()
+    upd_done.record(side)
+    return upd_done
 
 
 def _run_gpu(wl, keep_bps, steps, warmup, device):
@@ -107,28 +155,33 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
     qs = [make_queries(wl, pool, 0, t, [base_q + t] * wl.batch, device=device) for t in range(T)]
     torch.cuda.synchronize()
     results = {}
-    names = ["predict", "quantize", "indexer", "topk", "update"]
+    side = torch.cuda.Stream(device=device)          # default priority
     for keep_bp in keep_bps:
         spin.spin_reset_slots(st.handle, bufs["slot"],
                               torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
+        done = None
         for t in range(warmup):
             bufs["qpos"].fill_(base_q + t)
-            _round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep_bp)
+            done = _round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep_bp, side, done)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         qpos_host = [base_q + warmup + t for t in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        done = None
         for t in range(steps):
             bufs["qpos"].fill_(qpos_host[t])
             q, w = qs[warmup + t]
-            _round(spin, st, bufs, pool, q, w, keep_bp, evs[t])
+            done = _round(spin, st, bufs, pool, q, w, keep_bp, side, done, evs[t])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = {n: [] for n in names}
+        per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
         for e in evs:
-            for i, n in enumerate(names):
+            for i, n in enumerate(["predict", "quantize", "indexer", "topk"]):
                 per[n].append(e[i].elapsed_time(e[i + 1]) * 1e3)      # us
+            per["update"].append(e[5].elapsed_time(e[6]) * 1e3)
+        # a round ends when both the top-k (main) and the update (side) are done
+        per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[6])) * 1e3 for e in evs]
         cnt = bufs["cnt"].cpu()
         kept_pages = int(cnt.sum())
         if st.error() != 0:
@@ -141,6 +194,12 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
 def _median(x):
     s = sorted(x)
     return s[len(s) // 2]
+
+
+def _pct(x, p):
+    """p-th percentile (nearest rank) of a list."""
+    s = sorted(x)
+    return s[min(len(s) - 1, max(0, int(round(p / 100.0 * (len(s) - 1)))))]
 
 
 def _cpu_baseline(wl, keep_bp, n_req):
@@ -215,7 +274,9 @@ def main():
 
     main_r = res[keep_main]
     per = main_r["per_us"]
-    step_us = [sum(per[n][i] for n in per) for i in range(a.steps)]
+    step_us = per["step"]
+    pit = [per["predict"][i] + per["quantize"][i] + per["indexer"][i] + per["topk"][i]
+           for i in range(a.steps)]
     ms_per_step = main_r["wall_s"] * 1e3 / a.steps
     tokens_per_step = main_r["kept_pages"] * 64
     value = tokens_per_step / (ms_per_step / 1e3)
@@ -228,8 +289,7 @@ def main():
         sweep_out[str(10000 - k)] = {
             "kept_share": r["kept_pages"] / r["blocks"],
             "indexer_us": round(iu, 2),
-            "step_us_median": round(_median([sum(r["per_us"][n][i] for n in r["per_us"])
-                                             for i in range(a.steps)]), 2),
+            "step_us_median": round(_median(r["per_us"]["step"]), 2),
         }
     if "0" in sweep_out:
         base = sweep_out["0"]["indexer_us"]
@@ -255,18 +315,23 @@ def main():
                    "heads": wl.heads, "head_dim": wl.head_dim, "topk": wl.topk,
                    "target_sparsity_bp": a.sparsity_bp, "explore_bp": wl.explore_bp,
                    "rows": wl.rows, "block_table": "shuffled" if wl.shuffle else "identity"},
+        "indexer_tokens_per_s": tokens_per_step / (idx_us * 1e-6),
+        "indexer_roofline_tokens_per_s": HBM_PEAK_GBS * 1e9 / (
+            IDX_BYTES_PER_PAGE / 64 + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW / 64),
         "per_step_us": {
-            "predict_index_topk_median": round(_median([per["predict"][i] + per["quantize"][i] +
-                                                        per["indexer"][i] + per["topk"][i]
-                                                        for i in range(a.steps)]), 2),
+            "predict_index_topk_median": round(_median(pit), 2),
+            "predict_index_topk_p10": round(_pct(pit, 10), 2),
+            "predict_index_topk_p90": round(_pct(pit, 90), 2),
             "update_median": round(_median(per["update"]), 2),
             "whole_step_median": round(_median(step_us), 2),
-            **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items()},
+            **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items() if n != "step"},
+            "update_overlaps_topk": True,
         },
         "realized_block_sparsity": 1.0 - main_r["kept_pages"] / main_r["blocks"],
         "roofline": {"bound": "hbm", "kernel": "k_indexer", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": idx_bytes},
+                     "traffic": _measured_traffic(wl.name, a.sparsity_bp),
+                     "bytes_per_launch": idx_bytes},
         "sweep": sweep_out,
         "cpu_baseline": cpu,
         "context": "pages' serving run: 4720 -> 5421 output TPS (+14.9% at 50% sparsity, 8x B300, "

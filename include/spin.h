@@ -178,8 +178,10 @@ int spin_quantize_q(spin_state* st, const spin_batch* batch, const void* q_bf16,
  * computed with fp8 e4m3fn MFMA and fp32 accumulation.
  * k_pool: e4m3fn codes [pool_pages][64][head_dim]; k_scale: fp32 [pool_pages];
  * block_table: int32 [B][max_blocks] (logical block -> page).
- * scores: fp32 [B][R][max_blocks * 64] in kept order: element k*64 + t is slot
- * 64*kept_blocks[b][k] + t; slots after the row's position get -inf.
+ * scores: fp32 [B][R][max_blocks * 64], 16-byte aligned (SPIN_EINVAL
+ * otherwise), in kept order: element k*64 + t is slot 64*kept_blocks[b][k] + t;
+ * slots after the row's position get -inf; entries past the row's kept count
+ * are not written.
  * page_max (may be NULL): fp32 [B][R][max_blocks], element k = the largest of
  * the 64 scores of kept page k for that row (-inf if all are masked); it is
  * the optional top-k prefilter input of spin_topk_scores. */
@@ -196,7 +198,7 @@ int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
  * core attention): the `topk` kept slots i <= q_r with the largest scores,
  * ties to the lower slot, written ascending to topk_out int32 [B][R][topk],
  * padded with -1.  -0.0 ranks equal to +0.0.  scores as spin_indexer_scores
- * writes them (only slots <= q_r are read as candidates).  topk: 4..4096, a
+ * writes them, 16-byte aligned (only slots <= q_r are read as candidates).  topk: 4..4096, a
  * multiple of 4.  page_max (may be NULL): the per-page maxima written by
  * spin_indexer_scores for these scores; with at least `topk` valid pages its
  * topk-th largest value is a lower bound of the answer's smallest score, so

@@ -191,6 +191,7 @@ int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* 
   if (!k_pool || !k_scale || pool_pages < 1 || pool_pages > (int64_t(1) << 31) || !block_table ||
       !kept_blocks || !kept_count || !scores)
     return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0) return SPIN_EINVAL;
   if (!indexer_shape_ok(st)) return SPIN_EUNSUPPORTED;
   return hip_status(spin::launch_indexer(st->view, *batch, k_pool, k_scale, pool_pages,
                                          block_table, kept_blocks, kept_count, scores, page_max,
@@ -214,6 +215,7 @@ int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
   if (topk < 1 || topk > 4096 || topk % 4 != 0 || !scores || !kept_blocks || !kept_count ||
       !topk_out)
     return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0) return SPIN_EINVAL;
   const spin::TopkPlan p = spin::topk_plan(batch->B * batch->R, batch->max_blocks, topk);
   if ((p.levels > 1 || page_max) && (!workspace || workspace_bytes < p.bytes))
     return SPIN_EINVAL;

@@ -196,7 +196,11 @@ constexpr int kFusedCandPages = 4096;                        // listed candidate
 constexpr int kFusedCap = 8192;                              // survivors held in LDS
 constexpr int kFusedPerLane = kFusedCap / kFusedThreads;     // 8
 
-constexpr int kFusedBatch = 16;                              // pages per wave step
+#ifndef SPIN_TOPK_BATCH
+#define SPIN_TOPK_BATCH 32
+#endif
+static_assert(SPIN_TOPK_BATCH % 4 == 0 && SPIN_TOPK_BATCH <= 64, "4 pages per load");
+constexpr int kFusedBatch = SPIN_TOPK_BATCH;                 // pages per wave step
 
 struct FusedShared {
   TopkShared t;
@@ -207,6 +211,21 @@ struct FusedShared {
   int spos[kFusedCap];
   int scan[kFusedWaves];
 };
+
+// Inverse of ord_key for keys of non-NaN floats (the key of +0 gives +0).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Inclusive prefix sum within each 16-lane row of the wave (DPP row shifts;
+// lanes shifted in from outside the row read 0).
+__device__ __forceinline__ int row_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  return x;
+}
 
 // Exclusive prefix sum over n <= kFusedCandPages ints in LDS; returns the total.
 __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
@@ -331,30 +350,43 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
   __syncthreads();
 
   // 3. survivors per candidate page.  Wave w scans the contiguous candidate
-  // range [c_lo, c_hi), kFusedBatch pages per step with all loads in flight;
-  // lane l looks at slot l of each page.
+  // range [c_lo, c_hi), kFusedBatch pages per step.  Each 16-lane row of the
+  // wave takes one page per load (lane l: slots 4(l%16) .. 4(l%16)+3 as one
+  // 16-byte load), so one load instruction covers 4 pages.  A slot survives
+  // if it is valid, causal and its score is >= t1 (compared as floats:
+  // the key order and the float order agree, with -0 = +0).
   const int per_wave = (ncand + kFusedWaves - 1) / kFusedWaves;
   const int c_lo = min(ncand, w * per_wave), c_hi = min(ncand, c_lo + per_wave);
-  auto survivor_key = [&](int c, float v, uint32_t* key_out) {
-    const int j = sh.pagej[c];
-    const uint32_t key = ord_key(v);
-    *key_out = key;
-    return j >= 0 && j < bt.max_blocks && j * kBlock + l <= qr && key >= t1;
+  const float f1 = key_to_float(t1);
+  const int slot0 = 4 * (l & 15);
+  constexpr int kLoads = kFusedBatch / 4;
+  // lane's survivor flags (4 bits) for load i of the batch at c0; *c_out its page
+  auto survivors = [&](int c0, int i, const float4& v, int* c_out, int* j_out) {
+    const int c = c0 + 4 * i + (l >> 4);
+    const int j = (c < c_hi) ? sh.pagej[c] : -1;
+    *c_out = c;
+    *j_out = j;
+    const int lim = (j >= 0 && j < bt.max_blocks) ? qr - j * kBlock - slot0 : -1;
+    return int(v.x >= f1 && lim >= 0) | (int(v.y >= f1 && lim >= 1) << 1) |
+           (int(v.z >= f1 && lim >= 2) << 2) | (int(v.w >= f1 && lim >= 3) << 3);
+  };
+  auto load_batch = [&](int c0, float4* v) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int c = c0 + 4 * i + (l >> 4);
+      const int p = (c < c_hi) ? sh.pages[c] : 0;
+      v[i] = *reinterpret_cast<const float4*>(sc + size_t(p) * kBlock + slot0);
+    }
   };
   for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
-    float v[kFusedBatch];
+    float4 v[kLoads];
+    load_batch(c0, v);
 #pragma unroll
-    for (int u = 0; u < kFusedBatch; ++u) {
-      const int c = c0 + u;
-      v[u] = (c < c_hi) ? sc[size_t(sh.pages[c]) * kBlock + l] : -INFINITY;
-    }
-#pragma unroll
-    for (int u = 0; u < kFusedBatch; ++u) {
-      const int c = c0 + u;
-      uint32_t key;
-      const bool ok = (c < c_hi) && survivor_key(c, v[u], &key);
-      const uint64_t bal = __ballot(ok);
-      if (c < c_hi && l == 0) sh.pcount[c] = __popcll(bal);
+    for (int i = 0; i < kLoads; ++i) {
+      int c, j;
+      const int f = survivors(c0, i, v[i], &c, &j);
+      const int tot = row_inclusive_sum(__popc(f));
+      if ((l & 15) == 15 && c < c_hi) sh.pcount[c] = tot;
     }
   }
   __syncthreads();
@@ -363,24 +395,24 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
     if (tid == 0) done[row] = 0;
     return;
   }
-  // 4. collect them in position order
+  // 4. collect them in position order (pages ascending, slots ascending)
   for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
-    float v[kFusedBatch];
+    float4 v[kLoads];
+    load_batch(c0, v);
 #pragma unroll
-    for (int u = 0; u < kFusedBatch; ++u) {
-      const int c = c0 + u;
-      v[u] = (c < c_hi) ? sc[size_t(sh.pages[c]) * kBlock + l] : -INFINITY;
-    }
+    for (int i = 0; i < kLoads; ++i) {
+      int c, j;
+      const int f = survivors(c0, i, v[i], &c, &j);
+      const int n = __popc(f);
+      int o = row_inclusive_sum(n) - n + ((c < c_hi) ? sh.pcount[c] : 0);
+      const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-    for (int u = 0; u < kFusedBatch; ++u) {
-      const int c = c0 + u;
-      uint32_t key;
-      const bool ok = (c < c_hi) && survivor_key(c, v[u], &key);
-      const uint64_t bal = __ballot(ok);
-      if (ok) {
-        const int o = sh.pcount[c] + ballot_rank(bal);
-        sh.skey[o] = key;
-        sh.spos[o] = sh.pagej[c] * kBlock + l;
+      for (int k = 0; k < 4; ++k) {
+        if (f & (1 << k)) {
+          sh.skey[o] = ord_key(vals[k]);
+          sh.spos[o] = j * kBlock + slot0 + k;
+          ++o;
+        }
       }
     }
   }
