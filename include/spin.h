@@ -102,8 +102,8 @@ typedef struct spin_batch {
  *   bscore [max_slots][max_rows][max_blocks]  workspace: block scores S
  *   ukey [max_slots][max_blocks] uint64       workspace: exploration keys
  *   page_max [max_slots][max_rows][max_blocks] workspace: page maxima for the top-k
- *   topk_ws                                   workspace: top-k survivor buffers for
- *                                             max_slots * max_rows rows (to `total`)
+ *   topk_ws                                   empty (= total): the state's top-k runs on
+ *                                             the page maxima and needs no workspace
  * Workspace arrays are indexed by batch position b, not by slot. */
 typedef struct spin_state_layout {
   size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, page_max, topk_ws,
@@ -191,7 +191,8 @@ int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* 
                         float* page_max, hipStream_t stream);
 
 /* Bytes of caller-owned device workspace spin_topk_scores needs for this
- * batch shape and K (0 when every row fits one 16384-candidate chunk). */
+ * batch shape and K when it is called without page maxima (0 when every row
+ * fits one 16384-candidate chunk). */
 int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
 
 /* Per-row top-k over kept-order scores (v1 abstract: a fixed top-k goes to
@@ -203,10 +204,11 @@ int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
  * spin_indexer_scores for these scores; with at least `topk` valid pages its
  * topk-th largest value is a lower bound of the answer's smallest score, so
  * scores below it are dropped before ranking (the result is the same).
- * workspace: 256-byte aligned device memory of at least
- * spin_topk_workspace_bytes() bytes (may be NULL only when page_max is NULL
- * and the rows fit one 16384-candidate chunk); its contents need no
- * initialisation and are clobbered.  batch->slot is not read. */
+ * With page_max the whole top-k is one kernel and needs no workspace.
+ * Without it, workspace: 256-byte aligned device memory of at least
+ * spin_topk_workspace_bytes() bytes (may be NULL when the rows fit one
+ * 16384-candidate chunk); its contents need no initialisation and are
+ * clobbered.  batch->slot is not read. */
 int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
                      const float* page_max, const int32_t* kept_blocks, const int32_t* kept_count,
                      int32_t* topk_out, void* workspace, size_t workspace_bytes,

@@ -51,8 +51,7 @@ spin_state_layout make_layout(const spin_config* c) {
   l.bscore = off;     off = align_up(off + S * R * MB * 4);
   l.ukey = off;       off = align_up(off + S * MB * 8);
   l.page_max = off;   off = align_up(off + S * R * MB * 4);
-  l.topk_ws = off;
-  off = align_up(off + spin::topk_plan(int(S * R), int(MB), c->topk).bytes);
+  l.topk_ws = off;     // empty: with page maxima the top-k needs no workspace
   l.total = off;
   l.max_blocks = int32_t(MB);
   return l;
@@ -126,8 +125,8 @@ int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes, hipSt
   v.bscore = reinterpret_cast<float*>(st->base + lay.bscore);
   v.ukey = reinterpret_cast<uint64_t*>(st->base + lay.ukey);
   v.pmax = reinterpret_cast<float*>(st->base + lay.page_max);
-  v.topk_ws = st->base + lay.topk_ws;
-  v.topk_ws_bytes = lay.total - lay.topk_ws;
+  v.topk_ws = nullptr;
+  v.topk_ws_bytes = 0;
   v.L = cfg->num_layers;
   v.S = cfg->max_slots;
   v.max_ctx = cfg->max_ctx;
@@ -217,7 +216,7 @@ int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
     return SPIN_EINVAL;
   if (reinterpret_cast<uintptr_t>(scores) % 16 != 0) return SPIN_EINVAL;
   const spin::TopkPlan p = spin::topk_plan(batch->B * batch->R, batch->max_blocks, topk);
-  if ((p.levels > 1 || page_max) && (!workspace || workspace_bytes < p.bytes))
+  if (!page_max && p.levels > 1 && (!workspace || workspace_bytes < p.bytes))
     return SPIN_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPIN_EINVAL;
   return hip_status(spin::launch_topk(*batch, topk, scores, page_max, kept_blocks, kept_count,
@@ -239,7 +238,7 @@ int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf1
                            kept_count, scores, st->view.pmax, stream);
   if (rc) return rc;
   return spin_topk_scores(batch, st->cfg.topk, scores, st->view.pmax, kept_blocks, kept_count,
-                          topk_out, st->view.topk_ws, st->view.topk_ws_bytes, stream);
+                          topk_out, nullptr, 0, stream);
 }
 
 int spin_update(spin_state* st, int layer, const spin_batch* batch, const float* scores,

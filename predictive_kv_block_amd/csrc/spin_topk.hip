@@ -4,23 +4,25 @@
 // order (= ascending position).  The selection is exact, with ties to the
 // lower position.
 //
-// 1. k_topk_fused (one workgroup per row, when the indexer's per-page maxima
-//    are given): t1 = the K-th largest page maximum.  Each page whose maximum
-//    is >= t1 holds at least one score >= t1, so with at least K valid pages
-//    the row's K-th largest score is >= t1 and every score < t1 can be
-//    dropped.  Only pages with maximum >= t1 are read; their scores >= t1 are
-//    gathered in position order and ranked exactly, and the row is done.  Rows
-//    that do not fit its buffers fall through to step 2 with t1 as a filter.
-// 2. k_topk_level, level 0: the row is cut into chunks of kChunk; each chunk's
-//    surviving candidates are held in registers (wave w owns a contiguous
-//    segment, lane l every 64th element of it).  If at most K survive, all of
-//    them pass on; otherwise the chunk's local top-K is found by an MSB-first
-//    radix select over LDS histograms.  Every element of the row's top-K is in
-//    its chunk's local top-K, so nothing of the answer is lost.  Survivors are
-//    written in position order, K slots per chunk.
-// 3. Further levels repeat step 2 over the survivors until one chunk remains;
-//    that level writes the answer ascending, padded with -1.  Rows answered by
-//    step 1 are skipped by every level.
+// With the indexer's per-page maxima, k_topk_fused answers every row in one
+// launch (one workgroup per row): t1 = the K-th largest page maximum.  Each
+// page whose maximum is >= t1 holds at least one score >= t1, so with at
+// least K valid pages the row's K-th largest score is >= t1 and every score
+// < t1 can be dropped.  Only pages with maximum >= t1 are read; their scores
+// >= t1 are gathered in position order and ranked exactly.  A row that does
+// not fit those buffers is walked in chunks by the same workgroup, keeping a
+// running top-K.
+//
+// Without page maxima, the chunked levels (k_topk_level):
+// 1. level 0: the row is cut into chunks of kChunk; each chunk's candidates
+//    are held in registers (wave w owns a contiguous segment, lane l every
+//    64th element of it).  If at most K survive, all of them pass on;
+//    otherwise the chunk's local top-K is found by an MSB-first radix select
+//    over LDS histograms.  Every element of the row's top-K is in its chunk's
+//    local top-K, so nothing of the answer is lost.  Survivors are written in
+//    position order, K slots per chunk.
+// 2. Further levels repeat this over the survivors until one chunk remains;
+//    that level writes the answer ascending, padded with -1.
 //
 // k_miss: share of an all-keep top-k that falls in skipped blocks.
 #include "spin_device.h"
@@ -42,8 +44,6 @@ struct LevelArgs {
   const float* scores;
   const int32_t* kept;
   const int32_t* kept_count;
-  const uint32_t* thr_key;    // [rows] key lower bound from the page maxima, or null
-  const int32_t* done;        // [rows] 1 = answered by the fused kernel, or null
   // later levels' input: survivors of the previous level
   const uint32_t* in_keys;    // [rows][in_chunks * K]
   const int32_t* in_pos;      // [rows][in_chunks * K]
@@ -264,170 +264,23 @@ __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
   return total;
 }
 
-// grid (rows).  The whole top-k of a row in one workgroup when the page maxima
-// allow it: t1 = K-th largest page maximum; only pages whose maximum is >= t1
-// can hold scores >= t1; those scores (at least K of them) are collected in
-// position order and ranked exactly.  Rows that do not fit (fewer than K valid
-// pages, more than kFusedCandPages candidate pages or kFusedCap survivors)
-// leave done = 0 and thr_key = t1 (or 0) for the chunked levels.
-__global__ void __launch_bounds__(kFusedThreads)
-k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
-             const int32_t* kept, const int32_t* kept_count, int32_t* topk_out,
-             uint32_t* thr_key, int32_t* done) {
-  __shared__ FusedShared sh;
-  const int row = blockIdx.x;
-  const int b = row / bt.R, r = row % bt.R;
+// Top-min(K, n) of the n entries sh.skey/spos[0..n) (keys > 0, position
+// order), ties to the lower index.  With `out`, their positions are written to
+// out[0..K) ascending and padded with -1; without, they are compacted in place
+// into sh.skey/spos[0..min(K, n)).  n <= kFusedCap.  Returns min(K, n).
+__device__ int lds_topk(FusedShared& sh, int n, int K, int32_t* out) {
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
-  const size_t mb = size_t(bt.max_blocks);
-  int cnt = kept_count[b];
-  cnt = cnt < 0 ? 0 : (cnt > bt.max_blocks ? bt.max_blocks : cnt);
-  if (cnt > kFusedMaxPages || cnt < K) {
-    if (tid == 0) {
-      thr_key[row] = 0u;
-      done[row] = 0;
-    }
-    return;
-  }
-  const int qr = bt.qpos[b] + r;
-  const float* pm = page_max + size_t(row) * mb;
-  const float* sc = scores + size_t(row) * mb * kBlock;
-  const int32_t* kb = kept + size_t(b) * mb;
-
-  // 1. t1 over the page maxima (page p = w*1024 + i*64 + l held by lane l)
-  uint32_t pk[kFusedPageLanes];
-#pragma unroll
-  for (int i = 0; i < kFusedPageLanes; ++i) {
-    const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
-    const float v = (p < cnt) ? pm[p] : -INFINITY;
-    pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
-  }
-  int npages;
-  uint32_t kmin, kmax;
-  block_key_stats<kFusedThreads, kFusedPageLanes>(pk, sh.t, &npages, &kmin, &kmax);
-  if (npages < K) {
-    if (tid == 0) {
-      thr_key[row] = 0u;
-      done[row] = 0;
-    }
-    return;
-  }
-  uint32_t t1 = kmin;
-  if (npages > K) {
-    int n_eq;
-    radix_select_regs<kFusedThreads, kFusedPageLanes>(pk, K, kmin, kmax, sh.t, &t1, &n_eq);
-  }
-  if (tid == 0) thr_key[row] = t1;
-
-  // 2. candidate pages (maximum >= t1), listed in ascending kept order
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < kFusedPageLanes; ++i) mine += (pk[i] != 0u && pk[i] >= t1) ? 1 : 0;
-  mine = wave_sum(mine);
-  __syncthreads();
-  if (l == 0) sh.scan[w] = mine;
-  __syncthreads();
-  int before = 0, ncand = 0;
-#pragma unroll
-  for (int i = 0; i < kFusedWaves; ++i) {
-    before += (i < w) ? sh.scan[i] : 0;
-    ncand += sh.scan[i];
-  }
-  if (ncand > kFusedCandPages) {
-    if (tid == 0) done[row] = 0;
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < kFusedPageLanes; ++i) {
-    const bool sel = pk[i] != 0u && pk[i] >= t1;
-    const uint64_t bal = __ballot(sel);
-    if (sel) sh.pages[before + ballot_rank(bal)] = w * (kFusedPageLanes * kWave) + i * kWave + l;
-    before += __popcll(bal);
-  }
-  __syncthreads();
-
-  // kept entries of the candidate pages, looked up in parallel
-  for (int c = tid; c < ncand; c += kFusedThreads) sh.pagej[c] = kb[sh.pages[c]];
-  __syncthreads();
-
-  // 3. survivors per candidate page.  Wave w scans the contiguous candidate
-  // range [c_lo, c_hi), kFusedBatch pages per step.  Each 16-lane row of the
-  // wave takes one page per load (lane l: slots 4(l%16) .. 4(l%16)+3 as one
-  // 16-byte load), so one load instruction covers 4 pages.  A slot survives
-  // if it is valid, causal and its score is >= t1 (compared as floats:
-  // the key order and the float order agree, with -0 = +0).
-  const int per_wave = (ncand + kFusedWaves - 1) / kFusedWaves;
-  const int c_lo = min(ncand, w * per_wave), c_hi = min(ncand, c_lo + per_wave);
-  const float f1 = key_to_float(t1);
-  const int slot0 = 4 * (l & 15);
-  constexpr int kLoads = kFusedBatch / 4;
-  // lane's survivor flags (4 bits) for load i of the batch at c0; *c_out its page
-  auto survivors = [&](int c0, int i, const float4& v, int* c_out, int* j_out) {
-    const int c = c0 + 4 * i + (l >> 4);
-    const int j = (c < c_hi) ? sh.pagej[c] : -1;
-    *c_out = c;
-    *j_out = j;
-    const int lim = (j >= 0 && j < bt.max_blocks) ? qr - j * kBlock - slot0 : -1;
-    return int(v.x >= f1 && lim >= 0) | (int(v.y >= f1 && lim >= 1) << 1) |
-           (int(v.z >= f1 && lim >= 2) << 2) | (int(v.w >= f1 && lim >= 3) << 3);
-  };
-  auto load_batch = [&](int c0, float4* v) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = c0 + 4 * i + (l >> 4);
-      const int p = (c < c_hi) ? sh.pages[c] : 0;
-      v[i] = *reinterpret_cast<const float4*>(sc + size_t(p) * kBlock + slot0);
-    }
-  };
-  for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
-    float4 v[kLoads];
-    load_batch(c0, v);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      int c, j;
-      const int f = survivors(c0, i, v[i], &c, &j);
-      const int tot = row_inclusive_sum(__popc(f));
-      if ((l & 15) == 15 && c < c_hi) sh.pcount[c] = tot;
-    }
-  }
-  __syncthreads();
-  const int nsurv = block_exclusive_scan(sh.pcount, ncand, sh.scan);
-  if (nsurv > kFusedCap || nsurv < K) {
-    if (tid == 0) done[row] = 0;
-    return;
-  }
-  // 4. collect them in position order (pages ascending, slots ascending)
-  for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
-    float4 v[kLoads];
-    load_batch(c0, v);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      int c, j;
-      const int f = survivors(c0, i, v[i], &c, &j);
-      const int n = __popc(f);
-      int o = row_inclusive_sum(n) - n + ((c < c_hi) ? sh.pcount[c] : 0);
-      const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (f & (1 << k)) {
-          sh.skey[o] = ord_key(vals[k]);
-          sh.spos[o] = j * kBlock + slot0 + k;
-          ++o;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // 5. exact top-K of the survivors (element s = w*512 + i*64 + l held by lane l)
   uint32_t key[kFusedPerLane];
+  int pos[kFusedPerLane];
 #pragma unroll
-  for (int i = 0; i < kFusedPerLane; ++i) {
+  for (int i = 0; i < kFusedPerLane; ++i) {      // element s = w*512 + i*64 + l
     const int s = w * (kFusedPerLane * kWave) + i * kWave + l;
-    key[i] = (s < nsurv) ? sh.skey[s] : 0u;
+    key[i] = (s < n) ? sh.skey[s] : 0u;
+    pos[i] = (s < n) ? sh.spos[s] : 0;
   }
-  uint32_t thr = 0;                       // exactly K survivors: take them all
+  uint32_t thr = 0;                              // n <= K: every entry
   int n_eq = 0;
-  if (nsurv > K) {
+  if (n > K) {
     uint32_t smin, smax;
     int tot;
     block_key_stats<kFusedThreads, kFusedPerLane>(key, sh.t, &tot, &smin, &smax);
@@ -441,7 +294,7 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
   }
   gt = wave_sum(gt);
   eq = wave_sum(eq);
-  __syncthreads();
+  __syncthreads();                               // also: every read of sh above is done
   if (l == 0) {
     sh.t.wave_a[w] = gt;
     sh.t.wave_b[w] = eq;
@@ -455,7 +308,6 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
   }
   int eq_base = eq_before;
   int out_base = gt_before + min(n_eq, eq_before);
-  int32_t* o = topk_out + size_t(row) * K;
 #pragma unroll
   for (int i = 0; i < kFusedPerLane; ++i) {
     const bool is_eq = key[i] != 0u && key[i] == thr;
@@ -463,11 +315,245 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
     const bool sel = (key[i] != 0u && key[i] > thr) || (is_eq && eq_base + ballot_rank(eqb) < n_eq);
     const uint64_t selb = __ballot(sel);
     const int rank = out_base + ballot_rank(selb);
-    if (sel && rank < K) o[rank] = sh.spos[w * (kFusedPerLane * kWave) + i * kWave + l];
+    if (sel && rank < K) {
+      if (out) {
+        out[rank] = pos[i];
+      } else {
+        sh.skey[rank] = key[i];
+        sh.spos[rank] = pos[i];
+      }
+    }
     eq_base += __popcll(eqb);
     out_base += __popcll(selb);
   }
-  if (tid == 0) done[row] = 1;
+  const int m = min(n, K);
+  if (out)
+    for (int i = m + tid; i < K; i += kFusedThreads) out[i] = -1;
+  __syncthreads();
+  return m;
+}
+
+// grid (rows), 1024 threads: the whole top-k of a row.
+// Fast path (at least K valid pages, at most 16384 kept pages): t1 = the K-th
+// largest page maximum; only pages whose maximum is >= t1 can hold scores
+// >= t1, and those scores (at least K of them) are collected in position
+// order and ranked exactly.
+// Fallback (the row has fewer than K valid pages, more than kFusedCandPages
+// candidate pages or more than kFusedCap survivors): the row is walked in
+// chunks of 16384 slots (wave w: pages 16w .. 16w+15 of the chunk, lane l:
+// slot l); each chunk's top-K (scores >= t1 when t1 is known) is appended in
+// position order to the running result in LDS, which is cut back to its top K
+// whenever it holds more.  Every element of the answer is in its chunk's
+// top-K, so nothing of it is lost.
+__global__ void __launch_bounds__(kFusedThreads)
+k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
+             const int32_t* kept, const int32_t* kept_count, int32_t* topk_out) {
+  __shared__ FusedShared sh;
+  const int row = blockIdx.x;
+  const int b = row / bt.R, r = row % bt.R;
+  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
+  const size_t mb = size_t(bt.max_blocks);
+  int cnt = kept_count[b];
+  cnt = cnt < 0 ? 0 : (cnt > bt.max_blocks ? bt.max_blocks : cnt);
+  const int qr = bt.qpos[b] + r;
+  const float* sc = scores + size_t(row) * mb * kBlock;
+  const int32_t* kb = kept + size_t(b) * mb;
+  int32_t* out = topk_out + size_t(row) * K;
+  uint32_t lowest = 1u;                          // smallest key that can be in the answer
+
+  if (page_max && cnt >= K && cnt <= kFusedMaxPages) {
+    const float* pm = page_max + size_t(row) * mb;
+    // 1. t1 over the page maxima (page p = w*1024 + i*64 + l held by lane l)
+    uint32_t pk[kFusedPageLanes];
+#pragma unroll
+    for (int i = 0; i < kFusedPageLanes; ++i) {
+      const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
+      const float v = (p < cnt) ? pm[p] : -INFINITY;
+      pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
+    }
+    int npages;
+    uint32_t kmin, kmax;
+    block_key_stats<kFusedThreads, kFusedPageLanes>(pk, sh.t, &npages, &kmin, &kmax);
+    if (npages >= K) {
+      uint32_t t1 = kmin;
+      if (npages > K) {
+        int n_eq;
+        radix_select_regs<kFusedThreads, kFusedPageLanes>(pk, K, kmin, kmax, sh.t, &t1, &n_eq);
+      }
+      lowest = max(t1, 1u);
+
+      // 2. candidate pages (maximum >= t1), listed in ascending kept order
+      int mine = 0;
+#pragma unroll
+      for (int i = 0; i < kFusedPageLanes; ++i) mine += (pk[i] != 0u && pk[i] >= t1) ? 1 : 0;
+      mine = wave_sum(mine);
+      __syncthreads();
+      if (l == 0) sh.scan[w] = mine;
+      __syncthreads();
+      int before = 0, ncand = 0;
+#pragma unroll
+      for (int i = 0; i < kFusedWaves; ++i) {
+        before += (i < w) ? sh.scan[i] : 0;
+        ncand += sh.scan[i];
+      }
+      if (ncand <= kFusedCandPages) {
+#pragma unroll
+        for (int i = 0; i < kFusedPageLanes; ++i) {
+          const bool sel = pk[i] != 0u && pk[i] >= t1;
+          const uint64_t bal = __ballot(sel);
+          if (sel)
+            sh.pages[before + ballot_rank(bal)] = w * (kFusedPageLanes * kWave) + i * kWave + l;
+          before += __popcll(bal);
+        }
+        __syncthreads();
+        // kept entries of the candidate pages, looked up in parallel
+        for (int c = tid; c < ncand; c += kFusedThreads) sh.pagej[c] = kb[sh.pages[c]];
+        __syncthreads();
+
+        // 3. survivors per candidate page.  Wave w scans the contiguous
+        // candidate range [c_lo, c_hi), kFusedBatch pages per step.  Each
+        // 16-lane row of the wave takes one page per load (lane l: slots
+        // 4(l%16) .. 4(l%16)+3 as one 16-byte load), so one load instruction
+        // covers 4 pages.  A slot survives if it is valid, causal and its
+        // score is >= t1 (compared as floats: the key order and the float
+        // order agree, with -0 = +0).
+        const int per_wave = (ncand + kFusedWaves - 1) / kFusedWaves;
+        const int c_lo = min(ncand, w * per_wave), c_hi = min(ncand, c_lo + per_wave);
+        const float f1 = key_to_float(t1);
+        const int slot0 = 4 * (l & 15);
+        constexpr int kLoads = kFusedBatch / 4;
+        // lane's survivor flags (4 bits) for load i of the batch at c0
+        auto survivors = [&](int c0, int i, const float4& v, int* c_out, int* j_out) {
+          const int c = c0 + 4 * i + (l >> 4);
+          const int j = (c < c_hi) ? sh.pagej[c] : -1;
+          *c_out = c;
+          *j_out = j;
+          const int lim = (j >= 0 && j < bt.max_blocks) ? qr - j * kBlock - slot0 : -1;
+          return int(v.x >= f1 && lim >= 0) | (int(v.y >= f1 && lim >= 1) << 1) |
+                 (int(v.z >= f1 && lim >= 2) << 2) | (int(v.w >= f1 && lim >= 3) << 3);
+        };
+        auto load_batch = [&](int c0, float4* v) {
+#pragma unroll
+          for (int i = 0; i < kLoads; ++i) {
+            const int c = c0 + 4 * i + (l >> 4);
+            const int p = (c < c_hi) ? sh.pages[c] : 0;
+            v[i] = *reinterpret_cast<const float4*>(sc + size_t(p) * kBlock + slot0);
+          }
+        };
+        for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
+          float4 v[kLoads];
+          load_batch(c0, v);
+#pragma unroll
+          for (int i = 0; i < kLoads; ++i) {
+            int c, j;
+            const int f = survivors(c0, i, v[i], &c, &j);
+            const int tot = row_inclusive_sum(__popc(f));
+            if ((l & 15) == 15 && c < c_hi) sh.pcount[c] = tot;
+          }
+        }
+        __syncthreads();
+        const int nsurv = block_exclusive_scan(sh.pcount, ncand, sh.scan);
+        if (nsurv <= kFusedCap && nsurv >= K) {
+          // 4. collect them in position order (pages ascending, slots ascending)
+          for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
+            float4 v[kLoads];
+            load_batch(c0, v);
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+              int c, j;
+              const int f = survivors(c0, i, v[i], &c, &j);
+              const int n = __popc(f);
+              int o = row_inclusive_sum(n) - n + ((c < c_hi) ? sh.pcount[c] : 0);
+              const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                if (f & (1 << k)) {
+                  sh.skey[o] = ord_key(vals[k]);
+                  sh.spos[o] = j * kBlock + slot0 + k;
+                  ++o;
+                }
+              }
+            }
+          }
+          __syncthreads();
+          // 5. exact top-K of the survivors, written ascending
+          lds_topk(sh, nsurv, K, out);
+          return;
+        }
+      }
+    }
+  }
+
+  // ---------------------------------------------------------------- fallback
+  constexpr int kChunkPages = kFusedThreads * kFusedPageLanes / kBlock;   // 256
+  int n_run = 0;                                 // running result in sh.skey/spos[0..n_run)
+  for (int p0 = 0; p0 < cnt; p0 += kChunkPages) {
+    const int pw = p0 + w * kFusedPageLanes;     // this wave's first page
+    const int my_j = (l < kFusedPageLanes && pw + l < cnt) ? kb[pw + l] : -1;
+    float v[kFusedPageLanes];
+#pragma unroll
+    for (int i = 0; i < kFusedPageLanes; ++i)
+      v[i] = (pw + i < cnt) ? sc[size_t(pw + i) * kBlock + l] : -INFINITY;
+    uint32_t key[kFusedPageLanes];
+#pragma unroll
+    for (int i = 0; i < kFusedPageLanes; ++i) {
+      const int j = __builtin_amdgcn_readlane(my_j, i);
+      const bool ok = j >= 0 && j < bt.max_blocks && j * kBlock + l <= qr;
+      const uint32_t kk = ord_key(v[i]);
+      key[i] = (ok && kk >= lowest) ? kk : 0u;
+    }
+    int total;
+    uint32_t kmin, kmax;
+    block_key_stats<kFusedThreads, kFusedPageLanes>(key, sh.t, &total, &kmin, &kmax);
+    if (total == 0) continue;
+    const int want = min(K, total);
+    uint32_t thr = 0;
+    int n_eq = 0;
+    if (want < total)
+      radix_select_regs<kFusedThreads, kFusedPageLanes>(key, want, kmin, kmax, sh.t, &thr, &n_eq);
+    // append the chunk's selection in position order after the running result
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kFusedPageLanes; ++i) {
+      gt += (key[i] != 0u && key[i] > thr) ? 1 : 0;
+      eq += (key[i] != 0u && key[i] == thr) ? 1 : 0;
+    }
+    gt = wave_sum(gt);
+    eq = wave_sum(eq);
+    __syncthreads();
+    if (l == 0) {
+      sh.t.wave_a[w] = gt;
+      sh.t.wave_b[w] = eq;
+    }
+    __syncthreads();
+    int gt_before = 0, eq_before = 0;
+#pragma unroll
+    for (int i = 0; i < kFusedWaves; ++i) {
+      gt_before += (i < w) ? sh.t.wave_a[i] : 0;
+      eq_before += (i < w) ? sh.t.wave_b[i] : 0;
+    }
+    int eq_base = eq_before;
+    int out_base = n_run + gt_before + min(n_eq, eq_before);
+#pragma unroll
+    for (int i = 0; i < kFusedPageLanes; ++i) {
+      const bool is_eq = key[i] != 0u && key[i] == thr;
+      const uint64_t eqb = __ballot(is_eq);
+      const bool sel =
+          (key[i] != 0u && key[i] > thr) || (is_eq && eq_base + ballot_rank(eqb) < n_eq);
+      const uint64_t selb = __ballot(sel);
+      const int rank = out_base + ballot_rank(selb);
+      if (sel && rank < n_run + want) {
+        sh.skey[rank] = key[i];
+        sh.spos[rank] = __builtin_amdgcn_readlane(my_j, i) * kBlock + l;
+      }
+      eq_base += __popcll(eqb);
+      out_base += __popcll(selb);
+    }
+    __syncthreads();
+    n_run += want;
+    if (n_run > K) n_run = lds_topk(sh, n_run, K, nullptr);
+  }
+  lds_topk(sh, n_run, K, out);
 }
 
 // grid (rows, chunks of this level).
@@ -481,7 +567,6 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_level(LevelArgs a) {
   const int K = a.K;
   const size_t mb = size_t(a.bt.max_blocks);
   const int seg = c * kChunk + w * kSeg;  // first candidate of this wave
-  if (a.done && a.done[row]) return;      // the fused kernel already answered this row
 
   uint32_t key[kPerLane];
   int my_kept = -1;                       // level 0: kept entry of block i (lane i)
@@ -496,7 +581,6 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_level(LevelArgs a) {
       return;
     }
     const int qr = a.bt.qpos[b] + r;
-    const uint32_t lowest = a.thr_key ? max(a.thr_key[row], 1u) : 1u;
     const float* s = a.scores + size_t(row) * mb * kBlock;
     if (l < kPerLane && seg + l * kBlock < n) my_kept = a.kept[size_t(b) * mb + seg / kBlock + l];
     float v[kPerLane];
@@ -510,7 +594,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_level(LevelArgs a) {
       const int j = __builtin_amdgcn_readlane(my_kept, i);
       const bool ok = j >= 0 && j < a.bt.max_blocks && j * kBlock + l <= qr;
       const uint32_t kk = ord_key(v[i]);
-      key[i] = (ok && kk >= lowest) ? kk : 0u;
+      key[i] = ok ? kk : 0u;
     }
   } else {
     const uint32_t* ik = a.in_keys + size_t(row) * a.in_chunks * K;
@@ -649,8 +733,7 @@ TopkPlan topk_plan(int rows, int max_blocks, int K) {
   }
   p.buf_elems = size_t(rows) * size_t(widest) * size_t(K);
   p.count_elems = size_t(rows) * size_t(widest);
-  p.bytes = 2 * (align256(p.buf_elems * 4) * 2 + align256(p.count_elems * 4)) +
-            2 * align256(size_t(rows) * 4) + 256;
+  p.bytes = 2 * (align256(p.buf_elems * 4) * 2 + align256(p.count_elems * 4)) + 256;
   return p;
 }
 
@@ -663,8 +746,6 @@ hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, cons
   uint32_t* keys[2] = {nullptr, nullptr};
   int32_t* pos[2] = {nullptr, nullptr};
   int32_t* cnts[2] = {nullptr, nullptr};
-  uint32_t* thr = nullptr;
-  int32_t* done = nullptr;
   if (base) {
     size_t off = 0;
     for (int i = 0; i < 2; ++i) {
@@ -675,23 +756,18 @@ hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, cons
       cnts[i] = reinterpret_cast<int32_t*>(base + off);
       off += align256(p.count_elems * 4);
     }
-    if (page_max) {
-      thr = reinterpret_cast<uint32_t*>(base + off);
-      off += align256(size_t(rows) * 4);
-      done = reinterpret_cast<int32_t*>(base + off);
-    }
   }
-  if (thr)
+  if (page_max) {
     hipLaunchKernelGGL(k_topk_fused, dim3(rows), dim3(kFusedThreads), 0, s, bt, topk, scores,
-                       page_max, kept, kept_count, out, thr, done);
+                       page_max, kept, kept_count, out);
+    return hipGetLastError();
+  }
   LevelArgs a;
   a.bt = bt;
   a.K = topk;
   a.scores = scores;
   a.kept = kept;
   a.kept_count = kept_count;
-  a.thr_key = thr;
-  a.done = done;
   a.topk_out = out;
   for (int lv = 0; lv < p.levels; ++lv) {
     const bool first = lv == 0, final = lv == p.levels - 1;

@@ -134,6 +134,12 @@ TOPK_CASES = {
     "pm-clustered": (2, 8192, 2048, "clustered"),
     "pm-equal-maxima": (1, 4096, 2048, "plateau"),
     "pm-few-pages": (2, 1000, 2048, "random"),
+    # fused kernel's own fallback: ties at t1, a row over 16384 kept pages, K = 4096
+    # with running merges of up to 2K entries, and signed zeros
+    "pm-ties": (2, 4096, 2048, "ties"),
+    "pm-over-16k-pages": (1, 20000, 2048, "random"),
+    "pm-k4096-chunks": (1, 3000, 4096, "random"),
+    "pm-zeros": (2, 1200, 512, "zeros"),
 }
 
 
@@ -148,7 +154,7 @@ def test_topk_exact_on_identical_scores(gpu_lib, case):
     kept = [np.union1d(k, [nblocks(q + R - 1) - 1]) for k, q in zip(kept, qpos)]
     if pattern == "short":
         kept[0] = kept[0][:3]                                    # fewer candidates than K
-    if case == "two-levels":
+    if case in ("two-levels", "pm-over-16k-pages"):
         kept[1] = np.arange(nblocks(qpos[1]))                    # a whole row kept
     sc = rng.random((B, R, mb * 64)).astype(np.float32)
     if pattern == "ties":
