@@ -67,6 +67,10 @@ def _args():
     ap.add_argument("--sparsity-bp", type=int, default=5000)
     ap.add_argument("--sweep", default="0,4000", help="extra sparsities (bp) timed for scaling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--spacer-cycles", type=int, default=4000,
+                    help="device-clock cycles of spin before the update on the side stream")
+    ap.add_argument("--quantize-on-main", action="store_true",
+                    help="run the query quantiser on the main stream after the predictor")
     ap.add_argument("--cpu-requests", type=int, default=160)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
@@ -102,19 +106,26 @@ def _setup(wl, device):
     return spin, pool, cfg, st, bufs, make_queries
 
 
+QUANTIZE_ON_SIDE = True
+SPACER_CYCLES = 0
+
+
 def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
     """One SPIN round.
 
-    Main stream: predict -> quantise -> indexer -> top-k.  The EMA update runs
-    on `side` once the indexer is done, concurrently with the top-k: both only
-    read the scores and kept lists, and they write disjoint outputs.  The top-k
-    goes first on the stream that ran the indexer, so its workgroups are
-    resident before the update's fill the GPU.  The round starts after the
-    previous round's update (`prev_update`): the predictor reads the EMAs it
-    writes, and this round overwrites the kept lists and scores it reads.
-    `ev` = 7 timing events (5 on the main stream around predict, quantise,
-    indexer and top-k; 2 on `side` around the update), or None.  Returns the
-    event that marks this round's update as done.
+    Main stream: predict -> indexer -> top-k.  `side` runs the query
+    quantisation beside the predictor (both start once the previous round's
+    update is done; they touch disjoint memory), then, once the indexer is
+    done, the EMA update beside the top-k (both only read the scores and kept
+    lists and write disjoint outputs).  The top-k goes first on the stream that
+    ran the indexer, so its workgroups are resident before the update's fill
+    the GPU.  The round starts after the previous round's update
+    (`prev_update`): the predictor reads the EMAs it writes, and this round
+    overwrites the kept lists, scores and quantised queries it reads.
+    `ev` = 8 timing events (5 on the main stream around predict, indexer and
+    top-k plus the wait for the quantiser; 3 on `side` around quantise and
+    update), or None.  Returns the event that marks this round's update as
+    done.
     """
     import torch
 
@@ -122,12 +133,20 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
     main = torch.cuda.current_stream()
     if prev_update is not None:
         main.wait_event(prev_update)
-    ev = ev or [None] * 7
+    ev = ev or [None] * 8
     rec = lambda e, s: e.record(s) if e is not None else None
     rec(ev[0], main)
     spin.spin_predict_blocks(st.handle, 0, b["batch"], keep_bp, b["kept"], b["cnt"], b["flags"])
     rec(ev[1], main)
-    spin.spin_quantize_q(st.handle, b["batch"], q, w)
+    # quantiser on the side stream (already ordered after the previous update)
+    qs = side if QUANTIZE_ON_SIDE else main
+    rec(ev[5], qs)
+    spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
+    rec(ev[6], qs)
+    if QUANTIZE_ON_SIDE:
+        q_done = torch.cuda.Event()
+        q_done.record(side)
+        main.wait_event(q_done)
     rec(ev[2], main)
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
                              pool.block_table, b["kept"], b["cnt"], b["scores"], b["pmax"])
@@ -138,9 +157,14 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
                           b["topk_ws"], b["pmax"])
     rec(ev[4], main)
     side.wait_event(idx_done)
-    rec(ev[5], side)
+    if SPACER_CYCLES:
+        # a few microseconds of one-workgroup spin on the side stream, so the
+        # top-k's 96 full-CU workgroups are dispatched before the update's fill
+        # the GPU (both become ready when the indexer ends)
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(SPACER_CYCLES)
     spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"], stream=side)
-    rec(ev[6], side)
+    rec(ev[7], side)
     upd_done = torch.cuda.Event()
     upd_done.record(side)
     return upd_done
@@ -164,7 +188,7 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
             bufs["qpos"].fill_(base_q + t)
             done = _round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep_bp, side, done)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
         qpos_host = [base_q + warmup + t for t in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -177,11 +201,15 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
         wall = time.perf_counter() - t0
         per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
         for e in evs:
-            for i, n in enumerate(["predict", "quantize", "indexer", "topk"]):
-                per[n].append(e[i].elapsed_time(e[i + 1]) * 1e3)      # us
-            per["update"].append(e[5].elapsed_time(e[6]) * 1e3)
+            per["predict"].append(e[0].elapsed_time(e[1]) * 1e3)       # us
+            per["quantize"].append(e[5].elapsed_time(e[6]) * 1e3)      # beside predict
+            per["indexer"].append(e[2].elapsed_time(e[3]) * 1e3)
+            per["topk"].append(e[3].elapsed_time(e[4]) * 1e3)
+            per["update"].append(e[3].elapsed_time(e[7]) * 1e3)        # from the indexer's end
         # a round ends when both the top-k (main) and the update (side) are done
-        per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[6])) * 1e3 for e in evs]
+        per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[7])) * 1e3 for e in evs]
+        # critical path to the top-k: predict, the wait for the quantiser, indexer, top-k
+        per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
         cnt = bufs["cnt"].cpu()
         kept_pages = int(cnt.sum())
         if st.error() != 0:
@@ -265,6 +293,9 @@ def main():
     wl = WORKLOADS[a.workload]
     device = "cuda:0"
     torch.cuda.set_device(0)
+    global QUANTIZE_ON_SIDE, SPACER_CYCLES
+    QUANTIZE_ON_SIDE = not a.quantize_on_main
+    SPACER_CYCLES = a.spacer_cycles
     keep_main = 10000 - a.sparsity_bp
     sweep = [10000 - int(s) for s in a.sweep.split(",") if s.strip() != ""]
     keeps = [keep_main] + [k for k in sweep if k != keep_main]
@@ -275,8 +306,7 @@ def main():
     main_r = res[keep_main]
     per = main_r["per_us"]
     step_us = per["step"]
-    pit = [per["predict"][i] + per["quantize"][i] + per["indexer"][i] + per["topk"][i]
-           for i in range(a.steps)]
+    pit = per["to_topk"]
     ms_per_step = main_r["wall_s"] * 1e3 / a.steps
     tokens_per_step = main_r["kept_pages"] * 64
     value = tokens_per_step / (ms_per_step / 1e3)
@@ -324,7 +354,9 @@ def main():
             "predict_index_topk_p90": round(_pct(pit, 90), 2),
             "update_median": round(_median(per["update"]), 2),
             "whole_step_median": round(_median(step_us), 2),
-            **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items() if n != "step"},
+            **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items()
+               if n not in ("step", "to_topk")},
+            "quantize_overlaps_predict": QUANTIZE_ON_SIDE,
             "update_overlaps_topk": True,
         },
         "realized_block_sparsity": 1.0 - main_r["kept_pages"] / main_r["blocks"],

@@ -2,7 +2,8 @@
 // selection, Philox exploration and the MTP row union.
 //
 // Two kernels per call:
-//   k_block_scores  (B x R x block-chunks workgroups, streams D and VB)
+//   k_block_scores  (B x R x block-chunks workgroups, streams D and VB, 128
+//                    blocks per wave with one batch of loads in flight)
 //       S_j = max over existing slots i of block j of max(V_i, D_{q-i}).
 //       For a block wholly at or before q this equals max(VB_j, max of the
 //       D window), where VB_j (the block max of V) is kept exact by the update
@@ -19,7 +20,13 @@ namespace spin {
 namespace {
 
 constexpr int kScoreWaves = 4;        // waves per workgroup in k_block_scores
-constexpr int kScoreBlocksPerWave = 16;
+constexpr int kScoreBatch = 16;       // blocks per load batch (one D load per lane per block)
+#ifndef SPIN_SCORE_BATCHES
+#define SPIN_SCORE_BATCHES 8
+#endif
+constexpr int kScoreBatchesPerWave = SPIN_SCORE_BATCHES;
+constexpr int kScoreBlocksPerWave = kScoreBatch * kScoreBatchesPerWave;   // 128
+static_assert(kScoreBatchesPerWave % 2 == 0, "double-buffered batches");
 constexpr int kSelectThreads = 1024;
 constexpr size_t kResidentLdsMax = 150 * 1024;   // dynamic LDS for the resident selection
 
@@ -36,6 +43,14 @@ __device__ __forceinline__ bool request_ok(const SpinView& v, const spin_batch& 
          num_blocks_of(q0 + bt.R - 1) <= bt.max_blocks && bt.max_blocks <= v.max_blocks;
 }
 
+// grid (ceil(max_blocks / (W * kScoreBlocksPerWave)), B, R), W waves: wave w
+// of workgroup x scores the kScoreBlocksPerWave consecutive blocks from
+// (x*W + w) * kScoreBlocksPerWave, in batches of kScoreBatch with the next
+// batch's loads in flight while the current one is reduced.  Lane l reads
+// D_{q - i} of slot i = 64 j + l (every batch issues the same loads; blocks
+// past the last full one read D_0 and are masked), and lanes 0..15 read VB of
+// the batch's blocks.  The partial block holding q (if any) is scored apart
+// from V and D directly.
 __global__ void __launch_bounds__(kScoreWaves * kWave)
 k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int b = blockIdx.y, r = blockIdx.z;
@@ -49,29 +64,55 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   int kb, nexp;
   budget(keep_bp, n, v.explore_bp, &kb, &nexp);
   if (kb >= n) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int jw = (blockIdx.x * kScoreWaves + wave) * kScoreBlocksPerWave;
+  if (jw >= n) return;
 
   const float* V = v.V + row * v.max_ctx;
   const float* D = v.D + row * v.max_ctx;
   const float* VB = v.VB + row * v.max_blocks;
   float* out = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
   const int l = lane_id();
-  const int j0 = (blockIdx.x * kScoreWaves + threadIdx.x / kWave) * kScoreBlocksPerWave;
+  const int nfull = (q + 1) / kBlock;          // blocks wholly at or before q
 
-  float d[kScoreBlocksPerWave], vv[kScoreBlocksPerWave];
+  float dbuf[2][kScoreBatch];
+  float vbuf[2];
+  auto issue = [&](int u, int t) {
+    const int jb = jw + t * kScoreBatch;
 #pragma unroll
-  for (int m = 0; m < kScoreBlocksPerWave; ++m) {
-    const int j = j0 + m;
-    const int i = j * kBlock + l;
-    const bool in = (j < n) && (i <= q);
-    d[m] = in ? D[q - i] : -INFINITY;
-    const bool full = (j * kBlock + kBlock - 1) <= q;
-    vv[m] = (j < n) ? (full ? VB[j] : (in ? V[i] : -INFINITY)) : -INFINITY;
+    for (int m = 0; m < kScoreBatch; ++m) {
+      const int j = jb + m;
+      dbuf[u][m] = D[j < nfull ? q - (j * kBlock + l) : 0];
+    }
+    const int jl = jb + (l % kScoreBatch);
+    vbuf[u] = VB[jl < nfull ? jl : 0];
+  };
+  auto reduce = [&](int u, int t) {
+    const int jb = jw + t * kScoreBatch;
+    float mine = -INFINITY;                    // lane m < kScoreBatch keeps S of block jb + m
+#pragma unroll
+    for (int m = 0; m < kScoreBatch; ++m) {
+      const float dm = wave_max(dbuf[u][m]);
+      if (l == m) mine = dm;
+    }
+    mine = fmaxf(mine, vbuf[u]);
+    if (l < kScoreBatch && jb + l < nfull) out[jb + l] = mine;
+  };
+  issue(0, 0);
+#pragma unroll
+  for (int t = 0; t < kScoreBatchesPerWave; t += 2) {
+    issue(1, t + 1);
+    reduce(0, t);
+    if (t + 2 < kScoreBatchesPerWave) issue(0, t + 2);
+    reduce(1, t + 1);
   }
-#pragma unroll
-  for (int m = 0; m < kScoreBlocksPerWave; ++m) {
-    const int j = j0 + m;
-    const float sj = wave_max(fmaxf(d[m], vv[m]));
-    if (l == 0 && j < n) out[j] = sj;
+
+  // the partial block (slots 64 nfull .. q), owned by the wave whose range holds it
+  if (nfull < n && nfull >= jw && nfull < jw + kScoreBlocksPerWave) {
+    const int i = nfull * kBlock + l;
+    const float z = (i <= q) ? fmaxf(V[i], D[q - i]) : -INFINITY;
+    const float sj = wave_max(z);
+    if (l == 0) out[nfull] = sj;
   }
 }
 
