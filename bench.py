@@ -22,12 +22,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_DENSE_PEAK_TFLOPS = 5000.0 # MI355X dense fp8 MFMA
 PAGE_BYTES = 64 * 128          # fp8 keys of one 64-token page
 # Algorithmic bytes the indexer kernel moves per kept page and row: the page's
 # keys, its scale, its block-table entry, its kept-list entry, 64 fp32 scores
-# and the page's maximum score per row.
+# and the page's four quarter maxima per row.
 IDX_BYTES_PER_PAGE = PAGE_BYTES + 4 + 4 + 4
-IDX_SCORE_BYTES_PER_PAGE_ROW = 64 * 4 + 4       # scores + the page maximum
+IDX_SCORE_BYTES_PER_PAGE_ROW = 64 * 4 + 16      # scores + the page's quarter maxima
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_indexer_ctx512k-b96_hbm_traffic.md")
@@ -100,7 +101,7 @@ def _setup(wl, device):
         scores=torch.empty(B, wl.rows, nb * 64, dtype=torch.float32, device=device),
         topk=torch.empty(B, wl.rows, wl.topk, dtype=torch.int32, device=device),
     )
-    bufs["pmax"] = torch.empty(B, wl.rows, nb, dtype=torch.float32, device=device)
+    bufs["pq"] = torch.empty(B, wl.rows, nb, 4, dtype=torch.float32, device=device)
     bufs["topk_ws"] = torch.empty(max(256, spin.spin_topk_workspace_bytes(bufs["batch"], wl.topk)),
                                   dtype=torch.uint8, device=device)
     return spin, pool, cfg, st, bufs, make_queries
@@ -110,7 +111,7 @@ QUANTIZE_ON_SIDE = True
 SPACER_CYCLES = 0
 
 
-def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
+def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None, accepted=None):
     """One SPIN round.
 
     Main stream: predict -> indexer -> top-k.  `side` runs the query
@@ -124,8 +125,9 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
     overwrites the kept lists, scores and quantised queries it reads.
     `ev` = 8 timing events (5 on the main stream around predict, indexer and
     top-k plus the wait for the quantiser; 3 on `side` around quantise and
-    update), or None.  Returns the event that marks this round's update as
-    done.
+    update), or None.  `accepted` (int32 [B], device): MTP acceptances, whose
+    prefix-valid replay replaces the single-row update.  Returns the event that
+    marks this round's update as done.
     """
     import torch
 
@@ -149,12 +151,12 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
         main.wait_event(q_done)
     rec(ev[2], main)
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
-                             pool.block_table, b["kept"], b["cnt"], b["scores"], b["pmax"])
+                             pool.block_table, b["kept"], b["cnt"], b["scores"], b["pq"])
     idx_done = torch.cuda.Event()
     idx_done.record(main)
     rec(ev[3], main)
     spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
-                          b["topk_ws"], b["pmax"])
+                          b["topk_ws"], b["pq"])
     rec(ev[4], main)
     side.wait_event(idx_done)
     if SPACER_CYCLES:
@@ -163,7 +165,11 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
         # the GPU (both become ready when the indexer ends)
         with torch.cuda.stream(side):
             torch.cuda._sleep(SPACER_CYCLES)
-    spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"], stream=side)
+    if accepted is None:
+        spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"], stream=side)
+    else:
+        spin.spin_mtp_replay(st.handle, 0, b["batch"], accepted, b["scores"], b["kept"], b["cnt"],
+                             stream=side)
     rec(ev[7], side)
     upd_done = torch.cuda.Event()
     upd_done.record(side)
@@ -173,10 +179,23 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None):
 def _run_gpu(wl, keep_bps, steps, warmup, device):
     import torch
 
+    from workload import acceptances, positions
+
     spin, pool, cfg, st, bufs, make_queries = _setup(wl, device)
     T = warmup + steps
-    base_q = wl.ctx - T
-    qs = [make_queries(wl, pool, 0, t, [base_q + t] * wl.batch, device=device) for t in range(T)]
+    if wl.rows == 1:
+        qpos_all = (torch.arange(T, dtype=torch.int64) + (wl.ctx - T))[:, None].repeat(1, wl.batch)
+        acc_all = None
+    else:
+        # MTP: each request advances by its accepted drafts + 1 per round, and
+        # the round's EMA update is the prefix-valid replay of those rows
+        if T > wl.steps:
+            raise SystemExit(f"{wl.name} has {wl.steps} rounds; asked for {T}")
+        acc = acceptances(wl)
+        qpos_all = positions(wl, acc)[:T]
+        acc_all = acc[:T].to(torch.int32).to(device)
+    qs = [make_queries(wl, pool, 0, t, qpos_all[t].tolist(), device=device) for t in range(T)]
+    qpos_all = qpos_all.to(torch.int32).to(device)
     torch.cuda.synchronize()
     results = {}
     side = torch.cuda.Stream(device=device)          # default priority
@@ -184,19 +203,21 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
         spin.spin_reset_slots(st.handle, bufs["slot"],
                               torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
         done = None
+        acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
         for t in range(warmup):
-            bufs["qpos"].fill_(base_q + t)
-            done = _round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep_bp, side, done)
+            bufs["qpos"].copy_(qpos_all[t])
+            done = _round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep_bp, side, done,
+                          accepted=acc_of(t))
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
-        qpos_host = [base_q + warmup + t for t in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         done = None
         for t in range(steps):
-            bufs["qpos"].fill_(qpos_host[t])
+            bufs["qpos"].copy_(qpos_all[warmup + t])
             q, w = qs[warmup + t]
-            done = _round(spin, st, bufs, pool, q, w, keep_bp, side, done, evs[t])
+            done = _round(spin, st, bufs, pool, q, w, keep_bp, side, done, evs[t],
+                          accepted=acc_of(warmup + t))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
@@ -248,7 +269,7 @@ def _cpu_baseline(wl, keep_bp, n_req):
     kv = O.e4m3fn_decode(pool.key_codes.numpy())
     scv = pool.key_scale.numpy().astype(np.float64)
     table = pool.block_table[0].numpy()
-    q = wl.ctx - 1
+    q = wl.ctx - wl.rows
     qb, w = make_queries(wl1, pool, 0, 5, [q], device="cpu")
     qv, wv, _, _ = O.fp8_query_operands(qb[0].float().numpy(), w[0].numpy())
     tokens = 0
@@ -259,7 +280,7 @@ def _cpu_baseline(wl, keep_bp, n_req):
         st.D[:] = random_state(wl.ctx, 0.0, seed=r + 77).double().numpy()
         st.step = 5
         t0 = time.perf_counter()
-        out = O.decode_round(st, q, 1, keep_bp, wl.explore_bp, 0x5350494E, 0, qv, wv, kv, scv,
+        out = O.decode_round(st, q, wl.rows, keep_bp, wl.explore_bp, 0x5350494E, 0, qv, wv, kv, scv,
                              table, wl.topk, wl.alpha)
         elapsed += time.perf_counter() - t0
         tokens += len(out["kept"]) * 64
@@ -311,6 +332,7 @@ def main():
     tokens_per_step = main_r["kept_pages"] * 64
     value = tokens_per_step / (ms_per_step / 1e3)
     idx_us = sum(per["indexer"]) / a.steps
+    idx_flops = main_r["kept_pages"] * 64 * wl.rows * wl.heads * wl.head_dim * 2
     idx_bytes = main_r["kept_pages"] * (IDX_BYTES_PER_PAGE + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW)
     achieved = idx_bytes / (idx_us * 1e-6) / 1e9
     sweep_out = {}
@@ -346,6 +368,7 @@ def main():
                    "target_sparsity_bp": a.sparsity_bp, "explore_bp": wl.explore_bp,
                    "rows": wl.rows, "block_table": "shuffled" if wl.shuffle else "identity"},
         "indexer_tokens_per_s": tokens_per_step / (idx_us * 1e-6),
+        "indexer_row_tokens_per_s": wl.rows * tokens_per_step / (idx_us * 1e-6),
         "indexer_roofline_tokens_per_s": HBM_PEAK_GBS * 1e9 / (
             IDX_BYTES_PER_PAGE / 64 + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW / 64),
         "per_step_us": {
@@ -364,6 +387,10 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _measured_traffic(wl.name, a.sparsity_bp),
                      "bytes_per_launch": idx_bytes},
+        "indexer_mfma": {"dtype": "fp8 e4m3", "flops_per_launch": idx_flops,
+                         "achieved_tflops": round(idx_flops / (idx_us * 1e-6) / 1e12, 1),
+                         "peak_tflops": FP8_DENSE_PEAK_TFLOPS,
+                         "frac": round(idx_flops / (idx_us * 1e-6) / 1e12 / FP8_DENSE_PEAK_TFLOPS, 4)},
         "sweep": sweep_out,
         "cpu_baseline": cpu,
         "context": "pages' serving run: 4720 -> 5421 output TPS (+14.9% at 50% sparsity, 8x B300, "

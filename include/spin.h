@@ -101,12 +101,12 @@ typedef struct spin_batch {
  *   qexp [max_slots][max_rows][heads] int32   workspace: query exponents e
  *   bscore [max_slots][max_rows][max_blocks]  workspace: block scores S
  *   ukey [max_slots][max_blocks] uint64       workspace: exploration keys
- *   page_max [max_slots][max_rows][max_blocks] workspace: page maxima for the top-k
+ *   page_qmax [max_slots][max_rows][max_blocks][4] workspace: per-page quarter maxima
  *   topk_ws                                   empty (= total): the state's top-k runs on
- *                                             the page maxima and needs no workspace
+ *                                             the page quarter maxima and needs no workspace
  * Workspace arrays are indexed by batch position b, not by slot. */
 typedef struct spin_state_layout {
-  size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, page_max, topk_ws,
+  size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, page_qmax, topk_ws,
       total;
   int32_t max_blocks;     /* ceil(max_ctx / 64) */
   int32_t reserved;
@@ -182,16 +182,17 @@ int spin_quantize_q(spin_state* st, const spin_batch* batch, const void* q_bf16,
  * otherwise), in kept order: element k*64 + t is slot 64*kept_blocks[b][k] + t;
  * slots after the row's position get -inf; entries past the row's kept count
  * are not written.
- * page_max (may be NULL): fp32 [B][R][max_blocks], element k = the largest of
- * the 64 scores of kept page k for that row (-inf if all are masked); it is
- * the optional top-k prefilter input of spin_topk_scores. */
+ * page_qmax (may be NULL): fp32 [B][R][max_blocks][4], 16-byte aligned: for kept page k of
+ * each row, element c = the largest score of its slots 16c .. 16c+15 (-inf if
+ * all are masked); it is the optional top-k prefilter input of
+ * spin_topk_scores. */
 int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* k_pool,
                         const float* k_scale, int64_t pool_pages, const int32_t* block_table,
                         const int32_t* kept_blocks, const int32_t* kept_count, float* scores,
-                        float* page_max, hipStream_t stream);
+                        float* page_qmax, hipStream_t stream);
 
 /* Bytes of caller-owned device workspace spin_topk_scores needs for this
- * batch shape and K when it is called without page maxima (0 when every row
+ * batch shape and K when it is called without page quarter maxima (0 when every row
  * fits one 16384-candidate chunk). */
 int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
 
@@ -200,17 +201,18 @@ int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
  * ties to the lower slot, written ascending to topk_out int32 [B][R][topk],
  * padded with -1.  -0.0 ranks equal to +0.0.  scores as spin_indexer_scores
  * writes them, 16-byte aligned (only slots <= q_r are read as candidates).  topk: 4..4096, a
- * multiple of 4.  page_max (may be NULL): the per-page maxima written by
- * spin_indexer_scores for these scores; with at least `topk` valid pages its
- * topk-th largest value is a lower bound of the answer's smallest score, so
- * scores below it are dropped before ranking (the result is the same).
- * With page_max the whole top-k is one kernel and needs no workspace.
+ * multiple of 4.  page_qmax (may be NULL, else 16-byte aligned): the per-page
+ * quarter maxima written by spin_indexer_scores for these scores; they belong to distinct
+ * slots, so the topk-th largest of them is a lower bound of the answer's
+ * smallest score, and scores below it are dropped before ranking (the result
+ * is the same).
+ * With page_qmax the whole top-k is one kernel and needs no workspace.
  * Without it, workspace: 256-byte aligned device memory of at least
  * spin_topk_workspace_bytes() bytes (may be NULL when the rows fit one
  * 16384-candidate chunk); its contents need no initialisation and are
  * clobbered.  batch->slot is not read. */
 int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
-                     const float* page_max, const int32_t* kept_blocks, const int32_t* kept_count,
+                     const float* page_qmax, const int32_t* kept_blocks, const int32_t* kept_count,
                      int32_t* topk_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 

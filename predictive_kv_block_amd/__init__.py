@@ -51,7 +51,7 @@ class SpinBatch(ctypes.Structure):
 class SpinLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("V", "D", "VB", "step", "request_id", "error", "q8", "wq", "qexp",
-                 "bscore", "ukey", "page_max", "topk_ws", "total")] + [
+                 "bscore", "ukey", "page_qmax", "topk_ws", "total")] + [
         ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
@@ -179,10 +179,10 @@ def spin_quantize_q(h, batch, q_bf16, w, stream=None):
 
 
 def spin_indexer_scores(h, batch, k_pool, k_scale, block_table, kept_blocks, kept_count, scores,
-                        page_max=None, stream=None):
+                        page_qmax=None, stream=None):
     _check(load().spin_indexer_scores(h, ctypes.byref(batch), _p(k_pool), _p(k_scale),
                                       int(k_scale.numel()), _p(block_table), _p(kept_blocks),
-                                      _p(kept_count), _p(scores), _p(page_max), _stream(stream)))
+                                      _p(kept_count), _p(scores), _p(page_qmax), _stream(stream)))
 
 
 def spin_topk_workspace_bytes(batch, topk):
@@ -192,11 +192,11 @@ def spin_topk_workspace_bytes(batch, topk):
 
 
 def spin_topk_scores(batch, topk, scores, kept_blocks, kept_count, topk_out, workspace=None,
-                     page_max=None, stream=None):
+                     page_qmax=None, stream=None):
     """workspace: a uint8 device tensor of >= spin_topk_workspace_bytes bytes;
-    page_max: the optional page maxima from spin_indexer_scores."""
+    page_qmax: the optional per-page quarter maxima from spin_indexer_scores."""
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().spin_topk_scores(ctypes.byref(batch), int(topk), _p(scores), _p(page_max),
+    _check(load().spin_topk_scores(ctypes.byref(batch), int(topk), _p(scores), _p(page_qmax),
                                    _p(kept_blocks), _p(kept_count), _p(topk_out), _p(workspace),
                                    nbytes, _stream(stream)))
 

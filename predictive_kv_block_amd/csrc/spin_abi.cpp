@@ -50,7 +50,7 @@ spin_state_layout make_layout(const spin_config* c) {
   l.qexp = off;       off = align_up(off + S * R * H * 4);
   l.bscore = off;     off = align_up(off + S * R * MB * 4);
   l.ukey = off;       off = align_up(off + S * MB * 8);
-  l.page_max = off;   off = align_up(off + S * R * MB * 4);
+  l.page_qmax = off;   off = align_up(off + S * R * MB * 16);
   l.topk_ws = off;     // empty: with page maxima the top-k needs no workspace
   l.total = off;
   l.max_blocks = int32_t(MB);
@@ -124,7 +124,7 @@ int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes, hipSt
   v.qexp = reinterpret_cast<int32_t*>(st->base + lay.qexp);
   v.bscore = reinterpret_cast<float*>(st->base + lay.bscore);
   v.ukey = reinterpret_cast<uint64_t*>(st->base + lay.ukey);
-  v.pmax = reinterpret_cast<float*>(st->base + lay.page_max);
+  v.pqmax = reinterpret_cast<float*>(st->base + lay.page_qmax);
   v.topk_ws = nullptr;
   v.topk_ws_bytes = 0;
   v.L = cfg->num_layers;
@@ -184,16 +184,18 @@ int spin_quantize_q(spin_state* st, const spin_batch* batch, const void* q_bf16,
 int spin_indexer_scores(spin_state* st, const spin_batch* batch, const uint8_t* k_pool,
                         const float* k_scale, int64_t pool_pages, const int32_t* block_table,
                         const int32_t* kept_blocks, const int32_t* kept_count, float* scores,
-                        float* page_max, hipStream_t stream) {
+                        float* page_qmax, hipStream_t stream) {
   int rc = check_batch(st, batch);
   if (rc) return rc;
   if (!k_pool || !k_scale || pool_pages < 1 || pool_pages > (int64_t(1) << 31) || !block_table ||
       !kept_blocks || !kept_count || !scores)
     return SPIN_EINVAL;
-  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0) return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(page_qmax) % 16 != 0)
+    return SPIN_EINVAL;
   if (!indexer_shape_ok(st)) return SPIN_EUNSUPPORTED;
   return hip_status(spin::launch_indexer(st->view, *batch, k_pool, k_scale, pool_pages,
-                                         block_table, kept_blocks, kept_count, scores, page_max,
+                                         block_table, kept_blocks, kept_count, scores, page_qmax,
                                          stream));
 }
 
@@ -206,7 +208,7 @@ int spin_topk_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes) 
 }
 
 int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
-                     const float* page_max, const int32_t* kept_blocks, const int32_t* kept_count,
+                     const float* page_qmax, const int32_t* kept_blocks, const int32_t* kept_count,
                      int32_t* topk_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
   int rc = check_plain_batch(batch);
@@ -214,12 +216,14 @@ int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
   if (topk < 1 || topk > 4096 || topk % 4 != 0 || !scores || !kept_blocks || !kept_count ||
       !topk_out)
     return SPIN_EINVAL;
-  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0) return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(page_qmax) % 16 != 0)
+    return SPIN_EINVAL;
   const spin::TopkPlan p = spin::topk_plan(batch->B * batch->R, batch->max_blocks, topk);
-  if (!page_max && p.levels > 1 && (!workspace || workspace_bytes < p.bytes))
+  if (!page_qmax && p.levels > 1 && (!workspace || workspace_bytes < p.bytes))
     return SPIN_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPIN_EINVAL;
-  return hip_status(spin::launch_topk(*batch, topk, scores, page_max, kept_blocks, kept_count,
+  return hip_status(spin::launch_topk(*batch, topk, scores, page_qmax, kept_blocks, kept_count,
                                       topk_out, workspace, stream));
 }
 
@@ -235,9 +239,9 @@ int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf1
   rc = spin_quantize_q(st, batch, q_bf16, w, stream);
   if (rc) return rc;
   rc = spin_indexer_scores(st, batch, k_pool, k_scale, pool_pages, block_table, kept_blocks,
-                           kept_count, scores, st->view.pmax, stream);
+                           kept_count, scores, st->view.pqmax, stream);
   if (rc) return rc;
-  return spin_topk_scores(batch, st->cfg.topk, scores, st->view.pmax, kept_blocks, kept_count,
+  return spin_topk_scores(batch, st->cfg.topk, scores, st->view.pqmax, kept_blocks, kept_count,
                           topk_out, nullptr, 0, stream);
 }
 

@@ -5,8 +5,8 @@
 //   wq = w * 2^e, so sum_h wq_h ReLU(q8_h . k) equals the bf16-query score up
 //   to the rounding of q to e4m3fn.
 // k_indexer: one wave per kept page (64 tokens x 128 fp8 = 8 KB, contiguous in
-//   the pool); optionally also the page's maximum score per row, which lets
-//   the top-k discard most candidates before ranking them.  Heads form the M side of v_mfma_scale_f32_16x16x128_f8f6f4 and
+//   the pool); optionally also, per row, the maxima of the page's four 16-slot
+//   quarters, which let the top-k discard most candidates before ranking them.  Heads form the M side of v_mfma_scale_f32_16x16x128_f8f6f4 and
 //   tokens the N side, so one MFMA does 16 heads x 16 tokens over the whole
 //   head dim; a page is 4 head tiles x 4 token tiles per row.  ReLU, the head
 //   weights and the head sum run on the accumulator registers, the 4 lane
@@ -172,7 +172,7 @@ template <int R>
 __global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
-          const int32_t* kept, const int32_t* kept_count, float* scores, float* page_max) {
+          const int32_t* kept, const int32_t* kept_count, float* scores, float* page_qmax) {
   constexpr int F = kFlushRows / R > 0 ? kFlushRows / R : 1;   // pages per flush
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kDim];
   __shared__ float s_w[R * kHeads];
@@ -250,9 +250,20 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           out = (j * kBlock + l <= q0 + r) ? val * sc : -INFINITY;
         }
         my_out[(r * F + mf) * kBlock + l] = out;
-        if (page_max) {   // every lane writes the same word (no divergent store)
-          const float pm = wave_max(out);
-          page_max[(size_t(b) * R + r) * mb + kw + m] = pm;
+        if (page_qmax) {
+          // maxima of the page's four 16-slot quarters (DPP row reduction;
+          // lane 16c + 15 holds quarter c), written as one 16-byte row
+          float x = out;
+          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                           __float_as_int(-INFINITY), __float_as_int(x), 0x111, 0xF, 0xF, false)));
+          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                           __float_as_int(-INFINITY), __float_as_int(x), 0x112, 0xF, 0xF, false)));
+          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                           __float_as_int(-INFINITY), __float_as_int(x), 0x114, 0xF, 0xF, false)));
+          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                           __float_as_int(-INFINITY), __float_as_int(x), 0x118, 0xF, 0xF, false)));
+          if ((l & 15) == 15)
+            page_qmax[((size_t(b) * R + r) * mb + kw + m) * 4 + (l >> 4)] = x;
         }
       }
       if (mf == F - 1 || m + 1 == npages) {
@@ -298,26 +309,26 @@ hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* 
 hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t* k_pool,
                           const float* k_scale, int64_t pool_pages, const int32_t* table,
                           const int32_t* kept, const int32_t* kept_count, float* scores,
-                          float* page_max, hipStream_t s) {
+                          float* page_qmax, hipStream_t s) {
   const int per_wg = kIdxWaves * kPagesPerWave;
   const dim3 grid(unsigned((bt.max_blocks + per_wg - 1) / per_wg), unsigned(bt.B));
   const dim3 block(kIdxWaves * kWave);
   switch (bt.R) {
     case 1:
       hipLaunchKernelGGL(k_indexer<1>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_max);
+                         table, kept, kept_count, scores, page_qmax);
       break;
     case 2:
       hipLaunchKernelGGL(k_indexer<2>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_max);
+                         table, kept, kept_count, scores, page_qmax);
       break;
     case 3:
       hipLaunchKernelGGL(k_indexer<3>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_max);
+                         table, kept, kept_count, scores, page_qmax);
       break;
     case 4:
       hipLaunchKernelGGL(k_indexer<4>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_max);
+                         table, kept, kept_count, scores, page_qmax);
       break;
     default:
       return hipErrorInvalidValue;

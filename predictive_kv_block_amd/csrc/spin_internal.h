@@ -18,7 +18,7 @@ struct SpinView {
   int32_t* qexp;     // [S][max_rows][H]
   float* bscore;     // [S][max_rows][max_blocks]
   uint64_t* ukey;    // [S][max_blocks]
-  float* pmax;       // [S][max_rows][max_blocks] page maxima of the last indexer call
+  float* pqmax;      // [S][max_rows][max_blocks][4] per-page quarter maxima of the last indexer call
   void* topk_ws;     // top-k level buffers for max_slots * max_rows rows
   size_t topk_ws_bytes;
   int L, S, max_ctx, max_blocks, H, d, max_rows, topk, warmup, explore_bp;
@@ -57,8 +57,8 @@ hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* 
 hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t* k_pool,
                           const float* k_scale, int64_t pool_pages, const int32_t* table,
                           const int32_t* kept, const int32_t* kept_count, float* scores,
-                          float* page_max, hipStream_t s);
-hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_max,
+                          float* page_qmax, hipStream_t s);
+hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_qmax,
                        const int32_t* kept, const int32_t* kept_count, int32_t* out, void* ws,
                        hipStream_t s);
 hipError_t launch_update(const SpinView& v, int layer, const spin_batch& bt,

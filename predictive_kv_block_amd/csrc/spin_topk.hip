@@ -4,14 +4,15 @@
 // order (= ascending position).  The selection is exact, with ties to the
 // lower position.
 //
-// With the indexer's per-page maxima, k_topk_fused answers every row in one
-// launch (one workgroup per row): t1 = the K-th largest page maximum.  Each
-// page whose maximum is >= t1 holds at least one score >= t1, so with at
-// least K valid pages the row's K-th largest score is >= t1 and every score
-// < t1 can be dropped.  Only pages with maximum >= t1 are read; their scores
-// >= t1 are gathered in position order and ranked exactly.  A row that does
-// not fit those buffers is walked in chunks by the same workgroup, keeping a
-// running top-K.
+// With the indexer's per-page quarter maxima (the largest score of each
+// 16-slot quarter of a page), k_topk_fused answers every row in one launch
+// (one workgroup per row): t1 = the K-th largest of the pages' top quarter
+// maxima.  Those are scores of distinct slots, so the row's K-th largest score
+// is >= t1 and every score < t1 can be dropped; only pages whose maximum is
+// >= t1 can hold such scores.  Those pages are read, their scores >= t1
+// gathered in position order and ranked exactly.  A row that does not fit
+// those buffers is walked in chunks by the same workgroup, keeping a running
+// top-K.
 //
 // Without page maxima, the chunked levels (k_topk_level):
 // 1. level 0: the row is cut into chunks of kChunk; each chunk's candidates
@@ -334,11 +335,12 @@ __device__ int lds_topk(FusedShared& sh, int n, int K, int32_t* out) {
 }
 
 // grid (rows), 1024 threads: the whole top-k of a row.
-// Fast path (at least K valid pages, at most 16384 kept pages): t1 = the K-th
-// largest page maximum; only pages whose maximum is >= t1 can hold scores
-// >= t1, and those scores (at least K of them) are collected in position
-// order and ranked exactly.
-// Fallback (the row has fewer than K valid pages, more than kFusedCandPages
+// Fast path (at most 16384 kept pages and at least K finite quarter maxima
+// among the ones used): t1 = the K-th largest of the pages' top-m quarter
+// maxima (m = 1, 2 or 4); only pages whose maximum is >= t1 can hold scores
+// >= t1, and those scores (at least K of them) are collected in position order
+// and ranked exactly.
+// Fallback (fewer than K finite quarter maxima, more than kFusedCandPages
 // candidate pages or more than kFusedCap survivors): the row is walked in
 // chunks of 16384 slots (wave w: pages 16w .. 16w+15 of the chunk, lane l:
 // slot l); each chunk's top-K (scores >= t1 when t1 is known) is appended in
@@ -346,7 +348,7 @@ __device__ int lds_topk(FusedShared& sh, int n, int K, int32_t* out) {
 // whenever it holds more.  Every element of the answer is in its chunk's
 // top-K, so nothing of it is lost.
 __global__ void __launch_bounds__(kFusedThreads)
-k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
+k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
              const int32_t* kept, const int32_t* kept_count, int32_t* topk_out) {
   __shared__ FusedShared sh;
   const int row = blockIdx.x;
@@ -361,28 +363,57 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_max,
   int32_t* out = topk_out + size_t(row) * K;
   uint32_t lowest = 1u;                          // smallest key that can be in the answer
 
-  if (page_max && cnt >= K && cnt <= kFusedMaxPages) {
-    const float* pm = page_max + size_t(row) * mb;
-    // 1. t1 over the page maxima (page p = w*1024 + i*64 + l held by lane l)
+  if (page_qmax && cnt >= K / 4 && cnt <= kFusedMaxPages) {
+    const float* pq = page_qmax + size_t(row) * mb * 4;
+    // 1. t1 = the K-th largest of the pages' top-m quarter maxima, m = 1, 2 or
+    // 4: the smallest with m * cnt >= 2K that fits 16 values per lane (value
+    // e = w*1024 + i*64 + l: page e/m, rank e%m).  They are scores of
+    // distinct slots, so at least K slots score >= t1.
+    int lm = 0;
+    while (lm < 2 && (cnt << lm) < 2 * K && (cnt << (lm + 1)) <= kFusedMaxPages) ++lm;
     uint32_t pk[kFusedPageLanes];
 #pragma unroll
     for (int i = 0; i < kFusedPageLanes; ++i) {
-      const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
-      const float v = (p < cnt) ? pm[p] : -INFINITY;
+      const int e = w * (kFusedPageLanes * kWave) + i * kWave + l;
+      const int p = e >> lm, t = e & ((1 << lm) - 1);
+      float v = -INFINITY;
+      if (p < cnt) {
+        const float4 x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
+        if (lm == 2) {
+          v = t == 0 ? x.x : t == 1 ? x.y : t == 2 ? x.z : x.w;
+        } else {
+          const float a = fmaxf(x.x, x.y), b2 = fminf(x.x, x.y);
+          const float c = fmaxf(x.z, x.w), d = fminf(x.z, x.w);
+          const float top1 = fmaxf(a, c);
+          const float top2 = fmaxf(fminf(a, c), fmaxf(b2, d));
+          v = (lm == 1 && t == 1) ? top2 : top1;
+        }
+      }
       pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
     }
-    int npages;
+    int nvals;
     uint32_t kmin, kmax;
-    block_key_stats<kFusedThreads, kFusedPageLanes>(pk, sh.t, &npages, &kmin, &kmax);
-    if (npages >= K) {
+    block_key_stats<kFusedThreads, kFusedPageLanes>(pk, sh.t, &nvals, &kmin, &kmax);
+    if (nvals >= K) {
       uint32_t t1 = kmin;
-      if (npages > K) {
+      if (nvals > K) {
         int n_eq;
         radix_select_regs<kFusedThreads, kFusedPageLanes>(pk, K, kmin, kmax, sh.t, &t1, &n_eq);
       }
       lowest = max(t1, 1u);
 
       // 2. candidate pages (maximum >= t1), listed in ascending kept order
+      // (page p = w*1024 + i*64 + l held by lane l)
+#pragma unroll
+      for (int i = 0; i < kFusedPageLanes; ++i) {
+        const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
+        float v = -INFINITY;
+        if (p < cnt) {
+          const float4 x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
+          v = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+        }
+        pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
+      }
       int mine = 0;
 #pragma unroll
       for (int i = 0; i < kFusedPageLanes; ++i) mine += (pk[i] != 0u && pk[i] >= t1) ? 1 : 0;
@@ -737,7 +768,7 @@ TopkPlan topk_plan(int rows, int max_blocks, int K) {
   return p;
 }
 
-hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_max,
+hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_qmax,
                        const int32_t* kept, const int32_t* kept_count, int32_t* out, void* ws,
                        hipStream_t s) {
   const int rows = bt.B * bt.R;
@@ -757,9 +788,9 @@ hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, cons
       off += align256(p.count_elems * 4);
     }
   }
-  if (page_max) {
+  if (page_qmax) {
     hipLaunchKernelGGL(k_topk_fused, dim3(rows), dim3(kFusedThreads), 0, s, bt, topk, scores,
-                       page_max, kept, kept_count, out);
+                       page_qmax, kept, kept_count, out);
     return hipGetLastError();
   }
   LevelArgs a;

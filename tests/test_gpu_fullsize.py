@@ -26,9 +26,9 @@ def _round(st, bufs, pool, q, w, keep_bp):
     spin.spin_predict_blocks(st.handle, 0, b["batch"], keep_bp, b["kept"], b["cnt"], b["flags"])
     spin.spin_quantize_q(st.handle, b["batch"], q, w)
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
-                             pool.block_table, b["kept"], b["cnt"], b["scores"], b["pmax"])
+                             pool.block_table, b["kept"], b["cnt"], b["scores"], b["pq"])
     spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
-                          b["topk_ws"], b["pmax"])
+                          b["topk_ws"], b["pq"])
 
 
 @pytest.mark.timeout(600)
@@ -48,7 +48,7 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
                 cnt=torch.zeros(B, dtype=torch.int32, device=DEV),
                 flags=torch.zeros(B, nb, dtype=torch.uint8, device=DEV),
                 scores=torch.empty(B, 1, nb * 64, device=DEV),
-                pmax=torch.empty(B, 1, nb, device=DEV),
+                pq=torch.empty(B, 1, nb, 4, device=DEV),
                 topk=torch.empty(B, 1, wl.topk, dtype=torch.int32, device=DEV))
     bufs["topk_ws"] = torch.empty(spin.spin_topk_workspace_bytes(bufs["batch"], wl.topk),
                                   dtype=torch.uint8, device=DEV)
@@ -103,9 +103,10 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
             mg = dict(zip(slots.tolist(), mag[0].tolist()))
             assert_topk_tie_aware(g_topk[b, 0], ref["topk"][0], lambda x: rs[x],
                                   lambda x: score_tol(rs[x], mg[x]), f"round {t} b{b}")
-            # page maxima written by the indexer are the max of its own page scores
-            pm = np_(bufs["pmax"][b, 0, :n])
-            assert np.array_equal(pm, np_(g_scores[b, 0, : n * 64]).reshape(n, 64).max(axis=1))
+            # quarter maxima written by the indexer are those of its own page scores
+            pt = np_(bufs["pq"][b, 0, :n])
+            own = np_(g_scores[b, 0, : n * 64]).reshape(n, 4, 16).max(axis=2)
+            assert np.array_equal(pt, own)
         spin.spin_update(st.handle, 0, bufs["batch"], bufs["scores"], bufs["kept"], bufs["cnt"])
         torch.cuda.synchronize()
         for b in sorted(live):

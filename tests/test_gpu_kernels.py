@@ -93,14 +93,14 @@ def test_indexer_scores_parity(gpu_lib, R):
     rig.kept.copy_(torch.as_tensor(kt))
     rig.kept_count.copy_(torch.as_tensor([len(k) for k in kept], dtype=torch.int32))
     rig.scores.fill_(12345.0)
-    pmax = torch.full((B, R, mb), 777.0, device=DEV)
+    pq = torch.full((B, R, mb, 4), 777.0, device=DEV)
     _say("indexer R", R)
     spin.spin_quantize_q(rig.h, rig.batch, q.to(DEV), w.to(DEV))
     spin.spin_indexer_scores(rig.h, rig.batch, codes.to(DEV), sc.to(DEV),
                              torch.as_tensor(table).to(DEV), rig.kept, rig.kept_count, rig.scores,
-                             pmax)
+                             pq)
     torch.cuda.synchronize()
-    gpm = np_(pmax)
+    gpq = np_(pq)
     kv = O.e4m3fn_decode(np_(codes))
     scv = np_(sc).astype(np.float64)
     got = np_(rig.scores)
@@ -111,18 +111,18 @@ def test_indexer_scores_parity(gpu_lib, R):
         n = len(kept[b]) * 64
         assert_scores_close(got[b, :, :n], ref, mag, f"b{b}")
         assert np.all(got[b, :, n:] == 12345.0)                  # nothing written past kept
-        # page maxima: exactly the max of the GPU's own page scores
+        # quarter maxima: exactly the max of each 16-slot quarter of the GPU's own scores
         nk = len(kept[b])
         if nk:
-            own = got[b, :, :n].reshape(R, nk, 64).max(axis=2)
-            assert np.array_equal(gpm[b, :, :nk], own)
-        assert np.all(gpm[b, :, nk:] == 777.0)
+            own = got[b, :, :n].reshape(R, nk, 4, 16).max(axis=3)
+            assert np.array_equal(gpq[b, :, :nk], own)
+        assert np.all(gpq[b, :, nk:] == 777.0)
     assert rig.state.error() == 0
 
 
 # ------------------------------------------------------------------- top-k
 TOPK_CASES = {
-    # name: (rows R, max_blocks, K, pattern); "+pm" cases pass page maxima
+    # name: (rows R, max_blocks, K, pattern); "pm-" cases pass page quarter maxima
     "random": (2, 120, 512, "random"),
     "ties": (2, 120, 512, "ties"),
     "short": (2, 120, 512, "short"),
@@ -140,6 +140,9 @@ TOPK_CASES = {
     "pm-over-16k-pages": (1, 20000, 2048, "random"),
     "pm-k4096-chunks": (1, 3000, 4096, "random"),
     "pm-zeros": (2, 1200, 512, "zeros"),
+    # as many kept pages as K (the MTP shape: only the quarter-maxima bound filters)
+    "pm-pages-equal-k": (1, 3100, 2048, "random"),
+    "pm-pages-quarter-k": (2, 800, 2048, "random"),
 }
 
 
@@ -180,14 +183,14 @@ def test_topk_exact_on_identical_scores(gpu_lib, case):
     ws.fill_(0xA5)                                               # stale contents must not matter
     pm = None
     if case.startswith("pm-"):
-        # page maxima over each row's valid slots, in kept order (as the indexer writes them)
-        pmh = np.full((B, R, mb), -np.inf, dtype=np.float32)
+        # quarter maxima over each row's valid slots, in kept order (as the indexer writes them)
+        pmh = np.full((B, R, mb, 4), -np.inf, dtype=np.float32)
         for b in range(B):
             for r in range(R):
                 nk = len(kept[b])
                 slot = (kept[b][:, None] * 64 + np.arange(64)).reshape(nk, 64)
                 v = np.where(slot <= qpos[b] + r, sc[b, r, : nk * 64].reshape(nk, 64), -np.inf)
-                pmh[b, r, :nk] = v.max(axis=1)
+                pmh[b, r, :nk] = v.reshape(nk, 4, 16).max(axis=2)
         pm = torch.as_tensor(pmh, device=DEV)
     _say("topk", case)
     spin.spin_topk_scores(bt, K, torch.as_tensor(sc, device=DEV), kept_d, cnt_d, out, ws, pm)
