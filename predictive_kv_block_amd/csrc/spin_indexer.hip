@@ -48,12 +48,33 @@ constexpr int kDim = 128;
 #endif
 constexpr int kIdxWaves = SPIN_IDX_WAVES;
 constexpr int kPagesPerWave = SPIN_IDX_PAGES_PER_WAVE;
-constexpr int kStages = SPIN_IDX_STAGES;
+#ifndef SPIN_IDX_PAGES_PER_WAVE_MR
+#define SPIN_IDX_PAGES_PER_WAVE_MR 16  // the same with several query rows (more workgroups)
+#endif
+template <int R>
+constexpr int pages_per_wave() { return R == 1 ? kPagesPerWave : SPIN_IDX_PAGES_PER_WAVE_MR; }
+constexpr int kStages1 = SPIN_IDX_STAGES;     // ring depth for one query row
+#ifndef SPIN_IDX_STAGES_MR
+#define SPIN_IDX_STAGES_MR 2           // ring depth with several rows (more compute per page)
+#endif
+#ifndef SPIN_IDX_QPAD
+#define SPIN_IDX_QPAD 16               // bytes of LDS padding after each staged head row
+#endif
+// LDS row stride of the staged queries: the pad moves the 16 head rows that
+// one operand read touches onto different banks.
+constexpr int kQStride = kDim + SPIN_IDX_QPAD;
 #ifndef SPIN_IDX_FLUSH_ROWS
 #define SPIN_IDX_FLUSH_ROWS 32         // page-rows of scores staged per wave before a burst write
 #endif
 constexpr int kFlushRows = SPIN_IDX_FLUSH_ROWS;
-static_assert(kStages >= 2 && kPagesPerWave + kStages <= kWave, "indexer pipeline shape");
+#ifndef SPIN_IDX_FLUSH_ROWS_MR
+#define SPIN_IDX_FLUSH_ROWS_MR 32      // the same with several query rows
+#endif
+constexpr int kFlushRowsMR = SPIN_IDX_FLUSH_ROWS_MR;
+static_assert(kStages1 >= 2 && SPIN_IDX_STAGES_MR >= 2 && kPagesPerWave + kStages1 <= kWave &&
+                  SPIN_IDX_PAGES_PER_WAVE_MR + SPIN_IDX_STAGES_MR <= kWave,
+              "indexer pipeline shape");
+static_assert(kQStride % 16 == 0, "16-byte aligned query rows");
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -134,7 +155,7 @@ __device__ __forceinline__ float page_row_score(const PageRegs& kb, const uint8_
   float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    const v8i qa = *reinterpret_cast<const v8i*>(s_q + ((r * kHeads + ht * 16 + n16) * kDim) + g * 32);
+    const v8i qa = *reinterpret_cast<const v8i*>(s_q + (r * kHeads + ht * 16 + n16) * kQStride + g * 32);
     const float4 wv = *reinterpret_cast<const float4*>(s_w + r * kHeads + ht * 16 + g * 4);
     v4f acc[4];
 #pragma unroll
@@ -173,8 +194,11 @@ __global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
           const int32_t* kept, const int32_t* kept_count, float* scores, float* page_qmax) {
-  constexpr int F = kFlushRows / R > 0 ? kFlushRows / R : 1;   // pages per flush
-  __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kDim];
+  constexpr int kPagesPerWaveR = pages_per_wave<R>();
+  constexpr int F = (R == 1 ? kFlushRows : kFlushRowsMR) / R > 0
+                        ? (R == 1 ? kFlushRows : kFlushRowsMR) / R : 1;   // pages per flush
+  constexpr int kStages = R == 1 ? kStages1 : SPIN_IDX_STAGES_MR;
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kQStride];
   __shared__ float s_w[R * kHeads];
   __shared__ __attribute__((aligned(16))) float s_out[kIdxWaves * R * F * kBlock];
   const int b = blockIdx.y;
@@ -183,14 +207,14 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
     if (blockIdx.x == 0 && threadIdx.x == 0) flag_error(v.err, SPIN_ERR_KEPT);
     cnt = cnt < 0 ? 0 : bt.max_blocks;
   }
-  const int first = blockIdx.x * (kIdxWaves * kPagesPerWave);
+  const int first = blockIdx.x * (kIdxWaves * kPagesPerWaveR);
   if (first >= cnt) return;
 
   const int l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const size_t mb = size_t(bt.max_blocks);
-  const int kw = first + wave * kPagesPerWave;           // this wave's first kept position
-  const int npages = max(0, min(kPagesPerWave, cnt - kw));
+  const int kw = first + wave * kPagesPerWaveR;           // this wave's first kept position
+  const int npages = max(0, min(kPagesPerWaveR, cnt - kw));
 
   // Page metadata for this wave's pages, lane m holding page m (j = -1: invalid).
   int my_j = -1, my_p = 0;
@@ -215,7 +239,8 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   const uint8_t* q8 = v.q8 + size_t(b) * v.max_rows * kHeads * kDim;
   const float* wq = v.wq + size_t(b) * v.max_rows * kHeads;
   for (int i = threadIdx.x; i < R * kHeads * kDim / 16; i += kIdxWaves * kWave)
-    reinterpret_cast<uint4*>(s_q)[i] = reinterpret_cast<const uint4*>(q8)[i];
+    *reinterpret_cast<uint4*>(s_q + (i / (kDim / 16)) * kQStride + (i % (kDim / 16)) * 16) =
+        reinterpret_cast<const uint4*>(q8)[i];
   for (int i = threadIdx.x; i < R * kHeads; i += kIdxWaves * kWave) s_w[i] = 0.5f * wq[i];
 
   const int q0 = bt.qpos[b];
@@ -310,7 +335,7 @@ hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t
                           const float* k_scale, int64_t pool_pages, const int32_t* table,
                           const int32_t* kept, const int32_t* kept_count, float* scores,
                           float* page_qmax, hipStream_t s) {
-  const int per_wg = kIdxWaves * kPagesPerWave;
+  const int per_wg = kIdxWaves * (bt.R == 1 ? pages_per_wave<1>() : pages_per_wave<2>());
   const dim3 grid(unsigned((bt.max_blocks + per_wg - 1) / per_wg), unsigned(bt.B));
   const dim3 block(kIdxWaves * kWave);
   switch (bt.R) {
