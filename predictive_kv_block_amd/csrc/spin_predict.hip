@@ -46,11 +46,9 @@ __device__ __forceinline__ bool request_ok(const SpinView& v, const spin_batch& 
 // grid (ceil(max_blocks / (W * kScoreBlocksPerWave)), B, R), W waves: wave w
 // of workgroup x scores the kScoreBlocksPerWave consecutive blocks from
 // (x*W + w) * kScoreBlocksPerWave, in batches of kScoreBatch with the next
-// batch's loads in flight while the current one is reduced.  Lane l reads
-// D_{q - i} of slot i = 64 j + l (every batch issues the same loads; blocks
-// past the last full one read D_0 and are masked), and lanes 0..15 read VB of
-// the batch's blocks.  The partial block holding q (if any) is scored apart
-// from V and D directly.
+// batch's loads in flight while the current one is reduced.  Every batch
+// issues the same loads (blocks past the last full one are masked).  The
+// partial block holding q (if any) is scored apart from V and D directly.
 __global__ void __launch_bounds__(kScoreWaves * kWave)
 k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int b = blockIdx.y, r = blockIdx.z;
@@ -75,28 +73,44 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int l = lane_id();
   const int nfull = (q + 1) / kBlock;          // blocks wholly at or before q
 
-  float dbuf[2][kScoreBatch];
-  float vbuf[2];
+  // Group g of a batch is blocks jb + 4g .. jb + 4g + 3, whose D windows are the
+  // 256 consecutive offsets from q - 64 (jb + 4g) - 255: lane l loads 4 of them
+  // (16 bytes, 4-byte aligned), so 16-lane row k holds block jb + 4g + 3 - k.
+  // Rows of blocks that are not full may reach below offset 0; those lanes
+  // read offset 0 instead and their row is never stored.
+  constexpr int kGroups = kScoreBatch / 4;
+  float4 dbuf[2][kGroups];
+  float vbuf[2][kGroups];
+  const int row_k = l >> 4;
   auto issue = [&](int u, int t) {
     const int jb = jw + t * kScoreBatch;
 #pragma unroll
-    for (int m = 0; m < kScoreBatch; ++m) {
-      const int j = jb + m;
-      dbuf[u][m] = D[j < nfull ? q - (j * kBlock + l) : 0];
+    for (int gq = 0; gq < kGroups; ++gq) {
+      const int o = q - kBlock * (jb + 4 * gq) - (4 * kBlock - 1) + 4 * l;
+      __builtin_memcpy(&dbuf[u][gq], D + (o > 0 ? o : 0), sizeof(float4));
+      const int j = jb + 4 * gq + 3 - row_k;
+      vbuf[u][gq] = VB[j < nfull ? j : 0];
     }
-    const int jl = jb + (l % kScoreBatch);
-    vbuf[u] = VB[jl < nfull ? jl : 0];
   };
   auto reduce = [&](int u, int t) {
     const int jb = jw + t * kScoreBatch;
-    float mine = -INFINITY;                    // lane m < kScoreBatch keeps S of block jb + m
 #pragma unroll
-    for (int m = 0; m < kScoreBatch; ++m) {
-      const float dm = wave_max(dbuf[u][m]);
-      if (l == m) mine = dm;
+    for (int gq = 0; gq < kGroups; ++gq) {
+      const float4 x = dbuf[u][gq];
+      float m = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+      // max over the 16-lane row: row shifts 1, 2, 4, 8 (lanes shifted in from
+      // outside the row contribute -inf); lane 16k + 15 ends with the row's max
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                       __float_as_int(-INFINITY), __float_as_int(m), 0x111, 0xF, 0xF, false)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                       __float_as_int(-INFINITY), __float_as_int(m), 0x112, 0xF, 0xF, false)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                       __float_as_int(-INFINITY), __float_as_int(m), 0x114, 0xF, 0xF, false)));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(
+                       __float_as_int(-INFINITY), __float_as_int(m), 0x118, 0xF, 0xF, false)));
+      const int j = jb + 4 * gq + 3 - row_k;
+      if ((l & 15) == 15 && j < nfull) out[j] = fmaxf(m, vbuf[u][gq]);
     }
-    mine = fmaxf(mine, vbuf[u]);
-    if (l < kScoreBatch && jb + l < nfull) out[jb + l] = mine;
   };
   issue(0, 0);
 #pragma unroll
