@@ -229,16 +229,22 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
       uint32_t thr;
       int neq;
       radix_threshold<kSelectThreads, 4, uint32_t>(src, n, pcount, &thr, &neq, s_scr);
-      ordered_emit<kSelectThreads, 2, uint32_t>(
-          src, n, thr, neq, [&](int j, int) { s_flags[j] |= 5; }, s_scr);
+      if (neq == 0x7fffffff)
+        mark_at_least<kSelectThreads, 4, uint32_t>(src, n, thr, [&](int j) { s_flags[j] |= 5; });
+      else
+        ordered_emit<kSelectThreads, 2, uint32_t>(
+            src, n, thr, neq, [&](int j, int) { s_flags[j] |= 5; }, s_scr);
     }
     if (nexp > 0) {
       ExploreSrc src{u, s_flags};
       uint64_t thr;
       int neq;
       radix_threshold<kSelectThreads, 4, uint64_t>(src, n, nexp, &thr, &neq, s_scr);
-      ordered_emit<kSelectThreads, 2, uint64_t>(
-          src, n, thr, neq, [&](int j, int) { s_flags[j] |= 2; }, s_scr);
+      if (neq == 0x7fffffff)
+        mark_at_least<kSelectThreads, 4, uint64_t>(src, n, thr, [&](int j) { s_flags[j] |= 2; });
+      else
+        ordered_emit<kSelectThreads, 2, uint64_t>(
+            src, n, thr, neq, [&](int j, int) { s_flags[j] |= 2; }, s_scr);
     }
     __syncthreads();
   }

@@ -5,100 +5,35 @@
 // valid candidates with the largest keys, ties going to the lower index.  It is
 // described by a threshold key T and a count n_eq: j is selected iff it is
 // valid and (key > T, or key == T and fewer than n_eq valid candidates below j
-// have key T).  T is found by MSB-first radix passes over 8-bit digits (below
-// the prefix all valid keys share) with LDS histograms; the ordered pass then
-// walks each wave's contiguous segment with ballots, so selected candidates
-// come out in ascending index order.
+// have key T).  T is found by MSB-first radix passes over 8-bit digits with an
+// LDS histogram; the ordered pass then walks each wave's contiguous segment
+// with ballots, so selected candidates come out in ascending index order (or,
+// without a partial tie at T, a plain marking pass takes every key >= T).
 #pragma once
 
 #include "spin_device.h"
 
 namespace spin {
 
-// LDS scratch needed by the helpers below (ints): kSelHistCopies histograms,
-// broadcast words, per-wave counts and prefixes.
-constexpr int kSelHistCopies = 4;
-constexpr int kSelHist = 256 * kSelHistCopies;
+// LDS scratch needed by the helpers below (ints): histogram, broadcast words,
+// per-wave counts and prefixes.
+constexpr int kSelHist = 256;
 constexpr int kSelectScratchInts = kSelHist + 8 + 4 * 32;
 
-// Smallest and largest key over the valid candidates (all threads get them;
-// kmin > kmax when none is valid).
-template <int NT, int U, typename K, typename Src>
-__device__ void key_range(const Src& src, int n, K* kmin, K* kmax, int* s_scratch) {
-  constexpr int NW = NT / kWave;
-  K* s_lo = reinterpret_cast<K*>(s_scratch);            // uses the histogram area
-  K* s_hi = s_lo + NW;
-  const int tid = threadIdx.x;
-  K lo = ~K(0), hi = K(0);
-  for (int base = 0; base < n; base += NT * U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * NT + tid;
-      K key;
-      if (j < n && src.get(j, key)) {
-        lo = key < lo ? key : lo;
-        hi = key > hi ? key : hi;
-      }
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const K a = K(__shfl_xor(lo, o, kWave)), b = K(__shfl_xor(hi, o, kWave));
-    lo = a < lo ? a : lo;
-    hi = b > hi ? b : hi;
-  }
-  __syncthreads();
-  if (lane_id() == 0) {
-    s_lo[tid / kWave] = lo;
-    s_hi[tid / kWave] = hi;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    lo = s_lo[i] < lo ? s_lo[i] : lo;
-    hi = s_hi[i] > hi ? s_hi[i] : hi;
-  }
-  __syncthreads();
-  *kmin = lo;
-  *kmax = hi;
-}
-
-// Threshold of the `want` largest valid keys (0 < want <= number valid).
-// Radix windows of 8 bits; for 32-bit keys they start just below the bits
-// that every valid key shares (the common prefix of kmin and kmax), so
-// clustered keys waste no round.  Each wave adds into one of kSelHistCopies
-// histograms.
+// Threshold of the `want` largest valid keys (0 < want <= number valid), by
+// MSB-first rounds of 8-bit digits; the search stops early when the whole
+// threshold bucket is taken.
 template <int NT, int U, typename K, typename Src>
 __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int* neq_out,
                                 int* s_scratch) {
   static_assert(NT % kWave == 0, "whole waves");
-  constexpr int KB = int(sizeof(K)) * 8;
   int* s_hist = s_scratch;
   int* s_bc = s_scratch + kSelHist;
   const int tid = threadIdx.x;
-  // 32-bit keys (scores) cluster and share leading bits: start below them.
-  // 64-bit keys (uniform random words) do not: start at the top.
-  int hb = KB - 1;                         // highest bit where kmin and kmax differ
-  K kmin = 0;
-  if (sizeof(K) == 4) {
-    K kmax;
-    key_range<NT, U, K>(src, n, &kmin, &kmax, s_scratch);
-    if (kmin >= kmax) {                    // one distinct key: the lowest-index `want`
-      *thr_out = kmin;
-      *neq_out = want;
-      return;
-    }
-    while (!(((kmin ^ kmax) >> hb) & K(1))) --hb;
-  }
-  K mask = (hb == KB - 1) ? K(0) : ~((K(2) << hb) - K(1));
-  K prefix = kmin & mask;
+  K prefix = 0, mask = 0;
   int remaining = want;
   bool done = false;
-  int* my_hist = s_hist + 256 * ((tid / kWave) % kSelHistCopies);
-  for (int top = hb; top >= 0 && !done;) {
-    const int width = top + 1 < 8 ? top + 1 : 8;
-    const int shift = top + 1 - width;
-    const K dmask = K((1u << width) - 1u);
+  for (int shift = int(sizeof(K)) * 8 - 8; shift >= 0 && !done; shift -= 8) {
     for (int i = tid; i < kSelHist; i += NT) s_hist[i] = 0;
     __syncthreads();
     for (int base = 0; base < n; base += NT * U) {
@@ -111,7 +46,7 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        hist_add(my_hist, int((key[u] >> shift) & dmask), ok[u] && (key[u] & mask) == prefix);
+        hist_add(s_hist, int(key[u] >> shift) & 255, ok[u] && (key[u] & mask) == prefix);
     }
     __syncthreads();
     if (tid < kWave) {
@@ -121,14 +56,9 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
         s_bc[1] = 0;
         s_bc[2] = 0;
       }
-      int c[4], tot = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        c[b] = 0;
-#pragma unroll
-        for (int h = 0; h < kSelHistCopies; ++h) c[b] += s_hist[256 * h + 4 * l + b];
-        tot += c[b];
-      }
+      const int c0 = s_hist[4 * l], c1 = s_hist[4 * l + 1], c2 = s_hist[4 * l + 2],
+                c3 = s_hist[4 * l + 3];
+      const int tot = c0 + c1 + c2 + c3;
       int sfx = tot;  // inclusive suffix sum over lanes l..63
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -138,6 +68,7 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
       const int above = sfx - tot;
       if (above < remaining && remaining <= sfx) {
         int cum = above, digit = 4 * l, at = above;
+        const int c[4] = {c0, c1, c2, c3};
         for (int b = 3; b >= 0; --b) {
           if (cum + c[b] >= remaining) {
             digit = 4 * l + b;
@@ -156,10 +87,9 @@ __device__ void radix_threshold(const Src& src, int n, int want, K* thr_out, int
     const int at = s_bc[1];
     const int bucket = s_bc[2];
     prefix |= K(digit) << shift;
-    mask |= dmask << shift;
+    mask |= K(255) << shift;
     remaining -= at;
     done = bucket == remaining;        // the whole bucket is taken: stop early
-    top = shift - 1;
     __syncthreads();
   }
   // With an early stop, thr is the bucket's lowest key and every key of the
@@ -245,6 +175,21 @@ __device__ int ordered_emit(const Src& src, int n, K thr, int n_eq, const Emit& 
   }
   __syncthreads();
   return total;
+}
+
+// Calls mark(j) for every selected j when the selection has no partial tie
+// at the threshold (n_eq unbounded: every valid key >= thr), in any order.
+template <int NT, int U, typename K, typename Src, typename Mark>
+__device__ void mark_at_least(const Src& src, int n, K thr, const Mark& mark) {
+  for (int base = 0; base < n; base += NT * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * NT + threadIdx.x;
+      K key;
+      if (j < n && src.get(j, key) && key >= thr) mark(j);
+    }
+  }
+  __syncthreads();
 }
 
 // Count of valid candidates (all threads get the total).
