@@ -40,7 +40,17 @@ and RNG unstated.  The readings taken here (each marked READING below) are:
   * exploration draws: Philox4x64-10 (Salmon et al., SC'11) with
     key = (seed, layer), counter = (j div 4, step, request_id, 0), word j mod 4;
     the n_exp non-predicted blocks with the smallest words are explored;
-  * the first decode step of a (layer, request) is all-keep (warm-up).
+  * the first decode step of a (layer, request) is all-keep (warm-up);
+  * block pooling variants (v1, Figure 3 caption, "Mean and Top-4 compared
+    with Max pooling"): mean = the average of z over the block's existing
+    slots whose z is finite (never-observed slots carry no score), top-4 = the
+    average of the 4 largest such z (fewer if the block has fewer); a block
+    with no finite z scores -inf under every pooling;
+  * row-0 mask policy (v1 Table 7 and Figure 2, "row-0" vs "row-local union"):
+    the mask built for row 0 serves every row; the blocks past row 0's last
+    block, which only the later rows reach (they hold the draft positions),
+    are kept as predicted.  The row-0 update policy is the replay with
+    accepted = 0 (only row 0's scores update the EMAs).
 
 Every floating-point step runs in fp64 on the exact values of the inputs
 (fp8 codes decoded exactly, bf16/fp32 widened exactly).
@@ -188,13 +198,31 @@ def slot_scores(V, D, qpos):
     return np.maximum(V[i], D[qpos - i])
 
 
-def block_scores(V, D, qpos):
-    """S_j = max of z over the existing slots of block j  [radio]."""
+POOL_MAX, POOL_MEAN, POOL_TOP4 = "max", "mean", "top4"
+
+
+def block_scores(V, D, qpos, pooling=POOL_MAX):
+    """S_j = max of z over the existing slots of block j  [radio]; or, as the
+    v1 Figure 3 variants (READING above), the mean of the finite z, or the mean
+    of the 4 largest finite z."""
     z = slot_scores(V, D, qpos)
     n = num_blocks(qpos)
     padded = np.full(n * BLOCK, NEG_INF)
     padded[: qpos + 1] = z
-    return padded.reshape(n, BLOCK).max(axis=1) + 0.0     # -0 -> +0
+    blocks = padded.reshape(n, BLOCK)
+    if pooling == POOL_MAX:
+        return blocks.max(axis=1) + 0.0     # -0 -> +0
+    out = np.full(n, NEG_INF)
+    for j in range(n):
+        fin = blocks[j][np.isfinite(blocks[j])]
+        if len(fin) == 0:
+            continue
+        if pooling == POOL_TOP4:
+            fin = np.sort(fin)[::-1][:4]
+        elif pooling != POOL_MEAN:
+            raise ValueError(pooling)
+        out[j] = fin.mean() + 0.0
+    return out
 
 
 def top_blocks(S, count):
@@ -210,7 +238,7 @@ def explored_blocks(pred_mask, n_exp, keys):
     return np.sort(np.array(cand[:n_exp], dtype=np.int64))
 
 
-def predict_row(V, D, qpos, keep_bp, explore_bp, keys, all_keep):
+def predict_row(V, D, qpos, keep_bp, explore_bp, keys, all_keep, pooling=POOL_MAX):
     """Masks of one query row: (predicted bool[N], explored bool[N])."""
     n = num_blocks(qpos)
     pred = np.zeros(n, dtype=bool)
@@ -219,30 +247,40 @@ def predict_row(V, D, qpos, keep_bp, explore_bp, keys, all_keep):
     if all_keep or keep_bp >= 10000 or k_b >= n:
         pred[:] = True
         return pred, expl
-    S = block_scores(V, D, qpos)
+    S = block_scores(V, D, qpos, pooling)
     pred[top_blocks(S, p)] = True
     expl[explored_blocks(pred, n_exp, keys)] = True
     return pred, expl
 
 
+MASK_UNION, MASK_ROW0 = "union", "row0"
+
+
 def predict_blocks(V, D, qpos, rows, keep_bp, explore_bp, seed, layer, step,
-                   request_id, warmup_steps=1):
+                   request_id, warmup_steps=1, pooling=POOL_MAX, mask=MASK_UNION):
     """One request's kept block list for a round of `rows` query rows.
 
     Row r has query position qpos + r and builds its own mask; the kept set is
     the union over rows [digest; v1 Table 7, row-local union].  Exploration
-    keys do not depend on the row.  Returns (kept ascending int64[], flags
-    uint8[N_last]) with flag 1 = predicted by some row, 2 = explored only.
+    keys do not depend on the row.  With mask = MASK_ROW0 only row 0 builds a
+    mask, and the blocks past row 0's last block are added as predicted
+    (READING above).  Returns (kept ascending int64[], flags uint8[N_last])
+    with flag 1 = predicted by some row, 2 = explored only.
     """
     n_last = num_blocks(qpos + rows - 1)
     all_keep = step < warmup_steps
     keys = explore_keys(n_last, seed, layer, step, request_id)
     pred_u = np.zeros(n_last, dtype=bool)
     expl_u = np.zeros(n_last, dtype=bool)
-    for r in range(rows):
-        pred, expl = predict_row(V, D, qpos + r, keep_bp, explore_bp, keys, all_keep)
+    mask_rows = 1 if mask == MASK_ROW0 else rows
+    if mask not in (MASK_UNION, MASK_ROW0):
+        raise ValueError(mask)
+    for r in range(mask_rows):
+        pred, expl = predict_row(V, D, qpos + r, keep_bp, explore_bp, keys, all_keep, pooling)
         pred_u[: len(pred)] |= pred
         expl_u[: len(expl)] |= expl
+    if mask == MASK_ROW0:
+        pred_u[num_blocks(qpos):] = True
     flags = np.where(pred_u, 1, np.where(expl_u, 2, 0)).astype(np.uint8)
     return np.nonzero(flags)[0].astype(np.int64), flags
 
@@ -403,7 +441,7 @@ class RequestState:
 
 def decode_round(state, qpos, rows, keep_bp, explore_bp, seed, layer,
                  qv, wv, key_values, page_scale, block_table, topk, alpha,
-                 accepted=0, warmup_steps=1):
+                 accepted=0, warmup_steps=1, pooling=POOL_MAX, mask=MASK_UNION):
     """predict -> index -> top-k -> update, the step order of [digest].
 
     Returns a dict with kept, flags, scores [R, kept*64], topk [R, K]; the
@@ -411,7 +449,7 @@ def decode_round(state, qpos, rows, keep_bp, explore_bp, seed, layer,
     """
     kept, flags = predict_blocks(state.V, state.D, qpos, rows, keep_bp, explore_bp,
                                  seed, layer, state.step, state.request_id,
-                                 warmup_steps)
+                                 warmup_steps, pooling, mask)
     scores = indexer_scores(qv, wv, key_values, page_scale, block_table, kept, qpos)
     tk = np.stack([topk_positions(scores[r], kept, qpos + r, topk) for r in range(rows)])
     ema_update(state.V, state.D, scores, kept, qpos, accepted, alpha)
