@@ -59,6 +59,26 @@ enum {
 };
 
 /* [host] Static configuration of one state buffer. */
+/* Predictor variants of the v1 listing (Figure 3 caption: Mean and Top-4
+ * against Max block pooling; Table 7 and Figure 2: row-0 mask against the
+ * row-local union), in spin_config.policy.  Max pooling and the union are the
+ * method; the others serve ablations.
+ *   SPIN_POOL_MAX   S_j = max of z over the block's existing slots
+ *   SPIN_POOL_MEAN  S_j = mean of the block's finite z (never-observed slots
+ *                   carry no score); -inf if none
+ *   SPIN_POOL_TOP4  S_j = mean of the block's 4 largest finite z (fewer if it
+ *                   has fewer); -inf if none
+ *   SPIN_MASK_ROW0  with R > 1, only row 0 builds a block mask, shared by
+ *                   every row; the blocks past row 0's last block (reached
+ *                   only by later rows) are kept as predicted.  The row-0
+ *                   EMA update is spin_update (or spin_mtp_replay with
+ *                   accepted = 0). */
+#define SPIN_POOL_MAX 0u
+#define SPIN_POOL_MEAN 1u
+#define SPIN_POOL_TOP4 2u
+#define SPIN_POOL_BITS 3u
+#define SPIN_MASK_ROW0 4u
+
 typedef struct spin_config {
   int32_t num_layers;   /* layers, each with its own V/D state */
   int32_t max_slots;    /* concurrent requests (state slots) */
@@ -71,7 +91,7 @@ typedef struct spin_config {
   int32_t warmup_steps; /* leading all-keep rounds of each (layer, request) */
   int32_t explore_bp;   /* exploration share of the kept budget, basis points */
   float alpha;          /* EMA history weight; beta = fp32(1 - alpha) */
-  uint32_t reserved;    /* must be 0 */
+  uint32_t policy;      /* SPIN_POOL_* | SPIN_MASK_ROW0; 0 = max pooling, row-local union */
   uint64_t seed;        /* Philox key word 0 for exploration */
 } spin_config;
 

@@ -37,7 +37,7 @@ class SpinConfig(ctypes.Structure):
         ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("topk", ctypes.c_int32),
         ("max_rows", ctypes.c_int32), ("warmup_steps", ctypes.c_int32),
         ("explore_bp", ctypes.c_int32), ("alpha", ctypes.c_float),
-        ("reserved", ctypes.c_uint32), ("seed", ctypes.c_uint64),
+        ("policy", ctypes.c_uint32), ("seed", ctypes.c_uint64),
     ]
 
 
@@ -123,10 +123,14 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+SPIN_POOL_MAX, SPIN_POOL_MEAN, SPIN_POOL_TOP4, SPIN_MASK_ROW0 = 0, 1, 2, 4
+
+
 def make_config(num_layers, max_slots, max_ctx, topk, max_rows=1, heads=64, head_dim=128,
-                warmup_steps=1, explore_bp=500, alpha=0.9, seed=0x5350494E):
+                warmup_steps=1, explore_bp=500, alpha=0.9, seed=0x5350494E, policy=0):
+    """policy: SPIN_POOL_MAX / SPIN_POOL_MEAN / SPIN_POOL_TOP4, optionally | SPIN_MASK_ROW0."""
     return SpinConfig(num_layers, max_slots, max_ctx, 64, heads, head_dim, topk, max_rows,
-                      warmup_steps, explore_bp, alpha, 0, seed)
+                      warmup_steps, explore_bp, alpha, int(policy), seed)
 
 
 def make_batch(slot, qpos, R, max_blocks):

@@ -17,7 +17,8 @@ int check_config(const spin_config* c) {
   if (!c) return SPIN_EINVAL;
   if (c->num_layers < 1 || c->max_slots < 1 || c->max_ctx < 1 || c->max_rows < 1 ||
       c->heads < 1 || c->head_dim < 1 || c->topk < 1 || c->warmup_steps < 0 ||
-      c->explore_bp < 0 || c->explore_bp > 10000 || c->reserved != 0 ||
+      c->explore_bp < 0 || c->explore_bp > 10000 || (c->policy & ~(SPIN_POOL_BITS | SPIN_MASK_ROW0)) != 0 ||
+      (c->policy & SPIN_POOL_BITS) == SPIN_POOL_BITS ||
       !(c->alpha >= 0.0f && c->alpha <= 1.0f))
     return SPIN_EINVAL;
   if (c->block_size != 64 || c->max_rows > 4 || c->topk > 4096 || c->topk % 4 != 0 ||
@@ -137,6 +138,8 @@ int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes, hipSt
   v.topk = cfg->topk;
   v.warmup = cfg->warmup_steps;
   v.explore_bp = cfg->explore_bp;
+  v.pooling = int(cfg->policy & SPIN_POOL_BITS);
+  v.mask_row0 = (cfg->policy & SPIN_MASK_ROW0) ? 1 : 0;
   v.alpha = cfg->alpha;
   v.seed = cfg->seed;
   const int hr = hip_status(spin::launch_fill_state(v, stream));

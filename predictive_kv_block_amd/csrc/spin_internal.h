@@ -19,9 +19,11 @@ struct SpinView {
   float* bscore;     // [S][max_rows][max_blocks]
   uint64_t* ukey;    // [S][max_blocks]
   float* pqmax;      // [S][max_rows][max_blocks][4] per-page quarter maxima of the last indexer call
-  void* topk_ws;     // top-k level buffers for max_slots * max_rows rows
+  void* topk_ws;     // unused (the state's top-k runs on the quarter maxima)
   size_t topk_ws_bytes;
   int L, S, max_ctx, max_blocks, H, d, max_rows, topk, warmup, explore_bp;
+  int pooling;       // SPIN_POOL_MAX / _MEAN / _TOP4
+  int mask_row0;     // 1: row 0's block mask serves every row
   float alpha;
   uint64_t seed;
 };

@@ -130,6 +130,73 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   }
 }
 
+// Sum over the wave (DPP, as wave_max).
+__device__ __forceinline__ float wave_sum_f(float v) {
+  int x = __float_as_int(v);
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp<kDppXor1, 0xF>(x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp<kDppXor2, 0xF>(x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp<kDppRowHalfMirror, 0xF>(x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp<kDppRowMirror, 0xF>(x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp<kDppRowBcast15, 0xA>(x)));
+  x = __float_as_int(__int_as_float(x) + __int_as_float(dpp<kDppRowBcast31, 0xC>(x)));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
+constexpr int kPoolBlocksPerWave = 16;
+
+// Mean / Top-4 block pooling (the ablation variants): z per slot from V and D
+// directly, one wave per block, lane t = slot 64 j + t; fp32 sums.
+// grid (ceil(max_blocks / (W * kPoolBlocksPerWave)), B, rows), W waves.
+template <int POOL>
+__global__ void __launch_bounds__(kScoreWaves * kWave)
+k_block_scores_pool(SpinView v, int layer, spin_batch bt, int keep_bp) {
+  const int b = blockIdx.y, r = blockIdx.z;
+  const int s = bt.slot[b];
+  const int q0 = bt.qpos[b];
+  if (!request_ok(v, bt, s, q0)) return;
+  const size_t row = size_t(layer) * v.S + s;
+  if (v.step[row] < v.warmup || keep_bp >= 10000) return;
+  const int q = q0 + r;
+  const int n = num_blocks_of(q);
+  int kb, nexp;
+  budget(keep_bp, n, v.explore_bp, &kb, &nexp);
+  if (kb >= n) return;
+  const float* V = v.V + row * v.max_ctx;
+  const float* D = v.D + row * v.max_ctx;
+  float* out = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
+  const int l = lane_id();
+  const int jw = (blockIdx.x * kScoreWaves + threadIdx.x / kWave) * kPoolBlocksPerWave;
+  for (int m = 0; m < kPoolBlocksPerWave; ++m) {
+    const int j = jw + m;
+    if (j >= n) break;
+    const int i = j * kBlock + l;
+    const float z = (i <= q) ? fmaxf(V[i], D[q - i]) : -INFINITY;
+    const bool fin = z > -INFINITY;
+    float sj;
+    if (POOL == int(SPIN_POOL_MEAN)) {
+      const int c = wave_sum(fin ? 1 : 0);
+      const float sum = wave_sum_f(fin ? z : 0.0f);
+      sj = c > 0 ? sum / float(c) : -INFINITY;
+    } else {
+      // the 4 largest: take the maximum, retire the lowest lane holding it
+      float x = z, sum = 0.0f;
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float t = wave_max(x);
+        if (t > -INFINITY) {
+          sum += t;
+          ++c;
+        }
+        const uint64_t at = __ballot(x == t);
+        if (l == __ffsll(static_cast<unsigned long long>(at)) - 1) x = -INFINITY;
+      }
+      sj = c > 0 ? sum / float(c) : -INFINITY;
+    }
+    if (l == 0) out[j] = sj + 0.0f;            // -0 -> +0
+  }
+}
+
 struct BlockScoreSrc {
   const float* S;
   __device__ bool get(int j, uint32_t& key) const {
@@ -206,7 +273,8 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
   }
   __syncthreads();
 
-  for (int r = 0; r < bt.R; ++r) {
+  const int mask_rows = v.mask_row0 ? 1 : bt.R;
+  for (int r = 0; r < mask_rows; ++r) {
     const int q = q0 + r;
     const int n = num_blocks_of(q);
     int kb, nexp;
@@ -249,6 +317,9 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
     __syncthreads();
   }
 
+  if (v.mask_row0)      // blocks only the later rows reach (the draft positions)
+    for (int j = num_blocks_of(q0) + tid; j < n_last; j += kSelectThreads) s_flags[j] |= 1;
+  __syncthreads();
   for (int j = tid; j < bt.max_blocks; j += kSelectThreads) {
     uint8_t f = 0;
     if (j < n_last) f = (s_flags[j] & 1) ? 1 : ((s_flags[j] & 2) ? 2 : 0);
@@ -270,9 +341,22 @@ hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, in
                           int32_t* kept, int32_t* kept_count, uint8_t* flags, hipStream_t s) {
   const int per_wg = kScoreWaves * kScoreBlocksPerWave;
   const unsigned chunks = unsigned((bt.max_blocks + per_wg - 1) / per_wg);
-  if (keep_bp < 10000)
-    hipLaunchKernelGGL(k_block_scores, dim3(chunks, bt.B, bt.R), dim3(kScoreWaves * kWave), 0, s,
-                       v, layer, bt, keep_bp);
+  const unsigned rows = v.mask_row0 ? 1u : unsigned(bt.R);
+  if (keep_bp < 10000) {
+    if (v.pooling == int(SPIN_POOL_MAX)) {
+      hipLaunchKernelGGL(k_block_scores, dim3(chunks, bt.B, rows), dim3(kScoreWaves * kWave), 0,
+                         s, v, layer, bt, keep_bp);
+    } else {
+      const int per = kScoreWaves * kPoolBlocksPerWave;
+      const dim3 grid(unsigned((bt.max_blocks + per - 1) / per), bt.B, rows);
+      if (v.pooling == int(SPIN_POOL_MEAN))
+        hipLaunchKernelGGL(k_block_scores_pool<int(SPIN_POOL_MEAN)>, grid,
+                           dim3(kScoreWaves * kWave), 0, s, v, layer, bt, keep_bp);
+      else
+        hipLaunchKernelGGL(k_block_scores_pool<int(SPIN_POOL_TOP4)>, grid,
+                           dim3(kScoreWaves * kWave), 0, s, v, layer, bt, keep_bp);
+    }
+  }
   const size_t resident_lds = size_t(bt.max_blocks) * 13;
   // Opt in to dynamic LDS beyond 64 KB for the resident variant (once).
   static const hipError_t lds_opt_in = hipFuncSetAttribute(
