@@ -75,6 +75,10 @@ def _args():
     ap.add_argument("--cpu-requests", type=int, default=160)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--fidelity", choices=("ablation", "budgets"), default=None,
+                    help="selection-fidelity run instead of the timing: MTP mask/update "
+                         "policies over target sparsities, or per-layer budgets")
+    ap.add_argument("--fid-targets", default=",".join(str(t) for t in FID_TARGETS))
     return ap.parse_args()
 
 
@@ -291,6 +295,198 @@ def _cpu_baseline(wl, keep_bp, n_req):
             "s_per_request_round": elapsed / n_req}
 
 
+# ------------------------------------------------------------ selection fidelity
+# Mean / p99 miss over eligible rows (v1, Table 5 caption) for the MTP policies
+# of v1 Figure 2 and Table 7, and the per-layer budgets of the v3 abstract.
+# Every round of every layer runs a shadow all-keep indexer + top-k beside the
+# sparse round; spin_measure_miss compares that top-k with the round's block
+# flags.  All R verification rows of a round count as decode rows.
+
+FID_TARGETS = (2000, 3000, 4000, 5000)
+FID_POLICIES = (("union", "prefix"), ("union", "row0"), ("row0", "prefix"), ("row0", "row0"))
+
+
+def _fidelity_inputs(wl, device):
+    """Per-layer pools, acceptances, positions and every round's queries."""
+    from workload import acceptances, make_pool, make_queries, positions
+
+    pools = [make_pool(wl, l, device=device) for l in range(wl.layers)]
+    acc = acceptances(wl)
+    qpos = positions(wl, acc)
+    qs = [[make_queries(wl, pools[l], l, t, qpos[t].tolist(), device=device)
+           for t in range(wl.steps)] for l in range(wl.layers)]
+    return pools, acc, qpos, qs
+
+
+def _fidelity_trace(wl, inputs, device, mask, update, keep_of, rounds=None):
+    """Run `rounds` MTP rounds over every layer under one policy.
+
+    mask: "union" (row-local union) or "row0" (row 0's mask for every row);
+    update: "prefix" (prefix-valid replay) or "row0" (row 0's scores only).
+    keep_of(t, layer, miss_so_far) -> keep_bp of that layer in round t, where
+    miss_so_far is the float32 [t, L, B, R] miss of the earlier rounds.
+    Returns miss [T, L, B, R], kept block counts [T, L, B] and the keep_bp
+    used [T, L].
+    """
+    import numpy as np
+    import torch
+
+    import predictive_kv_block_amd as spin
+
+    pools, acc, qpos_all, qs = inputs
+    T = rounds or wl.steps
+    L, B, R, nb, K = wl.layers, wl.batch, wl.rows, wl.blocks, wl.topk
+    policy = spin.SPIN_MASK_ROW0 if mask == "row0" else 0
+    cfg = spin.make_config(L, B, wl.ctx, K, max_rows=R, explore_bp=wl.explore_bp,
+                           alpha=wl.alpha, policy=policy)
+    st = spin.SpinState(cfg, device=device)
+    slot = torch.arange(B, dtype=torch.int32, device=device)
+    spin.spin_reset_slots(st.handle, slot, torch.arange(B, dtype=torch.int64, device=device) + 1000)
+    qpos = torch.zeros(B, dtype=torch.int32, device=device)
+    batch = spin.make_batch(slot, qpos, R, nb)
+    i32 = dict(dtype=torch.int32, device=device)
+    kept, cnt = torch.zeros(B, nb, **i32), torch.zeros(B, **i32)
+    flags = torch.zeros(B, nb, dtype=torch.uint8, device=device)
+    scores = torch.empty(B, R, nb * 64, dtype=torch.float32, device=device)
+    pq = torch.empty(B, R, nb, 4, dtype=torch.float32, device=device)
+    kept_all = torch.arange(nb, **i32)[None, :].repeat(B, 1).contiguous()
+    cnt_all = torch.zeros(B, **i32)
+    scores_all = torch.empty_like(scores)
+    pq_all = torch.empty_like(pq)
+    topk_all = torch.empty(B, R, K, **i32)
+    miss_dev = torch.zeros(L, B, R, dtype=torch.float32, device=device)
+    cnt_dev = torch.zeros(L, B, **i32)
+    acc_dev = acc.to(torch.int32).to(device)
+    miss = np.zeros((T, L, B, R), dtype=np.float32)
+    kept_n = np.zeros((T, L, B), dtype=np.int64)
+    keeps = np.zeros((T, L), dtype=np.int64)
+    for t in range(T):
+        qpos.copy_(qpos_all[t].to(torch.int32))
+        cnt_all.copy_((qpos + (R - 1)) // 64 + 1)
+        for l in range(L):
+            keep = int(keep_of(t, l, miss[:t]))
+            keeps[t, l] = keep
+            q, w = qs[l][t]
+            pool = pools[l]
+            spin.spin_predict_blocks(st.handle, l, batch, keep, kept, cnt, flags)
+            spin.spin_quantize_q(st.handle, batch, q, w)
+            spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale,
+                                     pool.block_table, kept_all, cnt_all, scores_all, pq_all)
+            spin.spin_topk_scores(batch, K, scores_all, kept_all, cnt_all, topk_all, None, pq_all)
+            spin.spin_measure_miss(batch, K, topk_all, flags, miss_dev[l])
+            spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale,
+                                     pool.block_table, kept, cnt, scores, pq)
+            if update == "prefix":
+                spin.spin_mtp_replay(st.handle, l, batch, acc_dev[t], scores, kept, cnt)
+            else:
+                spin.spin_update(st.handle, l, batch, scores, kept, cnt)
+            cnt_dev[l].copy_(cnt)
+        miss[t] = miss_dev.cpu().numpy()
+        kept_n[t] = cnt_dev.cpu().numpy()
+    if st.error() != 0:
+        raise RuntimeError(f"device error word {st.error()}")
+    return miss, kept_n, keeps
+
+
+def _fidelity_summary(miss, kept_n, keeps, qpos, rows, warmup, first_round=0):
+    """Mean and p99 miss over eligible rows, and the realized block sparsity.
+
+    A row (round t, layer l, request b, row r) is eligible when the round is
+    past warm-up (t >= warmup) and sparse for that row (its kept budget
+    ceil(keep * n / 10000) is below its block count n).  p99 is taken per
+    (layer, request) over that trace's eligible rows (linear interpolation),
+    then averaged, as in the pages' per-layer, per-trace p99; `p99_pooled` is
+    the p99 of all eligible rows together.  Realized sparsity = 1 - kept
+    blocks / blocks up to the round's last row, over the eligible rounds.
+    """
+    import numpy as np
+
+    miss = np.asarray(miss, dtype=np.float64)
+    T, L, B, R = miss.shape
+    qpos = np.asarray(qpos[:T], dtype=np.int64)                    # [T, B]
+    n_row = (qpos[:, :, None] + np.arange(R)[None, None, :]) // 64 + 1   # [T, B, R]
+    kb = (keeps[:, :, None, None] * n_row[:, None, :, :] + 9999) // 10000  # [T, L, B, R]
+    t_ok = (np.arange(T) >= max(warmup, first_round))[:, None, None, None]
+    elig = t_ok & (kb < n_row[:, None, :, :])
+    per_trace = []
+    per_layer = []
+    for l in range(L):
+        lm = []
+        for b in range(B):
+            x = miss[:, l, b, :][elig[:, l, b, :]]
+            if len(x):
+                per_trace.append(np.percentile(x, 99))
+                lm.append(x)
+        xl = np.concatenate(lm) if lm else np.zeros(0)
+        per_layer.append({"mean_miss": float(xl.mean()) if len(xl) else None,
+                          "p99_miss": float(np.mean([np.percentile(x, 99) for x in lm]))
+                          if lm else None})
+    allx = miss[elig]
+    rt = np.arange(T) >= max(warmup, first_round)
+    n_last = n_row[:, :, R - 1]                                     # [T, B]
+    tot = float(n_last[rt].sum()) * L
+    return {"eligible_rows": int(elig.sum()),
+            "mean_miss": float(allx.mean()) if len(allx) else None,
+            "p99_miss": float(np.mean(per_trace)) if per_trace else None,
+            "p99_pooled": float(np.percentile(allx, 99)) if len(allx) else None,
+            "realized_sparsity": 1.0 - float(kept_n[rt].sum()) / tot if tot else None,
+            "per_layer": per_layer}
+
+
+def _fidelity(mode, wl, device, targets):
+    import numpy as np
+
+    import predictive_kv_block_amd as spin
+
+    spin.load()
+    t0 = time.perf_counter()
+    inputs = _fidelity_inputs(wl, device)
+    qpos = inputs[2].numpy()
+    print(f"[fidelity] {wl.name}: inputs drawn in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    warm = 1                                   # the config's warm-up rounds
+    out = []
+    if mode == "ablation":
+        for tgt in targets:
+            for mask, upd in FID_POLICIES:
+                miss, kept_n, keeps = _fidelity_trace(wl, inputs, device, mask, upd,
+                                                      lambda t, l, m, k=10000 - tgt: k)
+                s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm)
+                rec = {"fidelity": "mtp_policy", "workload": wl.name, "target_sparsity_bp": tgt,
+                       "mask": mask, "update": upd, **s}
+                print(json.dumps(rec), flush=True)
+                out.append(rec)
+        return out
+    # per-layer budgets: W calibration rounds at the uniform mean keep, then
+    # spin_allocate_budgets from the per-layer mean miss of those rounds
+    W = 8
+    mean_keep = 10000 - targets[-1]
+    uni = _fidelity_trace(wl, inputs, device, "union", "prefix", lambda t, l, m: mean_keep)
+    plan = {}
+
+    def keep_of(t, l, m):
+        if t < W:
+            return mean_keep
+        if "keep" not in plan:
+            s = _fidelity_summary(m, np.ones((t, wl.layers, wl.batch)), np.full((t, wl.layers),
+                                  mean_keep), qpos, wl.rows, warm)
+            plan["calib_miss"] = [p["mean_miss"] for p in s["per_layer"]]
+            plan["keep"] = spin.spin_allocate_budgets(plan["calib_miss"], mean_keep)
+        return plan["keep"][l]
+
+    cal = _fidelity_trace(wl, inputs, device, "union", "prefix", keep_of)
+    for name, (miss, kept_n, keeps) in (("uniform", uni), ("per_layer", cal)):
+        s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm, first_round=W)
+        rec = {"fidelity": "layer_budgets", "workload": wl.name, "mean_keep_bp": mean_keep,
+               "calibration_rounds": W, "budgets": name,
+               "keep_bp": [int(k) for k in keeps[-1]], **s}
+        if name == "per_layer":
+            rec["calibration_mean_miss"] = plan["calib_miss"]
+        print(json.dumps(rec), flush=True)
+        out.append(rec)
+    return out
+
+
 def _copy_calibration(device):
     import torch
     n = 1 << 30
@@ -317,6 +513,9 @@ def main():
     global QUANTIZE_ON_SIDE, SPACER_CYCLES
     QUANTIZE_ON_SIDE = not a.quantize_on_main
     SPACER_CYCLES = a.spacer_cycles
+    if a.fidelity:
+        _fidelity(a.fidelity, wl, device, [int(x) for x in a.fid_targets.split(",")])
+        return
     keep_main = 10000 - a.sparsity_bp
     sweep = [10000 - int(s) for s in a.sweep.split(",") if s.strip() != ""]
     keeps = [keep_main] + [k for k in sweep if k != keep_main]
