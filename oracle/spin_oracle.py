@@ -46,6 +46,12 @@ and RNG unstated.  The readings taken here (each marked READING below) are:
     slots whose z is finite (never-observed slots carry no score), top-4 = the
     average of the 4 largest such z (fewer if the block has fewer); a block
     with no finite z scores -inf under every pooling;
+  * predictor quality (v1 Table 1): Pearson correlation over the slots where
+    prediction and indexer score are both finite; top-k recall = shared
+    slots of the two top-k sets over the indexer's top-k size;
+  * online miss estimate: the explored blocks are a uniform sample of the
+    non-predicted ones, so their share of top-k hits, scaled by skipped /
+    explored, estimates the miss (estimate_miss);
   * row-0 mask policy (v1 Table 7 and Figure 2, "row-0" vs "row-local union"):
     the mask built for row 0 serves every row; the blocks past row 0's last
     block, which only the later rows reach (they hold the draft positions),
@@ -382,6 +388,73 @@ def miss_rate(full_topk, flags):
     flags = np.asarray(flags)
     skipped = np.array([blk_j >= len(flags) or flags[blk_j] == 0 for blk_j in blk])
     return float(skipped.sum()) / len(full)
+
+
+def estimate_miss(sparse_topk, flags, qpos_r, k):
+    """Online estimate of one row's miss from its exploration hits, with no
+    all-keep indexer.
+
+    READING (the miss of the v1 Table 5 caption; the exploration share of
+    the digest and the radio summary, a random sample inside the budget): the
+    explored blocks E (flag 2) are a uniform sample without replacement of the
+    blocks U not predicted (flag != 1) among the row's N_r blocks, and
+    S = U minus E (flag 0) are skipped.  If h of the all-keep top-k slots lie
+    in E, h * |U| / |E| estimates how many lie in U, so h * |S| / (|E| * k_r)
+    estimates the share in S, k_r = min(k, qpos_r + 1) being the size of the
+    all-keep top-k.  h is counted on the sparse round's own top-k: every
+    all-keep top-k slot in a kept block is in it, so this h is never smaller.
+    Clamped to 1; 0 when nothing is skipped; -1 (no estimate) when blocks are
+    skipped but none explored.  fp64, returned rounded to fp32.
+    """
+    n = num_blocks(qpos_r)
+    f = np.asarray(flags)[:n]
+    n_skip = int((f == 0).sum())
+    n_expl = int((f == 2).sum())
+    if n_skip == 0:
+        return 0.0
+    if n_expl == 0:
+        return -1.0
+    t = np.asarray(sparse_topk, dtype=np.int64)
+    t = t[(t >= 0) & (t <= qpos_r)]
+    h = int((f[t // BLOCK] == 2).sum())
+    k_r = min(k, qpos_r + 1)
+    return float(np.float32(min(1.0, h * n_skip / (n_expl * k_r))))
+
+
+def pearson(pred, actual):
+    """Pearson correlation of a predictor's slot scores with the indexer's.
+
+    READING of v1 Table 1 ("Pearson correlation" of predicted and actual
+    indexer scores): over the slots where both are finite (a slot never
+    observed has no prediction); 0 when fewer than 2 such slots remain or
+    either side is constant on them.
+    """
+    x = np.asarray(pred, dtype=np.float64)
+    y = np.asarray(actual, dtype=np.float64)
+    m = np.isfinite(x) & np.isfinite(y)
+    x, y = x[m], y[m]
+    if len(x) < 2 or np.all(x == x[0]) or np.all(y == y[0]):
+        return 0.0
+    return float(np.corrcoef(x, y)[0, 1])
+
+
+def topk_recall(pred, actual, k):
+    """Top-k recall of a slot predictor (v1 Table 1): the share of the
+    indexer's top-k slots that are also in the predictor's top-k.
+
+    Both sets are taken by topk_positions over slots 0..len-1 (ties to the
+    lower slot; a -inf prediction ranks last); the share is of the
+    min(k, len) actual top-k slots.
+    """
+    n = len(actual)
+    nb = (n + BLOCK - 1) // BLOCK
+    allb = np.arange(nb)
+    pad = lambda v: np.concatenate([np.asarray(v, dtype=np.float64),
+                                    np.full(nb * BLOCK - n, NEG_INF)])
+    tp = topk_positions(pad(pred), allb, n - 1, k)
+    ta = topk_positions(pad(actual), allb, n - 1, k)
+    tp, ta = tp[tp >= 0], ta[ta >= 0]
+    return len(np.intersect1d(tp, ta)) / len(ta) if len(ta) else 0.0
 
 
 def allocate_budgets(miss, mean_keep_bp, eps=1e-3):
