@@ -34,15 +34,28 @@ IDX_SCORE_BYTES_PER_PAGE_ROW = 64 * 4 + 16      # scores + the page's quarter ma
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_indexer_ctx512k-b96_hbm_traffic.md")
 INDEXER_BUILD_FILES = ["predictive_kv_block_amd/csrc/spin_indexer.hip",
                        "predictive_kv_block_amd/csrc/spin_device.h",
-                       "predictive_kv_block_amd/csrc/spin_internal.h",
-                       "predictive_kv_block_amd/build.py"]
+                       "predictive_kv_block_amd/csrc/spin_internal.h"]
+
+
+def indexer_build_digest():
+    """SHA-256 over what the indexer kernel is compiled from: its source, the
+    headers it includes from the package, and the compiler flags."""
+    import hashlib
+
+    from predictive_kv_block_amd.build import FLAGS
+
+    h = hashlib.sha256()
+    for f in INDEXER_BUILD_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    h.update(" ".join(a for a in FLAGS if not a.startswith("/")).encode())
+    return h.hexdigest()
 
 
 def _measured_traffic(workload, sparsity_bp):
     """HBM bytes per indexer launch from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary, or None when that summary is for another workload or
     the indexer has been rebuilt from different sources since."""
-    import hashlib
     import re
 
     if workload != "ctx512k-b96" or sparsity_bp != 5000 or not os.path.exists(TRAFFIC_FILE):
@@ -52,11 +65,7 @@ def _measured_traffic(workload, sparsity_bp):
     d = re.search(r"^indexer_build_sha256 = ([0-9a-f]{64})$", text, re.M)
     if not t or not d:
         return None
-    h = hashlib.sha256()
-    for f in INDEXER_BUILD_FILES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return int(t.group(1)) if h.hexdigest() == d.group(1) else None
+    return int(t.group(1)) if indexer_build_digest() == d.group(1) else None
 
 
 def _args():
