@@ -11,6 +11,11 @@
  *     spin_update          -> EMA update from the observed slots (R == 1)
  *     spin_mtp_replay      -> prefix-valid EMA replay once acceptance is known
  *
+ * Measurement calls beside the round: spin_measure_miss (against an all-keep
+ * top-k), spin_estimate_miss (from exploration hits alone), spin_slot_scores
+ * and spin_predictor_fidelity (a slot predictor against the indexer), and the
+ * host allocator spin_allocate_budgets.
+ *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked [host].
  *   - Every call that takes a hipStream_t enqueues its kernels on that stream
@@ -270,6 +275,44 @@ int spin_mtp_replay(spin_state* st, int layer, const spin_batch* batch, const in
  * [B][R][topk]; block_flags: uint8 [B][max_blocks]; miss: fp32 [B][R]. */
 int spin_measure_miss(const spin_batch* batch, int topk, const int32_t* full_topk,
                       const uint8_t* block_flags, float* miss, hipStream_t stream);
+
+/* Predicted slot scores z_i = max(V_i, D_{q+r-i}) of every row (AI Radio
+ * episode, "Title and authors"), the values that block pooling reduces, for
+ * measuring a predictor against the indexer.  z_out: fp32
+ * [B][R][batch->max_blocks * 64]; entries past q + r are -inf, never-observed
+ * slots are -inf.  Requests with a bad slot or position are left untouched
+ * and flagged in the state's error word. */
+int spin_slot_scores(spin_state* st, int layer, const spin_batch* batch, float* z_out,
+                     hipStream_t stream);
+
+/* Online miss estimate from exploration hits, with no all-keep indexer (the
+ * miss of the v1 Table 5 caption; the random exploration share of the ai4snews
+ * digest, "arXiv深度剖析").  The explored blocks (flag 2) are a uniform sample
+ * of the blocks not predicted (flag != 1), so for row r with N_r blocks:
+ *     est[b][r] = min(1, hits * skipped / (explored * min(topk, q + r + 1)))
+ * where hits = entries of this round's (sparse) top-k topk_out[b][r][:] in
+ * explored blocks, skipped / explored = blocks < N_r with flag 0 / 2.  The
+ * ratio is taken in fp64 and rounded to fp32.  0 when nothing is skipped;
+ * -1 when blocks are skipped but none explored; NaN for a request whose qpos
+ * is negative or whose last row needs more than max_blocks blocks.
+ * topk_out: int32 [B][R][topk] (entries < 0 or past q + r are ignored);
+ * block_flags: uint8 [B][max_blocks]; est: fp32 [B][R].  batch->slot is not
+ * read. */
+int spin_estimate_miss(const spin_batch* batch, int topk, const int32_t* topk_out,
+                       const uint8_t* block_flags, float* est, hipStream_t stream);
+
+/* Quality of a slot predictor against the indexer (v1, Table 1: Pearson
+ * correlation and top-k recall).  pred, actual: fp32
+ * [B][R][batch->max_blocks * 64] slot scores; pred_topk, actual_topk: int32
+ * [B][R][topk], ascending with -1 padding (as spin_topk_scores writes them).
+ * out: fp64 [B][R][2] = (Pearson over the slots 0..q+r where both scores are
+ * finite, computed in fp64 from the means; 0 when fewer than 2 such slots
+ * remain or either side is constant on them;  recall = entries of pred_topk
+ * found in actual_topk / valid entries of actual_topk, 0 if none).  NaN for a
+ * request whose qpos is out of range.  batch->slot is not read. */
+int spin_predictor_fidelity(const spin_batch* batch, int topk, const float* pred,
+                            const float* actual, const int32_t* pred_topk,
+                            const int32_t* actual_topk, double* out, hipStream_t stream);
 
 /* [host] Per-layer keep budgets from measured miss rates (v3 abstract: the
  * block budget is allocated across layers by their measured miss rates).

@@ -14,7 +14,7 @@ __all__ = [
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
-    "EXPORTS",
+    "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so")
@@ -24,6 +24,7 @@ EXPORTS = [
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
+    "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
 ]
 
 SPIN_OK, SPIN_EINVAL, SPIN_EUNSUPPORTED, SPIN_EHIP, SPIN_ESTATE = 0, -1, -2, -3, -4
@@ -83,6 +84,9 @@ _SIGS = {
     "spin_allocate_budgets": [_i32, ctypes.POINTER(ctypes.c_double), _i32,
                               ctypes.POINTER(ctypes.c_int32)],
     "spin_status_string": [_i32],
+    "spin_slot_scores": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp],
+    "spin_estimate_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
+    "spin_predictor_fidelity": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp],
 }
 
 
@@ -226,6 +230,22 @@ def spin_mtp_replay(h, layer, batch, accepted, scores, kept_blocks, kept_count, 
 def spin_measure_miss(batch, topk, full_topk, block_flags, miss, stream=None):
     _check(load().spin_measure_miss(ctypes.byref(batch), int(topk), _p(full_topk),
                                     _p(block_flags), _p(miss), _stream(stream)))
+
+
+def spin_slot_scores(handle, layer, batch, z_out, stream=None):
+    _check(load().spin_slot_scores(handle, int(layer), ctypes.byref(batch), _p(z_out),
+                                   _stream(stream)))
+
+
+def spin_estimate_miss(batch, topk, topk_out, block_flags, est, stream=None):
+    _check(load().spin_estimate_miss(ctypes.byref(batch), int(topk), _p(topk_out),
+                                     _p(block_flags), _p(est), _stream(stream)))
+
+
+def spin_predictor_fidelity(batch, topk, pred, actual, pred_topk, actual_topk, out, stream=None):
+    _check(load().spin_predictor_fidelity(ctypes.byref(batch), int(topk), _p(pred), _p(actual),
+                                          _p(pred_topk), _p(actual_topk), _p(out),
+                                          _stream(stream)))
 
 
 def spin_allocate_budgets(miss, mean_keep_bp):

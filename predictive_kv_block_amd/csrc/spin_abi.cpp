@@ -5,6 +5,7 @@
 
 #include <new>
 
+#include "spin_fidelity.h"
 #include "spin_internal.h"
 
 namespace {
@@ -276,6 +277,33 @@ int spin_measure_miss(const spin_batch* batch, int topk, const int32_t* full_top
       topk < 1 || topk > 65536 || !full_topk || !block_flags || !miss)
     return SPIN_EINVAL;
   return hip_status(spin::launch_miss(*batch, topk, full_topk, block_flags, miss, stream));
+}
+
+int spin_slot_scores(spin_state* st, int layer, const spin_batch* batch, float* z_out,
+                     hipStream_t stream) {
+  int rc = check_batch(st, batch);
+  if (rc) return rc;
+  if (layer < 0 || layer >= st->cfg.num_layers || !z_out) return SPIN_EINVAL;
+  return hip_status(spin::launch_slot_scores(st->view, layer, *batch, z_out, stream));
+}
+
+int spin_estimate_miss(const spin_batch* batch, int topk, const int32_t* topk_out,
+                       const uint8_t* block_flags, float* est, hipStream_t stream) {
+  int rc = check_plain_batch(batch);
+  if (rc) return rc;
+  if (topk < 1 || topk > 65536 || !topk_out || !block_flags || !est) return SPIN_EINVAL;
+  return hip_status(spin::launch_estimate_miss(*batch, topk, topk_out, block_flags, est, stream));
+}
+
+int spin_predictor_fidelity(const spin_batch* batch, int topk, const float* pred,
+                            const float* actual, const int32_t* pred_topk,
+                            const int32_t* actual_topk, double* out, hipStream_t stream) {
+  int rc = check_plain_batch(batch);
+  if (rc) return rc;
+  if (topk < 1 || topk > 65536 || !pred || !actual || !pred_topk || !actual_topk || !out)
+    return SPIN_EINVAL;
+  return hip_status(spin::launch_predictor_fidelity(*batch, topk, pred, actual, pred_topk,
+                                                    actual_topk, out, stream));
 }
 
 int spin_allocate_budgets(int L, const double* miss, int mean_keep_bp, int32_t* keep_bp_out) {
