@@ -50,8 +50,10 @@ and RNG unstated.  The readings taken here (each marked READING below) are:
     prediction and indexer score are both finite; top-k recall = shared
     slots of the two top-k sets over the indexer's top-k size;
   * online miss estimate: the explored blocks are a uniform sample of the
-    non-predicted ones, so their share of top-k hits, scaled by skipped /
-    explored, estimates the miss (estimate_miss);
+    non-predicted ones; weighting each explored slot by the inverse sampling
+    rate places the all-keep top-k threshold inside the sparse round's own
+    top-k, and the explored slots above it, scaled by skipped / explored,
+    estimate the miss (estimate_miss);
   * row-0 mask policy (v1 Table 7 and Figure 2, "row-0" vs "row-local union"):
     the mask built for row 0 serves every row; the blocks past row 0's last
     block, which only the later rows reach (they hold the draft positions),
@@ -390,35 +392,63 @@ def miss_rate(full_topk, flags):
     return float(skipped.sum()) / len(full)
 
 
-def estimate_miss(sparse_topk, flags, qpos_r, k):
-    """Online estimate of one row's miss from its exploration hits, with no
-    all-keep indexer.
+def estimate_miss(sparse_topk, topk_scores, flags, qpos_r, k):
+    """Online estimate of one row's miss from its exploration blocks, with no
+    all-keep indexer.  Returns (estimate, upper bound).
 
     READING (the miss of the v1 Table 5 caption; the exploration share of
     the digest and the radio summary, a random sample inside the budget): the
     explored blocks E (flag 2) are a uniform sample without replacement of the
     blocks U not predicted (flag != 1) among the row's N_r blocks, and
-    S = U minus E (flag 0) are skipped.  If h of the all-keep top-k slots lie
-    in E, h * |U| / |E| estimates how many lie in U, so h * |S| / (|E| * k_r)
-    estimates the share in S, k_r = min(k, qpos_r + 1) being the size of the
-    all-keep top-k.  h is counted on the sparse round's own top-k: every
-    all-keep top-k slot in a kept block is in it, so this h is never smaller.
-    Clamped to 1; 0 when nothing is skipped; -1 (no estimate) when blocks are
-    skipped but none explored.  fp64, returned rounded to fp32.
+    S = U minus E (flag 0) are skipped; k_r = min(k, qpos_r + 1) is the size
+    of the all-keep top-k.
+
+    estimate: each slot of E stands for |U| / |E| slots of U, so the all-keep
+    top-k threshold is placed where the sparse round's own top-k, walked from
+    the highest score down (ties to the lower position) with weight 1 per
+    predicted slot and |U| / |E| per explored slot, first reaches k_r.  That
+    threshold is never below the sparse top-k's own, so the walk ends inside
+    it (or takes all of it when it is not full).  With c_E explored slots
+    passed on the way, c_E * |S| / (|E| * k_r) estimates the share of the
+    all-keep top-k in S.  Integer weights (|E| and |U|, target k_r * |E|)
+    make the walk exact.
+
+    upper bound: h * |S| / (|E| * k_r) with h all explored slots of the
+    sparse top-k; every all-keep top-k slot in a kept block is in it, and
+    when top slots are missed lower ones take their places, so h >= c_E.
+
+    Both clamped to 1; (0, 0) when nothing is skipped; (-1, -1) when blocks
+    are skipped but none explored.  Ratios in fp64, rounded to fp32.
     """
     n = num_blocks(qpos_r)
     f = np.asarray(flags)[:n]
     n_skip = int((f == 0).sum())
     n_expl = int((f == 2).sum())
+    n_u = n_skip + n_expl
     if n_skip == 0:
-        return 0.0
+        return 0.0, 0.0
     if n_expl == 0:
-        return -1.0
+        return -1.0, -1.0
     t = np.asarray(sparse_topk, dtype=np.int64)
-    t = t[(t >= 0) & (t <= qpos_r)]
-    h = int((f[t // BLOCK] == 2).sum())
+    sc = np.asarray(topk_scores, dtype=np.float64)
+    ok = (t >= 0) & (t <= qpos_r)
+    t, sc = t[ok], sc[ok]
+    blk = t // BLOCK
+    keep = f[blk] != 0                   # the top-k of a sparse round holds kept slots only
+    t, sc, blk = t[keep], sc[keep], blk[keep]
+    is_e = f[blk] == 2
     k_r = min(k, qpos_r + 1)
-    return float(np.float32(min(1.0, h * n_skip / (n_expl * k_r))))
+    order = np.lexsort((t, -(sc + 0.0)))   # score descending, then lower position
+    c_e = 0
+    acc = 0
+    for idx in order:
+        acc += n_u if is_e[idx] else n_expl
+        c_e += int(is_e[idx])
+        if acc >= k_r * n_expl:
+            break
+    h = int(is_e.sum())
+    ratio = lambda c: float(np.float32(min(1.0, c * n_skip / (n_expl * k_r))))
+    return ratio(c_e), ratio(h)
 
 
 def pearson(pred, actual):

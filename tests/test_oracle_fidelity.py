@@ -2,9 +2,11 @@
 estimate (exploration hits scaled by skipped / explored blocks), Pearson
 correlation and top-k recall of slot predictors (v1 Table 1).
 
-The miss estimate is checked by brute force over every exploration draw of
-tiny cases (its mean over all equally likely draws must equal the true miss
-exactly); Pearson and recall against hand-computed values, closed forms and
+The hit ratio is checked by brute force over every exploration draw of tiny
+cases (its mean over all equally likely draws must equal the true miss); the
+weighted-threshold estimate against blocks whose skipped twins repeat the
+explored scores (where it must equal the true miss exactly) and hand-walked
+cases; Pearson and recall against hand-computed values, closed forms and
 exhaustive averages over all predictor rankings."""
 import itertools
 import math
@@ -27,61 +29,103 @@ def _case(n_blocks, k, seed):
     return q, scores, full
 
 
+def _scores_of(scores, top):
+    return np.array([scores[p] if p >= 0 else 0.0 for p in top])
+
+
 @pytest.mark.parametrize("n_blocks,pred,n_exp,k,seed", [
     (6, [0, 3], 2, 40, 1), (7, [1], 3, 100, 2), (8, [0, 2, 5], 1, 64, 3), (5, [], 2, 200, 4)])
-def test_estimate_is_unbiased_over_all_draws(n_blocks, pred, n_exp, k, seed):
+def test_hit_ratio_is_unbiased_over_all_draws(n_blocks, pred, n_exp, k, seed):
+    """The upper-bound ratio, fed the all-keep top-k itself, is the plain
+    ratio estimator: its mean over every equally likely exploration draw is
+    the mean true miss.  Fed the sparse round's own top-k it can only grow,
+    and the weighted-threshold estimate never exceeds it."""
     q, scores, full = _case(n_blocks, k, seed)
     U = [j for j in range(n_blocks) if j not in pred]
     total = Fraction(0)
-    draws = 0
+    trues = []
     for E in itertools.combinations(U, n_exp):
         flags = np.zeros(n_blocks, dtype=np.uint8)
         flags[pred] = 1
         flags[list(E)] = 2
-        true_miss = O.miss_rate(full, flags)
-        # with h counted on the all-keep top-k itself the estimate is the
-        # plain ratio estimator; no clamp is reached in these cases
-        est = O.estimate_miss(full, flags, q, k)
-        assert 0.0 <= est < 1.0
-        total += Fraction(est)
-        draws += 1
-        # the sparse round's own top-k can only count more hits
+        trues.append(O.miss_rate(full, flags))
+        _, ub = O.estimate_miss(full, _scores_of(scores, full), flags, q, k)
+        assert 0.0 <= ub < 1.0                        # no clamp in these cases
+        total += Fraction(ub)
         kept = np.nonzero(flags)[0]
         row = scores[(kept[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)]
         sparse = O.topk_positions(row, kept, q, k)
-        assert O.estimate_miss(sparse, flags, q, k) >= est
-    flags = np.zeros(n_blocks, dtype=np.uint8)
-    flags[pred] = 1
-    true_u = float(np.isin(full // 64, U).sum()) / k            # miss with E empty
-    # E[h] = (n_exp / |U|) * (top-k slots in U); E[est] = E[h] (|U| - n_exp) / (n_exp k)
-    want = true_u * (len(U) - n_exp) / len(U)
-    assert math.isclose(float(total / draws), want, rel_tol=1e-6, abs_tol=1e-7)
-    # and that is the mean true miss over the draws as well
-    mean_true = np.mean([O.miss_rate(full, np.where(np.isin(np.arange(n_blocks), E), 2,
-                                                    np.where(np.isin(np.arange(n_blocks), pred),
-                                                             1, 0)))
-                         for E in itertools.combinations(U, n_exp)])
-    assert math.isclose(float(total / draws), mean_true, rel_tol=1e-6, abs_tol=1e-7)
+        est, ub_sparse = O.estimate_miss(sparse, _scores_of(scores, sparse), flags, q, k)
+        assert ub_sparse >= ub and est <= ub_sparse
+        assert 0.0 <= est
+    draws = len(trues)
+    true_u = float(np.isin(full // 64, U).sum()) / k                # all of U skipped
+    assert math.isclose(float(total / draws), true_u * (len(U) - n_exp) / len(U),
+                        rel_tol=1e-6, abs_tol=1e-7)
+    assert math.isclose(float(total / draws), float(np.mean(trues)), rel_tol=1e-6, abs_tol=1e-7)
+
+
+@pytest.mark.parametrize("c_e_true", [0, 5, 30, 64])
+def test_threshold_estimate_exact_on_mirrored_blocks(c_e_true):
+    """Skipped blocks that repeat the explored blocks' scores exactly: the
+    explored sample is then a perfect picture of U, the weighted walk stops
+    exactly at the all-keep threshold, and the estimate is the true miss."""
+    rng = np.random.default_rng(c_e_true)
+    # blocks 0..2 predicted, 3..4 explored, 5..6 skipped twins of 3..4
+    vals_e = rng.permutation(np.arange(1000, 1128, dtype=np.float64))     # 128 explored slots
+    vals_p = rng.permutation(np.arange(0, 192, dtype=np.float64)) * 10.0 - 500.0
+    scores = np.concatenate([vals_p, vals_e, vals_e + 0.0])
+    q = 7 * 64 - 1
+    flags = np.array([1, 1, 1, 2, 2, 0, 0], dtype=np.uint8)
+    # k: the all-keep top-k takes the top c_e_true explored values, their twins,
+    # and the predicted slots above the next explored value
+    e_sorted = np.sort(vals_e)[::-1]
+    thr = e_sorted[c_e_true - 1] if c_e_true else 1e9
+    nxt = e_sorted[c_e_true] if c_e_true < 128 else -1e9
+    n_p = int(((vals_p > nxt) & (vals_p >= min(thr, 1e9))).sum()) if c_e_true else 0
+    k = n_p + 2 * c_e_true
+    if k == 0:
+        k = 1
+        n_p = 1
+    full = O.topk_positions(scores, np.arange(7), q, k)
+    true_miss = O.miss_rate(full, flags)
+    kept = np.array([0, 1, 2, 3, 4])
+    row = scores[(kept[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)]
+    sparse = O.topk_positions(row, kept, q, k)
+    est, ub = O.estimate_miss(sparse, _scores_of(scores, sparse), flags, q, k)
+    assert est == np.float32(true_miss)
+    assert ub >= est
 
 
 def test_estimate_special_cases():
     q, scores, full = _case(4, 64, 9)
+    sc = _scores_of(scores, full)
     all_kept = np.array([1, 2, 1, 1], dtype=np.uint8)
-    assert O.estimate_miss(full, all_kept, q, 64) == 0.0          # nothing skipped
+    assert O.estimate_miss(full, sc, all_kept, q, 64) == (0.0, 0.0)      # nothing skipped
     no_expl = np.array([1, 0, 1, 0], dtype=np.uint8)
-    assert O.estimate_miss(full, no_expl, q, 64) == -1.0          # no estimate
-    # one explored block holding the whole top-k, three skipped: clamps to 1
+    assert O.estimate_miss(full, sc, no_expl, q, 64) == (-1.0, -1.0)     # no estimate
+    # one explored block holding the whole top-k, three skipped: each explored
+    # slot stands for |U| / |E| = 4, so the walk stops after 16 of them:
+    # 16 * 3 / 64; the hit ratio 64 * 3 / 64 clamps to 1
     flags = np.array([2, 0, 0, 0], dtype=np.uint8)
     top = np.arange(64)
-    assert O.estimate_miss(top, flags, q, 64) == 1.0
-    # h = 16 of k = 64 in the one explored block, 2 skipped: 16 * 2 / (1 * 64)
+    assert O.estimate_miss(top, np.arange(64.0), flags, q, 64) == (0.75, 1.0)
+    # h = 16 of k = 64 in the one explored block (|U| = 3, |E| = 1), 2 skipped
     flags = np.array([1, 2, 0, 0], dtype=np.uint8)
     top = np.concatenate([np.arange(48), 64 + np.arange(16)])
-    assert O.estimate_miss(top, flags, q, 64) == 0.5
-    # positions past the row's query and -1 padding are not hits; k_r = q + 1
+    # the explored slots score highest: the walk passes c explored slots with
+    # weight 3 until 3c >= 64 -> c = 22 > 16, so it takes all 16 and stops
+    # inside the predicted ones: estimate = upper = 16 * 2 / (1 * 64)
+    sc = np.concatenate([np.zeros(48), 100.0 + np.arange(16)])
+    assert O.estimate_miss(top, sc, flags, q, 64) == (0.5, 0.5)
+    # the explored slots score lowest: the predicted 48 (weight 1) and then
+    # c explored (weight 3): 48 + 3c >= 64 -> c = 6: 6 * 2 / 64
+    sc = np.concatenate([100.0 + np.arange(48), np.zeros(16)])
+    assert O.estimate_miss(top, sc, flags, q, 64) == (np.float32(12 / 64), 0.5)
+    # positions past the row's query and -1 padding are ignored; k_r = q + 1
     q2 = 64 + 9
     flags = np.array([1, 2], dtype=np.uint8)
-    assert O.estimate_miss(np.array([64, 65, 200, -1]), flags, q2, 4096) == 0.0
+    assert O.estimate_miss(np.array([64, 65, 200, -1]), np.ones(4), flags, q2, 4096) == (0.0, 0.0)
 
 
 def test_pearson_values():
