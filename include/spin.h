@@ -285,21 +285,34 @@ int spin_measure_miss(const spin_batch* batch, int topk, const int32_t* full_top
 int spin_slot_scores(spin_state* st, int layer, const spin_batch* batch, float* z_out,
                      hipStream_t stream);
 
-/* Online miss estimate from exploration hits, with no all-keep indexer (the
- * miss of the v1 Table 5 caption; the random exploration share of the ai4snews
- * digest, "arXiv深度剖析").  The explored blocks (flag 2) are a uniform sample
- * of the blocks not predicted (flag != 1), so for row r with N_r blocks:
- *     est[b][r] = min(1, hits * skipped / (explored * min(topk, q + r + 1)))
- * where hits = entries of this round's (sparse) top-k topk_out[b][r][:] in
- * explored blocks, skipped / explored = blocks < N_r with flag 0 / 2.  The
- * ratio is taken in fp64 and rounded to fp32.  0 when nothing is skipped;
- * -1 when blocks are skipped but none explored; NaN for a request whose qpos
- * is negative or whose last row needs more than max_blocks blocks.
- * topk_out: int32 [B][R][topk] (entries < 0 or past q + r are ignored);
- * block_flags: uint8 [B][max_blocks]; est: fp32 [B][R].  batch->slot is not
- * read. */
-int spin_estimate_miss(const spin_batch* batch, int topk, const int32_t* topk_out,
-                       const uint8_t* block_flags, float* est, hipStream_t stream);
+/* Online miss estimate of every row from its exploration blocks, with no
+ * all-keep indexer (the miss of the v1 Table 5 caption; the random
+ * exploration share of the ai4snews digest, "arXiv深度剖析").  The explored
+ * blocks E (flag 2) are a uniform sample of the blocks U not predicted
+ * (flag != 1) among the row's N_r blocks; S (flag 0) are skipped;
+ * k_r = min(topk, q + r + 1).
+ *   est[b][r][0]: walk this round's top-k topk_out[b][r][:] from the highest
+ *     score down (ties to the lower position) with weight |E| per predicted
+ *     slot and |U| per explored slot (each explored slot stands for |U|/|E|
+ *     slots of U); the walk stops at the first entry whose running weight
+ *     reaches k_r * |E|, which places the all-keep top-k threshold; with c_E
+ *     explored entries up to there, est = c_E * |S| / (|E| * k_r).
+ *   est[b][r][1]: the same ratio with every explored entry of the top-k (an
+ *     upper bound: when top slots are skipped, lower ones fill their places).
+ * Both in fp64, clamped to 1, rounded to fp32.  (0, 0) when nothing is
+ * skipped; (-1, -1) when blocks are skipped but none explored; NaN for a
+ * request whose qpos is negative or whose last row needs more than
+ * max_blocks blocks.
+ * scores: fp32 [B][R][max_blocks * 64] in kept-list layout (as written by
+ * spin_indexer_scores for these kept lists); kept_blocks / kept_count: the
+ * round's ascending kept lists; topk_out: int32 [B][R][topk], topk <= 4096
+ * (entries < 0, past q + r, or in blocks outside the kept list are
+ * ignored); block_flags: uint8 [B][max_blocks]; est: fp32 [B][R][2].
+ * batch->slot is not read. */
+int spin_estimate_miss(const spin_batch* batch, int topk, const float* scores,
+                       const int32_t* kept_blocks, const int32_t* kept_count,
+                       const int32_t* topk_out, const uint8_t* block_flags, float* est,
+                       hipStream_t stream);
 
 /* Quality of a slot predictor against the indexer (v1, Table 1: Pearson
  * correlation and top-k recall).  pred, actual: fp32

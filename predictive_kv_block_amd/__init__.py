@@ -85,7 +85,7 @@ _SIGS = {
                               ctypes.POINTER(ctypes.c_int32)],
     "spin_status_string": [_i32],
     "spin_slot_scores": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp],
-    "spin_estimate_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
+    "spin_estimate_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "spin_predictor_fidelity": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp],
 }
 
@@ -237,9 +237,11 @@ def spin_slot_scores(handle, layer, batch, z_out, stream=None):
                                    _stream(stream)))
 
 
-def spin_estimate_miss(batch, topk, topk_out, block_flags, est, stream=None):
-    _check(load().spin_estimate_miss(ctypes.byref(batch), int(topk), _p(topk_out),
-                                     _p(block_flags), _p(est), _stream(stream)))
+def spin_estimate_miss(batch, topk, scores, kept_blocks, kept_count, topk_out, block_flags, est,
+                       stream=None):
+    _check(load().spin_estimate_miss(ctypes.byref(batch), int(topk), _p(scores), _p(kept_blocks),
+                                     _p(kept_count), _p(topk_out), _p(block_flags), _p(est),
+                                     _stream(stream)))
 
 
 def spin_predictor_fidelity(batch, topk, pred, actual, pred_topk, actual_topk, out, stream=None):

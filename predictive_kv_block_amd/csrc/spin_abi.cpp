@@ -287,12 +287,17 @@ int spin_slot_scores(spin_state* st, int layer, const spin_batch* batch, float* 
   return hip_status(spin::launch_slot_scores(st->view, layer, *batch, z_out, stream));
 }
 
-int spin_estimate_miss(const spin_batch* batch, int topk, const int32_t* topk_out,
-                       const uint8_t* block_flags, float* est, hipStream_t stream) {
+int spin_estimate_miss(const spin_batch* batch, int topk, const float* scores,
+                       const int32_t* kept_blocks, const int32_t* kept_count,
+                       const int32_t* topk_out, const uint8_t* block_flags, float* est,
+                       hipStream_t stream) {
   int rc = check_plain_batch(batch);
   if (rc) return rc;
-  if (topk < 1 || topk > 65536 || !topk_out || !block_flags || !est) return SPIN_EINVAL;
-  return hip_status(spin::launch_estimate_miss(*batch, topk, topk_out, block_flags, est, stream));
+  if (topk < 1 || topk > 4096 || !scores || !kept_blocks || !kept_count || !topk_out ||
+      !block_flags || !est)
+    return SPIN_EINVAL;
+  return hip_status(spin::launch_estimate_miss(*batch, topk, scores, kept_blocks, kept_count,
+                                               topk_out, block_flags, est, stream));
 }
 
 int spin_predictor_fidelity(const spin_batch* batch, int topk, const float* pred,

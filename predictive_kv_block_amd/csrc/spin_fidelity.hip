@@ -12,7 +12,7 @@ namespace {
 
 constexpr int kSlotThreads = 256;
 constexpr int kSlotsPerThread = 4;
-constexpr int kEstThreads = 256;
+constexpr int kEstThreads = 1024;
 constexpr int kFidThreads = 1024;
 
 // z_i = max(V_i, D_{q+r-i}) for i <= q + r, -inf for the rest of the row.
@@ -65,46 +65,157 @@ __device__ void block_sum3(int& a, int& b, int& c, int* s_buf) {
   }
 }
 
-// One workgroup per (request, row): skipped and explored blocks among the
-// row's N_r blocks, top-k slots in explored blocks, then
-// min(1, hits * skipped / (explored * k_r)) in fp64, rounded to fp32.
+// Inclusive prefix sum over the workgroup of one int per thread, in thread
+// order; s_buf holds NT / 64 ints.
+template <int NT>
+__device__ int block_inclusive_sum(int x, int* s_buf) {
+  const int l = lane_id(), w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(x, o, kWave);
+    if (l >= o) x += t;
+  }
+  if (l == kWave - 1) s_buf[w] = x;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += s_buf[i];
+  __syncthreads();
+  return x + before;
+}
+
+constexpr int kEstMaxK = 4096;
+constexpr int kEstPerThread = kEstMaxK / kEstThreads;
+
+// One workgroup per (request, row).  Skipped / explored blocks among the
+// row's N_r blocks; the sparse top-k's entries as 64-bit keys (score order,
+// then lower position first, then an explored bit), sorted descending in
+// LDS; the weighted walk (|E| per predicted slot, |U| per explored slot,
+// target k_r * |E|) stops at the first entry whose running weight reaches the
+// target, and the explored entries up to it give the estimate; all explored
+// entries give the upper bound.  Ratios in fp64, rounded to fp32.
 __global__ void __launch_bounds__(kEstThreads)
-k_estimate_miss(spin_batch bt, int K, const int32_t* topk, const uint8_t* flags, float* est) {
+k_estimate_miss(spin_batch bt, int K, const float* scores, const int32_t* kept,
+                const int32_t* kept_count, const int32_t* topk, const uint8_t* flags,
+                float* est) {
+  __shared__ uint64_t s_key[kEstMaxK];
   __shared__ int s_buf[3 * (kEstThreads / kWave)];
+  __shared__ int s_bc[4];
   const int row = blockIdx.x;
   const int b = row / bt.R, r = row - b * bt.R;
   const int q0 = bt.qpos[b];
+  const int tid = threadIdx.x;
   if (q0 < 0 || q0 > bt.max_blocks * kBlock - bt.R) {
-    if (threadIdx.x == 0) est[row] = __builtin_nanf("");
+    if (tid == 0) est[2 * size_t(row)] = est[2 * size_t(row) + 1] = __builtin_nanf("");
     return;
   }
   const int q = q0 + r;
   const int n = num_blocks_of(q);
   const uint8_t* f = flags + size_t(b) * bt.max_blocks;
+  const int32_t* kl = kept + size_t(b) * bt.max_blocks;
+  int cnt = kept_count[b];
+  cnt = cnt < 0 ? 0 : (cnt > bt.max_blocks ? bt.max_blocks : cnt);
+  const float* sc = scores + size_t(row) * bt.max_blocks * kBlock;
   const int32_t* t = topk + size_t(row) * K;
-  int skipped = 0, explored = 0, hits = 0;
-  for (int j = threadIdx.x; j < n; j += kEstThreads) {
+
+  int skipped = 0, explored = 0, unused = 0;
+  for (int j = tid; j < n; j += kEstThreads) {
     const uint8_t x = f[j];
     skipped += x == 0 ? 1 : 0;
     explored += x == 2 ? 1 : 0;
   }
-  for (int e = threadIdx.x; e < K; e += kEstThreads) {
-    const int p = t[e];
-    hits += (p >= 0 && p <= q && f[p / kBlock] == 2) ? 1 : 0;
+  block_sum3<kEstThreads>(skipped, explored, unused, s_buf);
+  if (tid == 0) {
+    s_bc[0] = skipped;
+    s_bc[1] = explored;
   }
-  block_sum3<kEstThreads>(skipped, explored, hits, s_buf);
-  if (threadIdx.x == 0) {
-    float out;
-    if (skipped == 0) {
-      out = 0.0f;
-    } else if (explored == 0) {
-      out = -1.0f;
-    } else {
-      const int k_r = min(K, q + 1);
-      const double x = (double(hits) * double(skipped)) / (double(explored) * double(k_r));
-      out = float(x < 1.0 ? x : 1.0);
+  __syncthreads();
+  skipped = s_bc[0];
+  explored = s_bc[1];
+  if (skipped == 0 || explored == 0) {
+    if (tid == 0) est[2 * size_t(row)] = est[2 * size_t(row) + 1] = skipped == 0 ? 0.0f : -1.0f;
+    return;
+  }
+
+  // keys of the valid entries (0 for the rest, which sort last)
+  int np2 = 1;
+  while (np2 < K) np2 <<= 1;
+  for (int e = tid; e < np2; e += kEstThreads) {
+    uint64_t key = 0;
+    const int p = e < K ? t[e] : -1;
+    if (p >= 0 && p <= q) {
+      const int blk = p / kBlock;
+      const uint8_t fl = f[blk];
+      int lo = 0, hi = cnt;                // first kept index with kl >= blk
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (kl[mid] < blk) lo = mid + 1; else hi = mid;
+      }
+      if (fl != 0 && lo < cnt && kl[lo] == blk) {
+        const float v = sc[size_t(lo) * kBlock + (p & (kBlock - 1))] + 0.0f;
+        key = (uint64_t(ord_key(v)) << 32) | (uint64_t(0x3FFFFF - p) << 1) | (fl == 2 ? 1u : 0u);
+      }
     }
-    est[row] = out;
+    s_key[e] = key;
+  }
+  __syncthreads();
+  // bitonic sort, descending
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int e = tid; e < np2 / 2; e += kEstThreads) {
+        const int lo = 2 * stride * (e / stride) + (e % stride);
+        const int hi = lo + stride;
+        const bool desc = ((lo & size) == 0);
+        const uint64_t a = s_key[lo], c = s_key[hi];
+        if ((a < c) == desc) {
+          s_key[lo] = c;
+          s_key[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // weighted walk: thread i owns sorted entries [i * PT, i * PT + PT)
+  const int n_u = skipped + explored;
+  const int k_r = min(K, q + 1);
+  const int target = k_r * explored;
+  int wsum = 0, esum = 0;
+  int wt[kEstPerThread];
+  bool ise[kEstPerThread];
+#pragma unroll
+  for (int u = 0; u < kEstPerThread; ++u) {
+    const int e = tid * kEstPerThread + u;
+    const uint64_t key = e < np2 ? s_key[e] : 0;
+    ise[u] = key != 0 && (key & 1u);
+    wt[u] = key == 0 ? 0 : (ise[u] ? n_u : explored);
+    wsum += wt[u];
+    esum += ise[u] ? 1 : 0;
+  }
+  if (tid == 0) s_bc[2] = 0x7fffffff;
+  const int incl = block_inclusive_sum<kEstThreads>(wsum, s_buf);
+  int run = incl - wsum;
+#pragma unroll
+  for (int u = 0; u < kEstPerThread; ++u) {
+    run += wt[u];
+    if (wt[u] != 0 && run >= target) {
+      atomicMin(&s_bc[2], tid * kEstPerThread + u);
+      break;
+    }
+  }
+  __syncthreads();
+  const int stop = s_bc[2];
+  int c_e = 0;
+#pragma unroll
+  for (int u = 0; u < kEstPerThread; ++u)
+    c_e += (ise[u] && tid * kEstPerThread + u <= stop) ? 1 : 0;
+  int h = esum, z = 0;
+  block_sum3<kEstThreads>(c_e, h, z, s_buf);
+  if (tid == 0) {
+    const double den = double(explored) * double(k_r);
+    const double a = double(c_e) * double(skipped) / den;
+    const double c = double(h) * double(skipped) / den;
+    est[2 * size_t(row)] = float(a < 1.0 ? a : 1.0);
+    est[2 * size_t(row) + 1] = float(c < 1.0 ? c : 1.0);
   }
 }
 
@@ -264,10 +375,13 @@ hipError_t launch_slot_scores(const SpinView& v, int layer, const spin_batch& bt
   return hipGetLastError();
 }
 
-hipError_t launch_estimate_miss(const spin_batch& bt, int topk, const int32_t* topk_out,
-                                const uint8_t* flags, float* est, hipStream_t s) {
+hipError_t launch_estimate_miss(const spin_batch& bt, int topk, const float* scores,
+                                const int32_t* kept, const int32_t* kept_count,
+                                const int32_t* topk_out, const uint8_t* flags, float* est,
+                                hipStream_t s) {
+  if (topk > kEstMaxK) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_estimate_miss, dim3(bt.B * bt.R), dim3(kEstThreads), 0, s, bt, topk,
-                     topk_out, flags, est);
+                     scores, kept, kept_count, topk_out, flags, est);
   return hipGetLastError();
 }
 

@@ -75,9 +75,12 @@ def test_null_and_range_arguments_rejected_before_any_launch():
     assert lib.spin_measure_miss(ctypes.byref(b), 0, None, None, None, None) == spin.SPIN_EINVAL
     p = ctypes.c_void_p(256)
     assert lib.spin_slot_scores(None, 0, ctypes.byref(big), p, None) == spin.SPIN_EINVAL
-    assert lib.spin_estimate_miss(ctypes.byref(big), 0, p, p, p, None) == spin.SPIN_EINVAL
-    assert lib.spin_estimate_miss(ctypes.byref(big), 2048, None, p, p, None) == spin.SPIN_EINVAL
-    assert lib.spin_estimate_miss(ctypes.byref(b), 64, p, p, p, None) == spin.SPIN_EINVAL  # no qpos
+    assert lib.spin_estimate_miss(ctypes.byref(big), 0, p, p, p, p, p, p, None) == spin.SPIN_EINVAL
+    assert lib.spin_estimate_miss(ctypes.byref(big), 8192, p, p, p, p, p, p,
+                                  None) == spin.SPIN_EINVAL
+    assert lib.spin_estimate_miss(ctypes.byref(big), 2048, p, p, None, p, p, p,
+                                  None) == spin.SPIN_EINVAL
+    assert lib.spin_estimate_miss(ctypes.byref(b), 64, p, p, p, p, p, p, None) == spin.SPIN_EINVAL
     assert lib.spin_predictor_fidelity(ctypes.byref(big), 2048, p, p, p, p, None,
                                        None) == spin.SPIN_EINVAL
     assert lib.spin_predictor_fidelity(ctypes.byref(big), 0, p, p, p, p, p, None) == spin.SPIN_EINVAL

@@ -1,8 +1,8 @@
 """GPU parity of the selection-fidelity calls against the oracle: the slot
-predictions z = max(V, D) (bit-exact), the online miss estimate from
-exploration hits (bit-exact: integer counts, one fp64 ratio rounded to fp32),
-and predictor quality (Pearson within 1e-10, top-k recall exact).  Inputs are
-drawn on the host; every expected value comes from the oracle."""
+predictions z = max(V, D) (bit-exact), the online miss estimate from the
+exploration blocks (bit-exact: an integer weighted walk, fp64 ratios rounded
+to fp32), and predictor quality (Pearson within 1e-10, top-k recall exact).
+Inputs are drawn on the host; every expected value comes from the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -50,59 +50,85 @@ def test_slot_scores_exact(gpu_lib, R, blocks):
     assert rig.state.error() == 0
 
 
-def _flags_and_topk(rng, B, R, mb, qpos, K, p_skip, p_expl, hit_bias):
+def _est_inputs(rng, B, R, mb, qpos, K, p_skip, p_expl, bias, grid):
+    """Flags, ascending kept lists, kept-layout scores and each row's sparse
+    top-k (taken by the oracle over the kept slots, then shuffled, with an
+    ignored entry past the row's position where there is room)."""
     flags = np.zeros((B, mb), dtype=np.uint8)
+    kept = np.full((B, mb), -1, dtype=np.int32)
+    cnt = np.zeros(B, dtype=np.int32)
+    scores = np.zeros((B, R, mb * 64), dtype=np.float32)
     topk = np.full((B, R, K), -1, dtype=np.int32)
     for b in range(B):
         n = nblocks(int(qpos[b]) + R - 1)
         u = rng.random(n)
         flags[b, :n] = np.where(u < p_skip, 0, np.where(u < p_skip + p_expl, 2, 1))
         flags[b, n:] = rng.integers(0, 3, mb - n)        # past the rows: never read
+        kl = np.nonzero(flags[b, :n])[0]
+        kept[b, : len(kl)] = kl
+        cnt[b] = len(kl)
+        boost = np.repeat(np.where(flags[b, kl] == 2, bias, 0.0), 64)
         for r in range(R):
             q = int(qpos[b]) + r
-            kept = np.nonzero(flags[b, : nblocks(q)])[0]
-            slots = (kept[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
-            slots = slots[slots <= q]
-            # favour explored blocks a little so the estimate is not ~0
-            w = np.where(flags[b, slots // 64] == 2, hit_bias, 1.0)
-            m = min(K - 3, len(slots))
-            pick = np.sort(rng.choice(slots, size=m, replace=False, p=w / w.sum())) if m else []
-            topk[b, r, :m] = pick
-            topk[b, r, m: m + 3] = [q + 1, q + 70, -1][: max(0, min(3, K - m))]   # ignored
-    return flags, topk
+            v = rng.normal(size=len(kl) * 64) + boost
+            if grid:
+                v = np.round(v * grid) / grid                      # many equal scores
+            scores[b, r, : len(v)] = v
+            t = O.topk_positions(scores[b, r, : len(v)].astype(np.float64), kl, q, K)
+            if (t < 0).any():
+                t[np.nonzero(t < 0)[0][0]] = q + 1                 # ignored: past the row
+            topk[b, r] = rng.permutation(t)
+    return flags, kept, cnt, scores, topk
 
 
-@pytest.mark.parametrize("R,mb,K,p_skip,p_expl,bias", [
-    (1, 200, 256, 0.5, 0.05, 3.0), (4, 200, 2048, 0.5, 0.1, 2.0), (2, 8192, 2048, 0.5, 0.05, 1.0),
-    (1, 64, 4096, 0.3, 0.2, 50.0),          # clamps at 1 for some rows
-    (2, 50, 256, 0.0, 0.1, 1.0),            # nothing skipped: 0
-    (2, 50, 256, 0.5, 0.0, 1.0)])           # nothing explored: -1
-def test_estimate_miss_exact(gpu_lib, R, mb, K, p_skip, p_expl, bias):
+def _score_at(scores_row, kl, p):
+    j = int(np.searchsorted(kl, p // 64))
+    return float(scores_row[j * 64 + p % 64])
+
+
+@pytest.mark.parametrize("R,mb,K,p_skip,p_expl,bias,grid", [
+    (1, 200, 256, 0.5, 0.05, 0.0, 0), (4, 200, 2048, 0.5, 0.1, 0.5, 4), (2, 8192, 2048, 0.5, 0.05, 0.0, 0),
+    (1, 64, 4096, 0.3, 0.2, 3.0, 0),        # explored slots on top: clamps for some rows
+    (3, 300, 1024, 0.6, 0.1, -1.0, 2),      # explored slots low, heavy ties
+    (2, 50, 256, 0.0, 0.1, 0.0, 0),         # nothing skipped: 0
+    (2, 50, 256, 0.5, 0.0, 0.0, 0)])        # nothing explored: -1
+def test_estimate_miss_exact(gpu_lib, R, mb, K, p_skip, p_expl, bias, grid):
     rng = np.random.default_rng(mb + K + R)
     B = 4
     qpos = np.array([64 * mb - R, 64 * (mb // 3) + 5, 63, 0], dtype=np.int64)
-    flags, topk = _flags_and_topk(rng, B, R, mb, qpos, K, p_skip, p_expl, bias)
+    flags, kept, cnt, scores, topk = _est_inputs(rng, B, R, mb, qpos, K, p_skip, p_expl, bias,
+                                                 grid)
     qd = torch.as_tensor(qpos.astype(np.int32), device=DEV)
     slot = torch.arange(B, dtype=torch.int32, device=DEV)
     bt = spin.make_batch(slot, qd, R, mb)
-    est = torch.full((B, R), 5.0, device=DEV)
-    _say("estimate miss", R, mb, K, p_skip, p_expl)
-    spin.spin_estimate_miss(bt, K, torch.as_tensor(topk, device=DEV),
-                            torch.as_tensor(flags, device=DEV), est)
+    est = torch.full((B, R, 2), 5.0, device=DEV)
+    _say("estimate miss", R, mb, K, p_skip, p_expl, bias, grid)
+    spin.spin_estimate_miss(bt, K, torch.as_tensor(scores, device=DEV),
+                            torch.as_tensor(kept, device=DEV), torch.as_tensor(cnt, device=DEV),
+                            torch.as_tensor(topk, device=DEV), torch.as_tensor(flags, device=DEV),
+                            est)
     torch.cuda.synchronize()
     got = np_(est)
     for b in range(B):
+        kl = kept[b, : cnt[b]].astype(np.int64)
         for r in range(R):
-            want = O.estimate_miss(topk[b, r], flags[b], int(qpos[b]) + r, K)
-            assert np.float32(want) == got[b, r], (b, r, want, got[b, r])
+            q = int(qpos[b]) + r
+            t = topk[b, r]
+            ts = [_score_at(scores[b, r], kl, int(p)) if 0 <= p <= q else 0.0 for p in t]
+            want = O.estimate_miss(t, ts, flags[b], q, K)
+            assert (np.float32(want[0]), np.float32(want[1])) == (got[b, r, 0], got[b, r, 1]), \
+                (b, r, want, got[b, r])
 
 
 def test_estimate_miss_bad_position_is_nan(gpu_lib):
     mb, R = 10, 2
     qd = torch.tensor([64 * mb - 1, -3], dtype=torch.int32, device=DEV)   # row 1 needs block 10
     bt = spin.make_batch(torch.zeros(2, dtype=torch.int32, device=DEV), qd, R, mb)
-    est = torch.zeros(2, R, device=DEV)
-    spin.spin_estimate_miss(bt, 64, torch.full((2, R, 64), -1, dtype=torch.int32, device=DEV),
+    est = torch.zeros(2, R, 2, device=DEV)
+    spin.spin_estimate_miss(bt, 64, torch.zeros(2, R, mb * 64, device=DEV),
+                            torch.zeros(2, mb, dtype=torch.int32, device=DEV),
+                            torch.zeros(2, dtype=torch.int32, device=DEV),
+                            torch.full((2, R, 64), -1, dtype=torch.int32, device=DEV),
                             torch.zeros(2, mb, dtype=torch.uint8, device=DEV), est)
     torch.cuda.synchronize()
     assert np.all(np.isnan(np_(est)))
