@@ -84,9 +84,10 @@ def _args():
     ap.add_argument("--cpu-requests", type=int, default=160)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
-    ap.add_argument("--fidelity", choices=("ablation", "budgets"), default=None,
+    ap.add_argument("--fidelity", choices=("ablation", "budgets", "predictors"), default=None,
                     help="selection-fidelity run instead of the timing: MTP mask/update "
-                         "policies over target sparsities, or per-layer budgets")
+                         "policies over target sparsities, per-layer budgets, or slot "
+                         "predictor quality (Pearson, top-k recall)")
     ap.add_argument("--fid-targets", default=",".join(str(t) for t in FID_TARGETS))
     return ap.parse_args()
 
@@ -332,10 +333,14 @@ def _fidelity_trace(wl, inputs, device, mask, update, keep_of, rounds=None):
 
     mask: "union" (row-local union) or "row0" (row 0's mask for every row);
     update: "prefix" (prefix-valid replay) or "row0" (row 0's scores only).
-    keep_of(t, layer, miss_so_far) -> keep_bp of that layer in round t, where
-    miss_so_far is the float32 [t, L, B, R] miss of the earlier rounds.
-    Returns miss [T, L, B, R], kept block counts [T, L, B] and the keep_bp
-    used [T, L].
+    keep_of(t, layer, miss_so_far, est_so_far) -> keep_bp of that layer in
+    round t, given the measured miss [t, L, B, R] and the online estimates
+    [t, L, B, R, 2] of the earlier rounds.
+    Returns miss [T, L, B, R], kept block counts [T, L, B], the keep_bp used
+    [T, L], and the online estimates [T, L, B, R, 2] of each row's miss from
+    its exploration blocks and the sparse round's own top-k
+    (spin_estimate_miss: the weighted-threshold estimate and the hit-ratio
+    upper bound; -1 where nothing was explored).
     """
     import numpy as np
     import torch
@@ -363,17 +368,20 @@ def _fidelity_trace(wl, inputs, device, mask, update, keep_of, rounds=None):
     scores_all = torch.empty_like(scores)
     pq_all = torch.empty_like(pq)
     topk_all = torch.empty(B, R, K, **i32)
+    topk_sp = torch.empty(B, R, K, **i32)
+    est_dev = torch.zeros(L, B, R, 2, dtype=torch.float32, device=device)
     miss_dev = torch.zeros(L, B, R, dtype=torch.float32, device=device)
     cnt_dev = torch.zeros(L, B, **i32)
     acc_dev = acc.to(torch.int32).to(device)
     miss = np.zeros((T, L, B, R), dtype=np.float32)
+    est = np.zeros((T, L, B, R, 2), dtype=np.float32)
     kept_n = np.zeros((T, L, B), dtype=np.int64)
     keeps = np.zeros((T, L), dtype=np.int64)
     for t in range(T):
         qpos.copy_(qpos_all[t].to(torch.int32))
         cnt_all.copy_((qpos + (R - 1)) // 64 + 1)
         for l in range(L):
-            keep = int(keep_of(t, l, miss[:t]))
+            keep = int(keep_of(t, l, miss[:t], est[:t]))
             keeps[t, l] = keep
             q, w = qs[l][t]
             pool = pools[l]
@@ -385,19 +393,22 @@ def _fidelity_trace(wl, inputs, device, mask, update, keep_of, rounds=None):
             spin.spin_measure_miss(batch, K, topk_all, flags, miss_dev[l])
             spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale,
                                      pool.block_table, kept, cnt, scores, pq)
+            spin.spin_topk_scores(batch, K, scores, kept, cnt, topk_sp, None, pq)
+            spin.spin_estimate_miss(batch, K, scores, kept, cnt, topk_sp, flags, est_dev[l])
             if update == "prefix":
                 spin.spin_mtp_replay(st.handle, l, batch, acc_dev[t], scores, kept, cnt)
             else:
                 spin.spin_update(st.handle, l, batch, scores, kept, cnt)
             cnt_dev[l].copy_(cnt)
         miss[t] = miss_dev.cpu().numpy()
+        est[t] = est_dev.cpu().numpy()
         kept_n[t] = cnt_dev.cpu().numpy()
     if st.error() != 0:
         raise RuntimeError(f"device error word {st.error()}")
-    return miss, kept_n, keeps
+    return miss, kept_n, keeps, est
 
 
-def _fidelity_summary(miss, kept_n, keeps, qpos, rows, warmup, first_round=0):
+def _fidelity_summary(miss, kept_n, keeps, qpos, rows, warmup, first_round=0, est=None):
     """Mean and p99 miss over eligible rows, and the realized block sparsity.
 
     A row (round t, layer l, request b, row r) is eligible when the round is
@@ -407,6 +418,9 @@ def _fidelity_summary(miss, kept_n, keeps, qpos, rows, warmup, first_round=0):
     then averaged, as in the pages' per-layer, per-trace p99; `p99_pooled` is
     the p99 of all eligible rows together.  Realized sparsity = 1 - kept
     blocks / blocks up to the round's last row, over the eligible rounds.
+    With `est` (online estimates, -1 = none), the mean estimate over the
+    eligible rows that have one is reported beside the measured mean miss,
+    per layer and overall, with the rows' Pearson correlation to the miss.
     """
     import numpy as np
 
@@ -427,19 +441,118 @@ def _fidelity_summary(miss, kept_n, keeps, qpos, rows, warmup, first_round=0):
                 per_trace.append(np.percentile(x, 99))
                 lm.append(x)
         xl = np.concatenate(lm) if lm else np.zeros(0)
-        per_layer.append({"mean_miss": float(xl.mean()) if len(xl) else None,
-                          "p99_miss": float(np.mean([np.percentile(x, 99) for x in lm]))
-                          if lm else None})
+        rec = {"mean_miss": float(xl.mean()) if len(xl) else None,
+               "p99_miss": float(np.mean([np.percentile(x, 99) for x in lm])) if lm else None}
+        if est is not None:
+            el = np.asarray(est, dtype=np.float64)[:, l][elig[:, l]]      # [rows, 2]
+            el = el[el[:, 0] >= 0]
+            rec["online_mean_miss"] = float(el[:, 0].mean()) if len(el) else None
+            rec["online_upper_mean_miss"] = float(el[:, 1].mean()) if len(el) else None
+        per_layer.append(rec)
     allx = miss[elig]
     rt = np.arange(T) >= max(warmup, first_round)
     n_last = n_row[:, :, R - 1]                                     # [T, B]
     tot = float(n_last[rt].sum()) * L
-    return {"eligible_rows": int(elig.sum()),
+    online = {}
+    if est is not None:
+        e2 = np.asarray(est, dtype=np.float64)[elig]                      # [rows, 2]
+        has = e2[:, 0] >= 0
+        e, u, m = e2[has, 0], e2[has, 1], allx[has]
+        corr = lambda a: (float(np.corrcoef(a, m)[0, 1])
+                          if len(a) > 1 and a.std() > 0 and m.std() > 0 else None)
+        online = {"online_mean_miss": float(e.mean()) if len(e) else None,
+                  "online_upper_mean_miss": float(u.mean()) if len(u) else None,
+                  "online_rows_without_estimate": int((~has).sum()),
+                  "online_row_pearson": corr(e), "online_upper_row_pearson": corr(u)}
+    return {**online, "eligible_rows": int(elig.sum()),
             "mean_miss": float(allx.mean()) if len(allx) else None,
             "p99_miss": float(np.mean(per_trace)) if per_trace else None,
             "p99_pooled": float(np.percentile(allx, 99)) if len(allx) else None,
             "realized_sparsity": 1.0 - float(kept_n[rt].sum()) / tot if tot else None,
             "per_layer": per_layer}
+
+
+def _fidelity_predictors(wl, device, keeps):
+    """Table 1 of the v1 listing on a single-row workload: Pearson correlation
+    and top-k recall of slot predictors against the all-keep indexer, averaged
+    over requests and rounds 1..T-1.
+
+    Predictors: SPIN's z = max(V, D) from the state before the round (the
+    state itself runs SPIN rounds at each keep in `keeps`, observing only the
+    kept slots), prev-iter (the previous round's all-keep scores; the new
+    slots have none), and random (uniform values; expected recall K / N).
+    """
+    import numpy as np
+    import torch
+
+    import predictive_kv_block_amd as spin
+    from workload import make_pool, make_queries, positions
+
+    pool = make_pool(wl, 0, device=device)
+    B, nb, K, T = wl.batch, wl.blocks, wl.topk, wl.steps
+    qpos_all = positions(wl)
+    qs = [make_queries(wl, pool, 0, t, qpos_all[t].tolist(), device=device) for t in range(T)]
+    i32 = dict(dtype=torch.int32, device=device)
+    f32 = dict(dtype=torch.float32, device=device)
+    slot = torch.arange(B, **i32)
+    qpos = torch.zeros(B, **i32)
+    batch = spin.make_batch(slot, qpos, 1, nb)
+    kept, cnt = torch.zeros(B, nb, **i32), torch.zeros(B, **i32)
+    flags = torch.zeros(B, nb, dtype=torch.uint8, device=device)
+    scores, actual = torch.empty(B, 1, nb * 64, **f32), torch.empty(B, 1, nb * 64, **f32)
+    pq, pq_all = torch.empty(B, 1, nb, 4, **f32), torch.empty(B, 1, nb, 4, **f32)
+    kept_all = torch.arange(nb, **i32)[None, :].repeat(B, 1).contiguous()
+    cnt_all = torch.zeros(B, **i32)
+    z, prev, rnd = (torch.empty(B, 1, nb * 64, **f32) for _ in range(3))
+    ta, tp = torch.empty(B, 1, K, **i32), torch.empty(B, 1, K, **i32)
+    ws = torch.empty(max(256, spin.spin_topk_workspace_bytes(batch, K)), dtype=torch.uint8,
+                     device=device)
+    out = torch.empty(B, 1, 2, dtype=torch.float64, device=device)
+    slots = torch.arange(nb * 64, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.seed + 17)
+    res = []
+    for keep in keeps:
+        cfg = spin.make_config(1, B, wl.ctx, K, explore_bp=wl.explore_bp, alpha=wl.alpha)
+        st = spin.SpinState(cfg, device=device)
+        spin.spin_reset_slots(st.handle, slot, torch.arange(B, dtype=torch.int64,
+                                                            device=device) + 1000)
+        sums = {n: np.zeros(2) for n in ("spin", "prev_iter", "random")}
+        rows = 0
+        n_tok = 0
+        for t in range(T):
+            qpos.copy_(qpos_all[t].to(torch.int32))
+            cnt_all.copy_(qpos // 64 + 1)
+            q, w = qs[t]
+            spin.spin_slot_scores(st.handle, 0, batch, z)
+            spin.spin_predict_blocks(st.handle, 0, batch, keep, kept, cnt, flags)
+            spin.spin_quantize_q(st.handle, batch, q, w)
+            spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale,
+                                     pool.block_table, kept_all, cnt_all, actual, pq_all)
+            spin.spin_topk_scores(batch, K, actual, kept_all, cnt_all, ta, None, pq_all)
+            spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale,
+                                     pool.block_table, kept, cnt, scores, pq)
+            spin.spin_update(st.handle, 0, batch, scores, kept, cnt)
+            if t >= 1:
+                torch.rand(B, 1, nb * 64, generator=gen, device=device, out=rnd)
+                for name, p in (("spin", z), ("prev_iter", prev), ("random", rnd)):
+                    spin.spin_topk_scores(batch, K, p, kept_all, cnt_all, tp, ws)
+                    spin.spin_predictor_fidelity(batch, K, p, actual, tp, ta, out)
+                    sums[name] += out[:, 0, :].sum(dim=0).cpu().numpy()
+                rows += B
+                n_tok += int((qpos + 1).sum())
+            # prev-iter for the next round: these scores, none for later slots
+            torch.where(slots[None, None, :] <= qpos[:, None, None].long(), actual,
+                        torch.full_like(actual, float("-inf")), out=prev)
+        if st.error() != 0:
+            raise RuntimeError(f"device error word {st.error()}")
+        rec = {"fidelity": "predictors", "workload": wl.name, "keep_bp": keep,
+               "rounds": T - 1, "rows": rows, "topk": K, "k_over_n": K * rows / n_tok}
+        for name, v in sums.items():
+            rec[name] = {"pearson": float(v[0] / rows), "topk_recall": float(v[1] / rows)}
+        print(json.dumps(rec), flush=True)
+        res.append(rec)
+    return res
 
 
 def _fidelity(mode, wl, device, targets):
@@ -448,6 +561,8 @@ def _fidelity(mode, wl, device, targets):
     import predictive_kv_block_amd as spin
 
     spin.load()
+    if mode == "predictors":
+        return _fidelity_predictors(wl, device, [10000 - t for t in targets])
     t0 = time.perf_counter()
     inputs = _fidelity_inputs(wl, device)
     qpos = inputs[2].numpy()
@@ -458,38 +573,45 @@ def _fidelity(mode, wl, device, targets):
     if mode == "ablation":
         for tgt in targets:
             for mask, upd in FID_POLICIES:
-                miss, kept_n, keeps = _fidelity_trace(wl, inputs, device, mask, upd,
-                                                      lambda t, l, m, k=10000 - tgt: k)
-                s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm)
+                miss, kept_n, keeps, est = _fidelity_trace(wl, inputs, device, mask, upd,
+                                                           lambda t, l, m, e, k=10000 - tgt: k)
+                s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm, est=est)
                 rec = {"fidelity": "mtp_policy", "workload": wl.name, "target_sparsity_bp": tgt,
                        "mask": mask, "update": upd, **s}
                 print(json.dumps(rec), flush=True)
                 out.append(rec)
         return out
     # per-layer budgets: W calibration rounds at the uniform mean keep, then
-    # spin_allocate_budgets from the per-layer mean miss of those rounds
+    # spin_allocate_budgets from each layer's mean miss over those rounds,
+    # measured with the shadow all-keep indexer or estimated online from the
+    # exploration blocks alone
     W = 8
     mean_keep = 10000 - targets[-1]
-    uni = _fidelity_trace(wl, inputs, device, "union", "prefix", lambda t, l, m: mean_keep)
-    plan = {}
+    uni = _fidelity_trace(wl, inputs, device, "union", "prefix", lambda t, l, m, e: mean_keep)
+    runs = [("uniform", uni, None)]
+    for source in ("shadow", "online"):
+        plan = {}
 
-    def keep_of(t, l, m):
-        if t < W:
-            return mean_keep
-        if "keep" not in plan:
-            s = _fidelity_summary(m, np.ones((t, wl.layers, wl.batch)), np.full((t, wl.layers),
-                                  mean_keep), qpos, wl.rows, warm)
-            plan["calib_miss"] = [p["mean_miss"] for p in s["per_layer"]]
-            plan["keep"] = spin.spin_allocate_budgets(plan["calib_miss"], mean_keep)
-        return plan["keep"][l]
+        def keep_of(t, l, m, e, plan=plan, source=source):
+            if t < W:
+                return mean_keep
+            if "keep" not in plan:
+                if source == "online":
+                    m = np.where(e[..., 0] >= 0, e[..., 0], 0.0)
+                s = _fidelity_summary(m, np.ones((t, wl.layers, wl.batch)),
+                                      np.full((t, wl.layers), mean_keep), qpos, wl.rows, warm)
+                plan["calib_miss"] = [p["mean_miss"] for p in s["per_layer"]]
+                plan["keep"] = spin.spin_allocate_budgets(plan["calib_miss"], mean_keep)
+            return plan["keep"][l]
 
-    cal = _fidelity_trace(wl, inputs, device, "union", "prefix", keep_of)
-    for name, (miss, kept_n, keeps) in (("uniform", uni), ("per_layer", cal)):
-        s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm, first_round=W)
+        runs.append((f"per_layer_{source}",
+                     _fidelity_trace(wl, inputs, device, "union", "prefix", keep_of), plan))
+    for name, (miss, kept_n, keeps, est), plan in runs:
+        s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm, first_round=W, est=est)
         rec = {"fidelity": "layer_budgets", "workload": wl.name, "mean_keep_bp": mean_keep,
                "calibration_rounds": W, "budgets": name,
                "keep_bp": [int(k) for k in keeps[-1]], **s}
-        if name == "per_layer":
+        if plan:
             rec["calibration_mean_miss"] = plan["calib_miss"]
         print(json.dumps(rec), flush=True)
         out.append(rec)

@@ -55,3 +55,20 @@ def test_realized_sparsity_counts_blocks_to_the_last_row():
     s = bench._fidelity_summary(miss, kept, keeps, qpos, 2, warmup=1, first_round=3)
     assert np.isclose(s["realized_sparsity"], 1.0 - 40.0 / 101.0)
     assert s["eligible_rows"] == 2 * 2 * 3 * 2
+
+
+def test_online_estimates_are_reported_beside_the_miss():
+    miss, kept, keeps, qpos = _case(T=11, R=1)
+    rng = np.random.default_rng(3)
+    miss[:] = rng.random(miss.shape)
+    est = np.stack([miss, np.minimum(1.0, 2.0 * miss)], axis=-1)   # estimate exact, bound 2x
+    est[5, 0, 0, 0] = -1.0                                         # one row without an estimate
+    s = bench._fidelity_summary(miss, kept, keeps, qpos, 1, warmup=1, est=est)
+    assert s["online_rows_without_estimate"] == 1
+    keep = np.ones(miss[1:].shape, dtype=bool)
+    keep[4, 0, 0, 0] = False
+    assert np.isclose(s["online_mean_miss"], miss[1:][keep].mean())
+    assert np.isclose(s["online_upper_mean_miss"], np.minimum(1.0, 2.0 * miss[1:][keep]).mean())
+    assert np.isclose(s["online_row_pearson"], 1.0)
+    assert s["online_upper_row_pearson"] < 1.0
+    assert np.isclose(s["per_layer"][1]["online_mean_miss"], s["per_layer"][1]["mean_miss"])
