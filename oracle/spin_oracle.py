@@ -54,6 +54,9 @@ and RNG unstated.  The readings taken here (each marked READING below) are:
     rate places the all-keep top-k threshold inside the sparse round's own
     top-k, and the explored slots above it, scaled by skipped / explored,
     estimate the miss (estimate_miss);
+  * core attention over the top-k: every head attends to one shared cache
+    row per token (absorbed multi-head latent attention), softmax over the
+    row's valid top-k entries, the value being the row's first d_v entries;
   * row-0 mask policy (v1 Table 7 and Figure 2, "row-0" vs "row-local union"):
     the mask built for row 0 serves every row; the blocks past row 0's last
     block, which only the later rows reach (they hold the draft positions),
@@ -337,6 +340,39 @@ def topk_positions(scores_row, kept, qpos_r, k):
     out = np.full(k, -1, dtype=np.int64)
     out[: len(chosen)] = chosen
     return out
+
+
+# ---------------------------------------------------------------------------
+# Sparse core attention over the top-k  [v1 Abstract: a fixed top-k of
+# tokens goes to core attention].
+# ---------------------------------------------------------------------------
+def sparse_attention(q, kv_pages, block_table, topk, qpos_r, scale, d_v):
+    """Softmax attention of one query row over the slots of its top-k.
+
+    READING (the pages name DeepSeek-V3.2 / V4 and say only that a fixed top-k
+    of tokens goes to core attention): multi-head attention in which every
+    head attends to one shared cache row per token (the absorbed form of
+    multi-head latent attention): s_h(i) = scale * q_h . c_i over the valid
+    entries i of the top-k (>= 0 and <= qpos_r), o_h = sum_i softmax_i(s_h)
+    c_i[:d_v], lse_h = log sum_i exp(s_h(i)).  The cache row of slot i sits in
+    page block_table[i // 64] at row i % 64 (the indexer's block table).  A
+    row with no valid entry gives o = 0 and lse = -inf.
+    q: [H][d]; kv_pages: [P][64][d]; returns o [H][d_v], lse [H] (fp64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H = q.shape[0]
+    t = np.asarray(topk, dtype=np.int64)
+    t = t[(t >= 0) & (t <= qpos_r)]
+    if len(t) == 0:
+        return np.zeros((H, d_v)), np.full(H, NEG_INF)
+    pages = np.asarray(block_table, dtype=np.int64)[t // BLOCK]
+    rows = np.asarray(kv_pages, dtype=np.float64)[pages, t % BLOCK]    # [n][d]
+    s = scale * (q @ rows.T)                                           # [H][n]
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1)
+    o = (e @ rows[:, :d_v]) / l[:, None]
+    return o, m[:, 0] + np.log(l)
 
 
 # ---------------------------------------------------------------------------
