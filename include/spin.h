@@ -11,6 +11,9 @@
  *     spin_update          -> EMA update from the observed slots (R == 1)
  *     spin_mtp_replay      -> prefix-valid EMA replay once acceptance is known
  *
+ * The selection's consumer: spin_sparse_attention (core attention over the
+ * top-k).
+ *
  * Measurement calls beside the round: spin_measure_miss (against an all-keep
  * top-k), spin_estimate_miss (from exploration hits alone), spin_slot_scores
  * and spin_predictor_fidelity (a slot predictor against the indexer), and the
@@ -326,6 +329,35 @@ int spin_estimate_miss(const spin_batch* batch, int topk, const float* scores,
 int spin_predictor_fidelity(const spin_batch* batch, int topk, const float* pred,
                             const float* actual, const int32_t* pred_topk,
                             const int32_t* actual_topk, double* out, hipStream_t stream);
+
+/* [host] Workspace for spin_sparse_attention: 0 when each row runs as one
+ * share of its top-k list, else the per-share partial outputs. */
+int spin_attention_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
+
+/* Sparse core attention over each row's top-k, the consumer of the selection
+ * (v1 listing, Abstract: a fixed top-k of tokens goes to core attention).
+ * READING (the pages name DeepSeek-V3.2 / V4 and give no attention shape):
+ * the absorbed form of multi-head latent attention, 128 query heads sharing
+ * one cache row of 576 values per token (512 latent + 64 rotary), the value
+ * being the row's first 512:
+ *     s_h(i) = scale * q_h . c_i,   o_h = sum_i softmax_i(s_h) c_i[0:512],
+ *     lse_h = log sum_i exp(s_h(i))
+ * over the valid entries i of topk_idx[b][r][:] (>= 0, <= qpos + r, with a
+ * block-table entry in [0, pool_pages)); the cache row of slot i is row
+ * i % 64 of page block_table[b][i / 64] (the indexer's block table).
+ * q_bf16: [B][R][128][576] bf16, 16-byte aligned; kv_bf16:
+ * [pool_pages][64][576] bf16, 16-byte aligned; out_bf16: [B][R][128][512]
+ * bf16 (RNE from fp32), 8-byte aligned; lse: fp32 [B][R][128].  Scores and
+ * the softmax run in fp32 on the MFMA's fp32 sums of bf16 products; the
+ * weights enter the value product as bf16.  A row with no valid entry gets
+ * o = 0 and lse = -inf; a request whose qpos is negative or whose last row
+ * needs more than max_blocks blocks gets o = 0 and lse = NaN.  workspace:
+ * 256-byte aligned, spin_attention_workspace_bytes() bytes (NULL allowed
+ * when that is 0), clobbered.  topk <= 4096; batch->slot is not read. */
+int spin_sparse_attention(const spin_batch* batch, int topk, const int32_t* topk_idx,
+                          const void* q_bf16, const void* kv_bf16, int64_t pool_pages,
+                          const int32_t* block_table, float scale, void* out_bf16, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* [host] Per-layer keep budgets from measured miss rates (v3 abstract: the
  * block budget is allocated across layers by their measured miss rates).

@@ -14,7 +14,8 @@ __all__ = [
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
-    "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity", "EXPORTS",
+    "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
+    "spin_attention_workspace_bytes", "spin_sparse_attention", "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so")
@@ -25,6 +26,7 @@ EXPORTS = [
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
     "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
+    "spin_attention_workspace_bytes", "spin_sparse_attention",
 ]
 
 SPIN_OK, SPIN_EINVAL, SPIN_EUNSUPPORTED, SPIN_EHIP, SPIN_ESTATE = 0, -1, -2, -3, -4
@@ -87,6 +89,9 @@ _SIGS = {
     "spin_slot_scores": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp],
     "spin_estimate_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "spin_predictor_fidelity": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "spin_attention_workspace_bytes": [ctypes.POINTER(SpinBatch), _i32, ctypes.POINTER(_sz)],
+    "spin_sparse_attention": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _i64, _vp,
+                              ctypes.c_float, _vp, _vp, _vp, _sz, _vp],
 }
 
 
@@ -248,6 +253,22 @@ def spin_predictor_fidelity(batch, topk, pred, actual, pred_topk, actual_topk, o
     _check(load().spin_predictor_fidelity(ctypes.byref(batch), int(topk), _p(pred), _p(actual),
                                           _p(pred_topk), _p(actual_topk), _p(out),
                                           _stream(stream)))
+
+
+def spin_attention_workspace_bytes(batch, topk):
+    n = _sz()
+    _check(load().spin_attention_workspace_bytes(ctypes.byref(batch), int(topk), ctypes.byref(n)))
+    return n.value
+
+
+def spin_sparse_attention(batch, topk, topk_idx, q_bf16, kv_bf16, block_table, scale, out_bf16,
+                          lse, workspace=None, stream=None):
+    """q_bf16 [B,R,128,576] and kv_bf16 [pages,64,576] bf16 tensors; out_bf16 [B,R,128,512]."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().spin_sparse_attention(ctypes.byref(batch), int(topk), _p(topk_idx), _p(q_bf16),
+                                        _p(kv_bf16), int(kv_bf16.shape[0]), _p(block_table),
+                                        float(scale), _p(out_bf16), _p(lse), _p(workspace),
+                                        ws_bytes, _stream(stream)))
 
 
 def spin_allocate_budgets(miss, mean_keep_bp):

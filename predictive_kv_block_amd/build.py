@@ -31,7 +31,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["spin_abi.cpp", "spin_state.hip", "spin_predict.hip", "spin_indexer.hip",
-           "spin_topk.hip", "spin_update.hip", "spin_fidelity.hip"]
+           "spin_topk.hip", "spin_update.hip", "spin_fidelity.hip", "spin_attention.hip"]
 
 
 def _compile(src, build_dir=BUILD, extra=()):

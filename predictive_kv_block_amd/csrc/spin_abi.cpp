@@ -1,10 +1,13 @@
 // C ABI of the SPIN library: argument checks, state layout, kernel launches.
 #include <math.h>
+
+#include <cmath>
 #include <stdio.h>
 #include <string.h>
 
 #include <new>
 
+#include "spin_attention.h"
 #include "spin_fidelity.h"
 #include "spin_internal.h"
 
@@ -309,6 +312,36 @@ int spin_predictor_fidelity(const spin_batch* batch, int topk, const float* pred
     return SPIN_EINVAL;
   return hip_status(spin::launch_predictor_fidelity(*batch, topk, pred, actual, pred_topk,
                                                     actual_topk, out, stream));
+}
+
+int spin_attention_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes) {
+  int rc = check_plain_batch(batch);
+  if (rc) return rc;
+  if (!bytes || topk < 1 || topk > 4096) return SPIN_EINVAL;
+  *bytes = spin::attention_plan(*batch, topk).ws_bytes;
+  return SPIN_OK;
+}
+
+int spin_sparse_attention(const spin_batch* batch, int topk, const int32_t* topk_idx,
+                          const void* q_bf16, const void* kv_bf16, int64_t pool_pages,
+                          const int32_t* block_table, float scale, void* out_bf16, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_plain_batch(batch);
+  if (rc) return rc;
+  if (topk < 1 || topk > 4096 || !topk_idx || !q_bf16 || !kv_bf16 || !block_table ||
+      !out_bf16 || !lse || pool_pages < 1 || pool_pages > (int64_t(1) << 25) ||
+      !std::isfinite(scale))
+    return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(q_bf16) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(kv_bf16) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(out_bf16) % 8 != 0 || reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return SPIN_EINVAL;
+  const spin::AttnPlan p = spin::attention_plan(*batch, topk);
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes ||
+                         reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+    return SPIN_EINVAL;
+  return hip_status(spin::launch_attention(*batch, topk, topk_idx, q_bf16, kv_bf16, pool_pages,
+                                           block_table, scale, out_bf16, lse, workspace, stream));
 }
 
 int spin_allocate_budgets(int L, const double* miss, int mean_keep_bp, int32_t* keep_bp_out) {
