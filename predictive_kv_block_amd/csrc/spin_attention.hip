@@ -16,8 +16,10 @@
 //     already in the B-operand layout of the 32 PV MFMAs (registers 8ks..8ks+7
 //     are k-step ks), with no shuffle;
 //   - O^T accumulates in 16 32x32 tiles per wave (512 channels x 32 heads).
-// With more than one share per row, each share writes its normalised fp32
-// output and log-sum-exp, and a second kernel merges them.
+// The cache rows of a share are resolved (top-k entry -> block table -> row)
+// once, before the first tile.  With more than one share per row, each share
+// writes its normalised fp32 output and log-sum-exp, and a second kernel
+// merges them.
 #include "spin_attention.h"
 #include "spin_device.h"
 
@@ -34,6 +36,8 @@ constexpr int kKRow = kAttnDim + 8;                   // bf16 per row-major row 
 constexpr int kVRow = kAT + 8;                        // bf16 per transposed (channel) row
 constexpr int kChunks = kAttnDim / 8;                 // 16-byte chunks per cache row
 constexpr int kItems = (kAT / 4) * kChunks;           // (token quad, chunk) staging items
+constexpr int kItemsPerThread = (kItems + 255) / 256;
+constexpr int kMaxShare = 4096;                       // top-k entries per share (<= topk)
 constexpr int kTargetGroups = 512;                    // workgroups aimed for per launch
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -78,8 +82,8 @@ __global__ void __launch_bounds__(kAThreads, 1)
 k_attention(AttnArgs a) {
   __shared__ __align__(16) uint16_t s_k[kAT * kKRow];
   __shared__ __align__(16) uint16_t s_vt[kAttnValueDim * kVRow];
-  __shared__ int s_tok[kAT];
-  __shared__ uint32_t s_mask;
+  __shared__ int s_tok[kMaxShare];          // pool row of each entry of the share, -1 = skipped
+  __shared__ uint32_t s_mask[kMaxShare / kAT];
 
   const int split = blockIdx.x, row = blockIdx.y;
   const int b = row / a.bt.R, r = row - b * a.bt.R;
@@ -105,44 +109,60 @@ k_attention(AttnArgs a) {
     for (int i = 0; i < 16; ++i) acc[ct][i] = 0.0f;
   float m = -INFINITY, lsum = 0.0f;
 
-  for (int t0 = e0; ok && t0 < e1; t0 += kAT) {
-    if (tid < kAT) {
-      const int e = t0 + tid;
-      int prow = -1;
-      if (e < e1) {
-        const int p = a.topk[size_t(row) * a.K + e];
-        if (p >= 0 && p <= qr) {
-          const int pg = a.table[size_t(b) * a.bt.max_blocks + p / kBlock];
-          if (pg >= 0 && pg < a.pool_pages) prow = pg * kBlock + (p & (kBlock - 1));
-        }
+  // the share's cache rows, resolved once: top-k entry -> block table -> row
+  const int n_share = ok ? max(0, e1 - e0) : 0;
+  for (int i = tid; i < (n_share + kAT - 1) / kAT * kAT; i += kAThreads) {
+    int prow = -1;
+    if (i < n_share) {
+      const int p = a.topk[size_t(row) * a.K + e0 + i];
+      if (p >= 0 && p <= qr) {
+        const int pg = a.table[size_t(b) * a.bt.max_blocks + p / kBlock];
+        if (pg >= 0 && pg < a.pool_pages) prow = pg * kBlock + (p & (kBlock - 1));
       }
-      s_tok[tid] = prow;
-      const uint64_t bal = __ballot(prow >= 0);
-      if (tid == 0) s_mask = uint32_t(bal);
     }
-    __syncthreads();
-    const uint32_t vmask = s_mask;
+    s_tok[i] = prow;
+    const uint64_t bal = __ballot(prow >= 0);     // i - l is a multiple of 64
+    if (l == 0) {
+      s_mask[i / kAT] = uint32_t(bal);
+      s_mask[i / kAT + 1] = uint32_t(bal >> 32);
+    }
+  }
+  __syncthreads();
+
+  for (int t0 = 0; t0 < n_share; t0 += kAT) {
+    const uint32_t vmask = s_mask[t0 / kAT];
     if (vmask != 0) {
-      // gather: item (token quad tq, 16-byte chunk cc) of the tile
-      for (int it = tid; it < kItems; it += kAThreads) {
-        const int tq = it / kChunks, cc = it - tq * kChunks;
-        uint4 x[4];
+      // gather: item (token quad tq, 16-byte chunk cc) of the tile; every
+      // load of the thread is issued before the first LDS store.  Items run
+      // tq-fastest, so the 16 lanes of a transposed store cover 8 token quads
+      // x 2 chunks: 32 distinct banks
+      uint4 gq[kItemsPerThread][4];
+#pragma unroll
+      for (int k = 0; k < kItemsPerThread; ++k) {
+        const int it = tid + k * kAThreads;
+        const int tq = it & 7, cc = it >> 3;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int prow = s_tok[4 * tq + u];
-          x[u] = *reinterpret_cast<const uint4*>(a.kv + size_t(prow < 0 ? 0 : prow) * kAttnDim +
-                                                 8 * cc);
+          const int prow = it < kItems ? s_tok[t0 + 4 * tq + u] : -1;
+          gq[k][u] = *reinterpret_cast<const uint4*>(a.kv + size_t(prow < 0 ? 0 : prow) * kAttnDim +
+                                                     8 * (it < kItems ? cc : 0));
         }
+      }
+#pragma unroll
+      for (int k = 0; k < kItemsPerThread; ++k) {
+        const int it = tid + k * kAThreads;
+        if (it >= kItems) continue;
+        const int tq = it & 7, cc = it >> 3;
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          *reinterpret_cast<uint4*>(&s_k[(4 * tq + u) * kKRow + 8 * cc]) = x[u];
+          *reinterpret_cast<uint4*>(&s_k[(4 * tq + u) * kKRow + 8 * cc]) = gq[k][u];
         if (cc < kAttnValueDim / 8) {
           const int p0 = vt_pos(4 * tq);
 #pragma unroll
           for (int c2 = 0; c2 < 8; ++c2) {
             uint2 v;
-            v.x = half16(x[0], c2) | (half16(x[1], c2) << 16);
-            v.y = half16(x[2], c2) | (half16(x[3], c2) << 16);
+            v.x = half16(gq[k][0], c2) | (half16(gq[k][1], c2) << 16);
+            v.y = half16(gq[k][2], c2) | (half16(gq[k][3], c2) << 16);
             *reinterpret_cast<uint2*>(&s_vt[(8 * cc + c2) * kVRow + p0]) = v;
           }
         }
@@ -197,7 +217,7 @@ k_attention(AttnArgs a) {
           if (ks == 1 && (ct & 1) == 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
-    __syncthreads();              // the next tile overwrites s_tok, s_k and s_vt
+    __syncthreads();              // the next tile overwrites s_k and s_vt
   }
 
   // lane pair (l, l ^ 32) covers the head's 32 tokens per tile
@@ -231,16 +251,20 @@ k_attention(AttnArgs a) {
   }
 }
 
+constexpr int kCombineGroups = 16;                    // head groups per row in the merge
+
 // Merge of the shares of each row: lse = log sum_s exp(lse_s),
-// o = sum_s exp(lse_s - lse) o_s.  grid (rows), 256 threads; thread item
-// (head, 4-channel group).
+// o = sum_s exp(lse_s - lse) o_s.  grid (rows, kCombineGroups), 256 threads;
+// thread item (head, 4-channel group).
 __global__ void __launch_bounds__(256)
 k_attention_combine(AttnArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.bt.R;
   const bool ok = row_ok(a.bt, b);
-  for (int it = threadIdx.x; it < kAttnHeads * (kAttnValueDim / 4); it += 256) {
-    const int head = it / (kAttnValueDim / 4), cq = it - head * (kAttnValueDim / 4);
+  constexpr int kHeadsPerGroup = kAttnHeads / kCombineGroups;
+  for (int it = threadIdx.x; it < kHeadsPerGroup * (kAttnValueDim / 4); it += 256) {
+    const int head = blockIdx.y * kHeadsPerGroup + it / (kAttnValueDim / 4);
+    const int cq = it % (kAttnValueDim / 4);
     const size_t base = size_t(row) * a.splits * kAttnHeads + head;
     float mx = -INFINITY;
     for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.ws_lse[base + size_t(s) * kAttnHeads]);
@@ -315,7 +339,7 @@ hipError_t launch_attention(const spin_batch& bt, int topk, const int32_t* topk_
   a.ws_lse = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_o_bytes) : nullptr;
   hipLaunchKernelGGL(k_attention, dim3(p.splits, p.rows), dim3(kAThreads), 0, s, a);
   if (p.splits > 1)
-    hipLaunchKernelGGL(k_attention_combine, dim3(p.rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attention_combine, dim3(p.rows, kCombineGroups), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
