@@ -23,6 +23,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_DENSE_PEAK_TFLOPS = 5000.0 # MI355X dense fp8 MFMA
+BF16_DENSE_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA
 PAGE_BYTES = 64 * 128          # fp8 keys of one 64-token page
 # Algorithmic bytes the indexer kernel moves per kept page and row: the page's
 # keys, its scale, its block-table entry, its kept-list entry, 64 fp32 scores
@@ -89,6 +90,8 @@ def _args():
                          "policies over target sparsities, per-layer budgets, or slot "
                          "predictor quality (Pearson, top-k recall)")
     ap.add_argument("--fid-targets", default=",".join(str(t) for t in FID_TARGETS))
+    ap.add_argument("--attention", action="store_true",
+                    help="time the sparse core attention over a real round's top-k instead")
     return ap.parse_args()
 
 
@@ -618,6 +621,66 @@ def _fidelity(mode, wl, device, targets):
     return out
 
 
+def _attention_bench(wl, device, steps, warmup, keep_bp):
+    """Time the sparse core attention over the top-k of a real round.
+
+    Two rounds (the all-keep warm-up, then one at keep_bp) produce each
+    row's top-k from the indexer; a latent cache of the workload's full size
+    (pool pages x 64 tokens x 576 bf16) and bf16 queries for 128 heads are
+    drawn on the device; the attention over that top-k is then launched
+    `steps` times between HIP events on the current stream.
+    """
+    import torch
+
+    spin, pool, cfg, st, bufs, make_queries = _setup(wl, device)
+    from workload import positions
+
+    side = torch.cuda.Stream(device=device)
+    qp = positions(wl)
+    done = None
+    for t, keep in enumerate((10000, keep_bp)):
+        bufs["qpos"].copy_(qp[t].to(torch.int32))
+        q, w = make_queries(wl, pool, 0, t, qp[t].tolist(), device=device)
+        done = _round(spin, st, bufs, pool, q, w, keep, side, done)
+    torch.cuda.synchronize()
+    H, D, DV = 128, 576, 512
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed + 31)
+    kv = torch.empty(wl.pool_pages, 64, D, dtype=torch.bfloat16, device=device)
+    for i in range(0, wl.pool_pages, 8192):
+        kv[i:i + 8192].copy_(torch.randn(min(8192, wl.pool_pages - i), 64, D, device=device,
+                                         generator=g))
+    qa = torch.randn(wl.batch, wl.rows, H, D, device=device, generator=g).to(torch.bfloat16)
+    n = spin.spin_attention_workspace_bytes(bufs["batch"], wl.topk)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    out = torch.empty(wl.batch, wl.rows, H, DV, dtype=torch.bfloat16, device=device)
+    lse = torch.empty(wl.batch, wl.rows, H, device=device)
+    scale = 1.0 / 192 ** 0.5
+    args = (bufs["batch"], wl.topk, bufs["topk"], qa, kv, pool.block_table, scale, out, lse, ws)
+    for _ in range(warmup):
+        spin.spin_sparse_attention(*args)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        spin.spin_sparse_attention(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    tok = int((bufs["topk"] >= 0).sum())
+    rows = wl.batch * wl.rows
+    byts = tok * D * 2 + rows * (H * D * 2 + H * DV * 2 + H * 4 + wl.topk * 4)
+    flops = 2 * H * tok * (D + DV)
+    return {"workload": wl.name, "rows": rows, "topk": wl.topk, "attended_tokens": tok,
+            "us_per_launch": round(us, 2), "workspace_bytes": n,
+            "algorithmic_bytes": byts, "flops": flops,
+            "hbm": {"achieved_GBps": round(byts / us / 1e3, 1), "peak": HBM_PEAK_GBS,
+                    "frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)},
+            "mfma_bf16": {"achieved_TFLOPs": round(flops / us / 1e6, 1),
+                          "peak": BF16_DENSE_PEAK_TFLOPS,
+                          "frac": round(flops / us / 1e6 / BF16_DENSE_PEAK_TFLOPS, 4)}}
+
+
 def _copy_calibration(device):
     import torch
     n = 1 << 30
@@ -646,6 +709,10 @@ def main():
     SPACER_CYCLES = a.spacer_cycles
     if a.fidelity:
         _fidelity(a.fidelity, wl, device, [int(x) for x in a.fid_targets.split(",")])
+        return
+    if a.attention:
+        print(json.dumps({"attention": _attention_bench(wl, device, a.steps, a.warmup,
+                                                        10000 - a.sparsity_bp)}), flush=True)
         return
     keep_main = 10000 - a.sparsity_bp
     sweep = [10000 - int(s) for s in a.sweep.split(",") if s.strip() != ""]
