@@ -40,6 +40,7 @@ constexpr int kItemsPerThread = (kItems + 255) / 256;
 constexpr int kMaxShare = 4096;                       // top-k entries per share (<= topk)
 constexpr int kTargetGroups = 512;                    // workgroups aimed for per launch
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleLog2 = 8.0f;                  // reference-max slack (base 2)
 
 struct AttnArgs {
   spin_batch bt;
@@ -129,46 +130,53 @@ k_attention(AttnArgs a) {
   }
   __syncthreads();
 
+  // Gather of tile t0 into registers: item (token quad tq, 16-byte chunk cc).
+  // Items run tq-fastest, so the 16 lanes of a transposed store cover 8 token
+  // quads x 2 chunks: 32 distinct banks.  The next tile's loads are issued
+  // before the current tile's MFMAs, so their latency overlaps them.
+  uint4 gq[kItemsPerThread][4];
+  auto issue = [&](int t0) {
+#pragma unroll
+    for (int k = 0; k < kItemsPerThread; ++k) {
+      const int it = tid + k * kAThreads;
+      const int tq = it & 7, cc = it >> 3;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int prow = it < kItems ? s_tok[t0 + 4 * tq + u] : -1;
+        gq[k][u] = *reinterpret_cast<const uint4*>(a.kv + size_t(prow < 0 ? 0 : prow) * kAttnDim +
+                                                   8 * (it < kItems ? cc : 0));
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int k = 0; k < kItemsPerThread; ++k) {
+      const int it = tid + k * kAThreads;
+      if (it >= kItems) continue;
+      const int tq = it & 7, cc = it >> 3;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<uint4*>(&s_k[(4 * tq + u) * kKRow + 8 * cc]) = gq[k][u];
+      if (cc < kAttnValueDim / 8) {
+        const int p0 = vt_pos(4 * tq);
+#pragma unroll
+        for (int c2 = 0; c2 < 8; ++c2) {
+          uint2 v;
+          v.x = half16(gq[k][0], c2) | (half16(gq[k][1], c2) << 16);
+          v.y = half16(gq[k][2], c2) | (half16(gq[k][3], c2) << 16);
+          *reinterpret_cast<uint2*>(&s_vt[(8 * cc + c2) * kVRow + p0]) = v;
+        }
+      }
+    }
+  };
+
+  if (n_share > 0) issue(0);
   for (int t0 = 0; t0 < n_share; t0 += kAT) {
     const uint32_t vmask = s_mask[t0 / kAT];
+    stage();
+    __syncthreads();
+    if (t0 + kAT < n_share) issue(t0 + kAT);
     if (vmask != 0) {
-      // gather: item (token quad tq, 16-byte chunk cc) of the tile; every
-      // load of the thread is issued before the first LDS store.  Items run
-      // tq-fastest, so the 16 lanes of a transposed store cover 8 token quads
-      // x 2 chunks: 32 distinct banks
-      uint4 gq[kItemsPerThread][4];
-#pragma unroll
-      for (int k = 0; k < kItemsPerThread; ++k) {
-        const int it = tid + k * kAThreads;
-        const int tq = it & 7, cc = it >> 3;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int prow = it < kItems ? s_tok[t0 + 4 * tq + u] : -1;
-          gq[k][u] = *reinterpret_cast<const uint4*>(a.kv + size_t(prow < 0 ? 0 : prow) * kAttnDim +
-                                                     8 * (it < kItems ? cc : 0));
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kItemsPerThread; ++k) {
-        const int it = tid + k * kAThreads;
-        if (it >= kItems) continue;
-        const int tq = it & 7, cc = it >> 3;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          *reinterpret_cast<uint4*>(&s_k[(4 * tq + u) * kKRow + 8 * cc]) = gq[k][u];
-        if (cc < kAttnValueDim / 8) {
-          const int p0 = vt_pos(4 * tq);
-#pragma unroll
-          for (int c2 = 0; c2 < 8; ++c2) {
-            uint2 v;
-            v.x = half16(gq[k][0], c2) | (half16(gq[k][1], c2) << 16);
-            v.y = half16(gq[k][2], c2) | (half16(gq[k][3], c2) << 16);
-            *reinterpret_cast<uint2*>(&s_vt[(8 * cc + c2) * kVRow + p0]) = v;
-          }
-        }
-      }
-      __syncthreads();
-
       f32x16 s;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = 0.0f;
@@ -189,8 +197,12 @@ k_attention(AttnArgs a) {
         mx = fmaxf(mx, x[i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(m, mx);             // finite: the tile has a valid token
-      const float alpha = exp2f(m - mnew);         // 0 on the first tile
+      // The weights are taken against a reference m that moves only when the
+      // tile's maximum passes it by more than kRescaleLog2: weights stay below
+      // 2^kRescaleLog2, o and l share the reference, and o / l is unchanged,
+      // while the 256-register rescale of o runs on few tiles.
+      const float mnew = (mx > m + kRescaleLog2) ? mx : m;   // m = -inf: the first tile moves it
+      const float alpha = exp2f(m - mnew);         // 0 on the first tile, 1 unless m moved
       float psum = 0.0f;
       bf16x8 pb[2];
 #pragma unroll
