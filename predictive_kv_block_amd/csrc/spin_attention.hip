@@ -38,7 +38,8 @@ constexpr int kChunks = kAttnDim / 8;                 // 16-byte chunks per cach
 constexpr int kItems = (kAT / 4) * kChunks;           // (token quad, chunk) staging items
 constexpr int kItemsPerThread = (kItems + 255) / 256;
 constexpr int kMaxShare = 4096;                       // top-k entries per share (<= topk)
-constexpr int kTargetGroups = 512;                    // workgroups aimed for per launch
+constexpr int kMaxShares = 16;                        // shares per row at most
+constexpr double kMergeCostPerShare = 0.008;          // merge cost of one share-row, in tile-times
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleLog2 = 8.0f;                  // reference-max slack (base 2)
 
@@ -317,10 +318,26 @@ AttnPlan attention_plan(const spin_batch& bt, int topk) {
   AttnPlan p;
   p.rows = bt.B * bt.R;
   const int tiles = (topk + kAT - 1) / kAT;
-  int s = (kTargetGroups + p.rows - 1) / p.rows;
-  s = s < 1 ? 1 : (s > 16 ? 16 : s);
-  s = s > tiles ? tiles : s;
-  p.chunk = ((tiles + s - 1) / s) * kAT;
+  // One workgroup fills a CU, so the launch runs in ceil(groups / CUs) rounds
+  // of `tiles per share` tiles each; every share adds a partial that the merge
+  // reads (about kMergeCostPerShare tile-times per row and share, measured).
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int sp = 1; sp <= kMaxShares && sp <= tiles; ++sp) {
+    const double rounds = double((int64_t(p.rows) * sp + cus - 1) / cus);
+    const double cost = rounds * double((tiles + sp - 1) / sp) +
+                        (sp > 1 ? kMergeCostPerShare * p.rows * sp : 0.0);
+    if (sp == 1 || cost < best_cost) {
+      best = sp;
+      best_cost = cost;
+    }
+  }
+  p.chunk = ((tiles + best - 1) / best) * kAT;
   p.splits = (topk + p.chunk - 1) / p.chunk;
   p.ws_o_bytes = p.splits > 1 ? align256(size_t(p.rows) * p.splits * kAttnHeads * kAttnValueDim * 4)
                               : 0;
