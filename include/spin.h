@@ -351,7 +351,9 @@ int spin_attention_workspace_bytes(const spin_batch* batch, int topk, size_t* by
  * the softmax run in fp32 on the MFMA's fp32 sums of bf16 products; the
  * weights enter the value product as bf16.  A row with no valid entry gets
  * o = 0 and lse = -inf; a request whose qpos is negative or whose last row
- * needs more than max_blocks blocks gets o = 0 and lse = NaN.  workspace:
+ * needs more than max_blocks blocks gets o = 0 and lse = NaN.  A row may run
+ * as several shares of its list whose normalised outputs (bf16) and
+ * log-sum-exps are merged in fp32.  workspace:
  * 256-byte aligned, spin_attention_workspace_bytes() bytes (NULL allowed
  * when that is 0), clobbered.  topk <= 4096; batch->slot is not read. */
 int spin_sparse_attention(const spin_batch* batch, int topk, const int32_t* topk_idx,

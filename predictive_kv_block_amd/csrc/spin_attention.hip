@@ -18,8 +18,8 @@
 //   - O^T accumulates in 16 32x32 tiles per wave (512 channels x 32 heads).
 // The cache rows of a share are resolved (top-k entry -> block table -> row)
 // once, before the first tile.  With more than one share per row, each share
-// writes its normalised fp32 output and log-sum-exp, and a second kernel
-// merges them.
+// writes its normalised output (bf16) and log-sum-exp, and a second kernel
+// merges them in fp32.
 #include "spin_attention.h"
 #include "spin_device.h"
 
@@ -54,7 +54,7 @@ struct AttnArgs {
   const int32_t* topk;              // [rows][K]
   uint16_t* out;                    // [rows][128][512] bf16
   float* lse;                       // [rows][128]
-  float* ws_o;                      // [rows][splits][128][512]
+  uint16_t* ws_o;                   // [rows][splits][128][512] bf16, normalised per share
   float* ws_lse;                    // [rows][splits][128]
 };
 
@@ -252,19 +252,21 @@ k_attention(AttnArgs a) {
     if (hg == 0) a.lse[size_t(row) * kAttnHeads + head] = lse;
   } else {
     const size_t part = (size_t(row) * a.splits + split) * kAttnHeads + head;
-    float* o = a.ws_o + part * kAttnValueDim;
+    uint16_t* o = a.ws_o + part * kAttnValueDim;
 #pragma unroll
     for (int ct = 0; ct < kAttnValueDim / 32; ++ct)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(o + 32 * ct + 8 * g + 4 * hg) =
-            make_float4(acc[ct][4 * g] * inv, acc[ct][4 * g + 1] * inv,
-                        acc[ct][4 * g + 2] * inv, acc[ct][4 * g + 3] * inv);
+      for (int g = 0; g < 4; ++g) {
+        uint2 v;
+        v.x = bf16_bits(acc[ct][4 * g] * inv) | (bf16_bits(acc[ct][4 * g + 1] * inv) << 16);
+        v.y = bf16_bits(acc[ct][4 * g + 2] * inv) | (bf16_bits(acc[ct][4 * g + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(o + 32 * ct + 8 * g + 4 * hg) = v;
+      }
     if (hg == 0) a.ws_lse[part] = lse;
   }
 }
 
-constexpr int kCombineGroups = 16;                    // head groups per row in the merge
+constexpr int kCombineGroups = 64;                    // head groups per row in the merge (one item per thread)
 
 // Merge of the shares of each row: lse = log sum_s exp(lse_s),
 // o = sum_s exp(lse_s - lse) o_s.  grid (rows, kCombineGroups), 256 threads;
@@ -287,12 +289,12 @@ k_attention_combine(AttnArgs a) {
       for (int s = 0; s < a.splits; ++s) {
         const size_t part = base + size_t(s) * kAttnHeads;
         const float wgt = __expf(a.ws_lse[part] - mx);
-        const float4 v = *reinterpret_cast<const float4*>(a.ws_o + part * kAttnValueDim + 4 * cq);
+        const uint2 v = *reinterpret_cast<const uint2*>(a.ws_o + part * kAttnValueDim + 4 * cq);
         den += wgt;
-        o.x += wgt * v.x;
-        o.y += wgt * v.y;
-        o.z += wgt * v.z;
-        o.w += wgt * v.w;
+        o.x += wgt * __uint_as_float(v.x << 16);
+        o.y += wgt * __uint_as_float(v.x & 0xFFFF0000u);
+        o.z += wgt * __uint_as_float(v.y << 16);
+        o.w += wgt * __uint_as_float(v.y & 0xFFFF0000u);
       }
       const float inv = 1.0f / den;
       o.x *= inv;
@@ -339,7 +341,7 @@ AttnPlan attention_plan(const spin_batch& bt, int topk) {
   }
   p.chunk = ((tiles + best - 1) / best) * kAT;
   p.splits = (topk + p.chunk - 1) / p.chunk;
-  p.ws_o_bytes = p.splits > 1 ? align256(size_t(p.rows) * p.splits * kAttnHeads * kAttnValueDim * 4)
+  p.ws_o_bytes = p.splits > 1 ? align256(size_t(p.rows) * p.splits * kAttnHeads * kAttnValueDim * 2)
                               : 0;
   p.ws_bytes = p.splits > 1 ? p.ws_o_bytes + align256(size_t(p.rows) * p.splits * kAttnHeads * 4)
                             : 0;
@@ -364,7 +366,7 @@ hipError_t launch_attention(const spin_batch& bt, int topk, const int32_t* topk_
   a.topk = topk_idx;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.ws_o = p.splits > 1 ? static_cast<float*>(ws) : nullptr;
+  a.ws_o = p.splits > 1 ? static_cast<uint16_t*>(ws) : nullptr;
   a.ws_lse = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_o_bytes) : nullptr;
   hipLaunchKernelGGL(k_attention, dim3(p.splits, p.rows), dim3(kAThreads), 0, s, a);
   if (p.splits > 1)

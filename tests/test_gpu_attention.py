@@ -2,8 +2,10 @@
 
 Tolerance, from the arithmetic: the kernel rounds each softmax weight to bf16
 before the value product (relative error <= 2^-9 per weight, so <= 2^-9 *
-max_i |v_ic| on output channel c) and rounds the output to bf16 (<= 2^-9 |o|);
-fp32 sums, exp2 and the split merge add far less.  Bound used:
+max_i |v_ic| on output channel c), rounds each share's normalised partial to
+bf16 (<= 2^-9 |o_s| <= 2^-9 max_i |v_ic|, and the merge is a convex
+combination of the partials) and rounds the output to bf16 (<= 2^-9 |o|);
+fp32 sums and exp2 add far less.  Bound used:
 |o - o_ref| <= 2^-8 * max_i |v_ic| + 2^-8 * |o_ref|.  The log-sum-exp moves by
 at most the largest score error, which for fp32 sums of 576 bf16 products is
 below scale * 576 * 2^-23 * max_i sum_d |q_d k_id|; 1e-5 (1 + |lse|) covers
