@@ -331,7 +331,9 @@ int spin_predictor_fidelity(const spin_batch* batch, int topk, const float* pred
                             const int32_t* actual_topk, double* out, hipStream_t stream);
 
 /* [host] Workspace for spin_sparse_attention: 0 when each row runs as one
- * share of its top-k list, else the per-share partial outputs. */
+ * share of its top-k list, else the per-share partial outputs.  The share
+ * count depends on the current device's compute-unit count: query it with
+ * the device current that will run the call. */
 int spin_attention_workspace_bytes(const spin_batch* batch, int topk, size_t* bytes);
 
 /* Sparse core attention over each row's top-k, the consumer of the selection
