@@ -17,9 +17,12 @@
 //     are k-step ks), with no shuffle;
 //   - O^T accumulates in 16 32x32 tiles per wave (512 channels x 32 heads).
 // The cache rows of a share are resolved (top-k entry -> block table -> row)
-// once, before the first tile.  With more than one share per row, each share
-// writes its normalised output (bf16) and log-sum-exp, and a second kernel
-// merges them in fp32.
+// once, before the first tile, and each tile's gather is issued into
+// registers before the previous tile's MFMAs.  The softmax weights are taken
+// against a reference maximum that moves only when a tile passes it by more
+// than 2^8, so the rescale of O is rare.  With more than one share per row,
+// each share writes its normalised output (bf16) and log-sum-exp, and a second
+// kernel merges them in fp32.
 #include "spin_attention.h"
 #include "spin_device.h"
 
