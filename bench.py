@@ -90,6 +90,8 @@ def _args():
                          "policies over target sparsities, per-layer budgets, or slot "
                          "predictor quality (Pearson, top-k recall)")
     ap.add_argument("--fid-targets", default=",".join(str(t) for t in FID_TARGETS))
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the HBM rates of a streaming read, a copy and a page gather")
     ap.add_argument("--attention", action="store_true",
                     help="time the sparse core attention over a real round's top-k instead")
     return ap.parse_args()
@@ -681,6 +683,47 @@ def _attention_bench(wl, device, steps, warmup, keep_bp):
                           "frac": round(flops / us / 1e6 / BF16_DENSE_PEAK_TFLOPS, 4)}}
 
 
+def _ceilings(device, reps=10):
+    """HBM rates this part reaches with plain torch kernels: streaming reads
+    of 4 GiB (a sum, row sums, and a matrix-vector product), a device copy
+    (2 GiB read + 2 GiB written), and a gather of random 8 KB pages into a
+    fresh output (the indexer's read pattern, with a write stream beside
+    it).  GB/s of bytes moved."""
+    import torch
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    out = {}
+    x = torch.ones(1 << 30, dtype=torch.float32, device=device)           # 4 GiB
+    m = x.view(1 << 17, 1 << 13)
+    v = torch.ones(1 << 13, dtype=torch.float32, device=device)
+    reads = {"sum": lambda: x.sum(), "row_sums": lambda: m.sum(dim=1), "gemv": lambda: m @ v}
+    out["read_GBps"] = {k: round(x.numel() * 4 / timed(f) / 1e9, 1) for k, f in reads.items()}
+    del x, m, v
+    a = torch.ones(1 << 29, dtype=torch.float32, device=device)           # 2 GiB
+    b = torch.empty_like(a)
+    out["copy_GBps"] = round(2 * a.numel() * 4 / timed(lambda: b.copy_(a)) / 1e9, 1)
+    del a, b
+    pages = torch.ones(786432, 2048, dtype=torch.float32, device=device)  # 6 GiB of 8 KB pages
+    g = torch.Generator(device=device)
+    g.manual_seed(7)
+    idx = torch.randperm(pages.shape[0], generator=g, device=device)[:393216]
+    t = timed(lambda: pages.index_select(0, idx))
+    out["page_gather_GBps"] = round(2 * idx.numel() * 8192 / t / 1e9, 1)
+    out["page_gather_read_GBps"] = round(idx.numel() * 8192 / t / 1e9, 1)
+    return out
+
+
 def _copy_calibration(device):
     import torch
     n = 1 << 30
@@ -709,6 +752,9 @@ def main():
     SPACER_CYCLES = a.spacer_cycles
     if a.fidelity:
         _fidelity(a.fidelity, wl, device, [int(x) for x in a.fid_targets.split(",")])
+        return
+    if a.ceilings:
+        print(json.dumps({"hbm_ceilings": _ceilings(device)}), flush=True)
         return
     if a.attention:
         print(json.dumps({"attention": _attention_bench(wl, device, a.steps, a.warmup,
