@@ -338,3 +338,40 @@ def test_allocate_budgets_invariants():
     assert np.array_equal(O.allocate_budgets([0.1] * 4, 5000), [5000] * 4)
     out = O.allocate_budgets([0.0, 0.0, 0.0, 1.0], 5000)       # clamps: one layer saturates
     assert out[3] == 10000 and out[:3].sum() == 10000 and np.all(out[:3] >= 2500)
+
+
+def _largest_remainder(exact):
+    """Integer basis points from exact Fractions: floors, then +1 to the
+    largest remainders (ties to the lower layer) until the total is whole."""
+    base = [int(math.floor(x)) for x in exact]
+    rem = int(sum(exact)) - sum(base)
+    order = sorted(range(len(exact)), key=lambda l: (-(exact[l] - base[l]), l))
+    for l in order[:rem]:
+        base[l] += 1
+    return base
+
+
+@pytest.mark.parametrize("L,mean,seed", [(2, 5000, 1), (4, 6000, 2), (7, 5500, 3), (12, 7000, 4)])
+def test_allocate_budgets_unclamped_closed_form(L, mean, seed):
+    """Without clamping the rule is keep_l = L * mean * w_l / sum(w), w_l = m_l + 1e-3:
+    computed exactly in rationals, then rounded by largest remainder."""
+    rng = np.random.default_rng(seed)
+    m = 0.05 + rng.random(L) * 0.05                  # near-equal: no layer reaches a clamp
+    w = [Fraction(float(x)) + Fraction(1, 1000) for x in m]
+    exact = [Fraction(L * mean) * wl / sum(w) for wl in w]
+    assert all(Fraction(mean, 2) < x < 10000 for x in exact)
+    assert list(O.allocate_budgets(m, mean)) == _largest_remainder(exact)
+
+
+def test_allocate_budgets_clamped_closed_forms():
+    # the cap binds: the high-miss layer takes 10000, the other the rest of 2 * mean
+    assert list(O.allocate_budgets([0.0, 0.9], 7000)) == [4000, 10000]
+    # the floor binds: the low-miss layer keeps mean / 2, the other the rest
+    assert list(O.allocate_budgets([0.0, 0.9], 6000)) == [3000, 9000]
+    # three layers, one capped: the other two share 3 * mean - 10000 in proportion
+    m = [0.10, 0.12, 0.95]
+    out = O.allocate_budgets(m, 6500)
+    w = [Fraction(0.10) + Fraction(1, 1000), Fraction(0.12) + Fraction(1, 1000)]
+    rest = Fraction(3 * 6500 - 10000)
+    assert out[2] == 10000
+    assert list(out[:2]) == _largest_remainder([rest * w[0] / sum(w), rest * w[1] / sum(w)])
