@@ -100,3 +100,30 @@ def test_allocate_budgets_matches_oracle(L, mean):
         assert sum(got) == L * mean
     with pytest.raises(spin.SpinError):
         spin.spin_allocate_budgets([0.1, 1.5], 5000)
+
+
+def test_header_is_plain_c_and_links():
+    """include/spin.h compiles as C11, and a C program that takes the address
+    of every entry point links against libspin.so (the boundary is a C ABI)."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    cc = shutil.which("gcc")
+    if cc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = "#include \"spin.h\"\n#include <stdio.h>\nint main(void) {\n  void* fns[] = {\n"
+    src += ",\n".join(f"    (void*)&{name}" for name in spin.EXPORTS)
+    src += "\n  };\n  printf(\"%d\\n\", (int)(sizeof(fns) / sizeof(fns[0])));\n  return 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "abi_check.c")
+        exe = os.path.join(d, "abi_check")
+        with open(c, "w") as f:
+            f.write(src)
+        lib_dir = os.path.dirname(spin.LIB_PATH)
+        r = subprocess.run([cc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                            "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                            c, "-o", exe, "-L", lib_dir, "-l:libspin.so",
+                            "-Wl,--allow-shlib-undefined"],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
