@@ -12,6 +12,8 @@
 //   weights and the head sum run on the accumulator registers, the 4 lane
 //   groups are folded with two cross-lane adds, and every lane then holds the
 //   score of token `lane`; rows are staged in LDS and written in bursts.
+#include <atomic>
+
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -33,7 +35,7 @@ constexpr int kDim = 128;
 #define SPIN_IDX_NONTEMPORAL 0
 #endif
 #ifndef SPIN_IDX_STAGES
-#define SPIN_IDX_STAGES 3              // key ring depth: pages in flight + the one on the MFMAs
+#define SPIN_IDX_STAGES 2              // key ring depth: pages in flight + the one on the MFMAs
 #endif
 #ifndef SPIN_IDX_NT_STORE
 #define SPIN_IDX_NT_STORE 1            // streaming (non-temporal) score stores
@@ -71,6 +73,14 @@ constexpr int kFlushRows = SPIN_IDX_FLUSH_ROWS;
 #define SPIN_IDX_FLUSH_ROWS_MR 32      // the same with several query rows
 #endif
 constexpr int kFlushRowsMR = SPIN_IDX_FLUSH_ROWS_MR;
+#ifndef SPIN_IDX_MIN_PAGES_PER_WG
+#define SPIN_IDX_MIN_PAGES_PER_WG 16   // smallest share of the batch's pages a workgroup takes
+#endif
+constexpr int kIdxMinPagesPerWg = SPIN_IDX_MIN_PAGES_PER_WG;
+#ifndef SPIN_IDX_ROUNDS
+#define SPIN_IDX_ROUNDS 4              // dispatch rounds of resident workgroups per launch
+#endif
+constexpr int kIdxRounds = SPIN_IDX_ROUNDS;
 static_assert(kStages1 >= 2 && SPIN_IDX_STAGES_MR >= 2 && kPagesPerWave + kStages1 <= kWave &&
                   SPIN_IDX_PAGES_PER_WAVE_MR + SPIN_IDX_STAGES_MR <= kWave,
               "indexer pipeline shape");
@@ -170,6 +180,10 @@ __device__ __forceinline__ float page_row_score(const PageRegs& kb, const uint8_
       part[tt] = fmaf(wv.z, relu2(acc[tt][2]), part[tt]);
       part[tt] = fmaf(wv.w, relu2(acc[tt][3]), part[tt]);
     }
+    // One head tile's epilogue at a time: without this fence the scheduler
+    // gathers the ReLU terms of all 64 accumulators ahead of their FMAs and
+    // the kernel no longer fits 3 waves per SIMD.
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
@@ -179,21 +193,45 @@ __device__ __forceinline__ float page_row_score(const PageRegs& kb, const uint8_
   return g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
 }
 
-// grid (ceil(max_blocks / (W * P)), B), W waves of 64 threads, P = pages per wave.
-// Wave w of workgroup x handles the P consecutive kept positions starting at
-// x*W*P + w*P.  Page metadata (kept entry -> block table -> scale) sits in
-// lanes 0..P-1 and is read back with scalar lane reads, so every branch on it
-// is wave-uniform.  Keys stream through a ring of kStages register buffers:
-// while page m is on the MFMAs, pages m+1 .. m+kStages-1 are in flight.
-// Score rows are staged in LDS and written kFlushRows/R pages at a time as one
-// contiguous burst per row: single 256-byte rows, each written long after its
-// neighbours, reach HBM as scattered partial-row writes that stall the key
-// stream far more than their share of the bytes.
+// Count of kept pages of row b as the kernels use it: negative counts read as
+// 0 and counts above max_blocks as max_blocks (both are reported as errors).
+__device__ __forceinline__ int kept_pages_of(const int32_t* kept_count, int b, int max_blocks) {
+  const int c = kept_count[b];
+  return c < 0 ? 0 : (c > max_blocks ? max_blocks : c);
+}
+
+// 64-bit value of lane `src` (wave-uniform result).
+__device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(uint64_t(x)), src);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(uint64_t(x) >> 32), src);
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// Balanced split.  The batch's kept pages, taken row after row in kept order,
+// form one sequence of T pages; the workgroups used (whole dispatch rounds of
+// the resident workgroups, or one partial round for a small batch) take equal
+// consecutive shares of it, so every workgroup finishes at about the same
+// time whatever the kept counts are (per-row chunks of fixed size leave a
+// partial last dispatch round that costs a full one).  A share that crosses a row boundary is processed
+// one row segment at a time: the segment's queries are staged in LDS and its
+// pages split into 4 consecutive wave ranges.  Every wave walks the counts
+// itself, so the workgroup's barriers are uniform.
+//
+// Within a wave range, page metadata (kept entry -> block table -> scale) for
+// up to P pages sits in lanes 0..P-1 and is read back with scalar lane reads,
+// so every branch on it is wave-uniform.  Keys stream through a ring of
+// kStages register buffers: while page m is on the MFMAs, pages m+1 ..
+// m+kStages-1 are in flight.  Score rows are staged in LDS and written
+// kFlushRows/R pages at a time as one contiguous burst per row: single
+// 256-byte rows, each written long after its neighbours, reach HBM as
+// scattered partial-row writes that stall the key stream far more than their
+// share of the bytes.
 template <int R>
 __global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
-          const int32_t* kept, const int32_t* kept_count, float* scores, float* page_qmax) {
+          const int32_t* kept, const int32_t* kept_count, float* scores, float* page_qmax,
+          int resident) {
   constexpr int kPagesPerWaveR = pages_per_wave<R>();
   constexpr int F = (R == 1 ? kFlushRows : kFlushRowsMR) / R > 0
                         ? (R == 1 ? kFlushRows : kFlushRowsMR) / R : 1;   // pages per flush
@@ -201,127 +239,186 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kQStride];
   __shared__ float s_w[R * kHeads];
   __shared__ __attribute__((aligned(16))) float s_out[kIdxWaves * R * F * kBlock];
-  const int b = blockIdx.y;
-  int cnt = kept_count[b];
-  if (cnt < 0 || cnt > bt.max_blocks) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) flag_error(v.err, SPIN_ERR_KEPT);
-    cnt = cnt < 0 ? 0 : bt.max_blocks;
-  }
-  const int first = blockIdx.x * (kIdxWaves * kPagesPerWaveR);
-  if (first >= cnt) return;
+  __shared__ int s_seg[3 * kWave];
 
   const int l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const size_t mb = size_t(bt.max_blocks);
-  const int kw = first + wave * kPagesPerWaveR;           // this wave's first kept position
-  const int npages = max(0, min(kPagesPerWaveR, cnt - kw));
 
-  // Page metadata for this wave's pages, lane m holding page m (j = -1: invalid).
-  int my_j = -1, my_p = 0;
-  float my_sc = 0.0f;
-  if (l < npages) {
-    const int j = kept[size_t(b) * mb + kw + l];
-    if (j < 0 || j >= bt.max_blocks) {
-      flag_error(v.err, SPIN_ERR_KEPT);
-    } else {
-      const int p = table[size_t(b) * mb + j];
-      if (p < 0 || int64_t(p) >= pool_pages) {
-        flag_error(v.err, SPIN_ERR_PAGE);
-      } else {
-        my_j = j;
-        my_p = p;
-        my_sc = k_scale[p];
-      }
+  // Total kept pages T (per lane the low and high parts of its counts, so the
+  // wave sums stay within int).
+  int64_t total = 0;
+  for (int r0 = 0; r0 < bt.B; r0 += kWave) {
+    int c = 0;
+    if (r0 + l < bt.B) {
+      const int raw = kept_count[r0 + l];
+      c = kept_pages_of(kept_count, r0 + l, bt.max_blocks);
+      if (raw != c && blockIdx.x == 0 && wave == 0) flag_error(v.err, SPIN_ERR_KEPT);
     }
+    total += (int64_t(wave_sum(c >> 12)) << 12) + wave_sum(c & 4095);
   }
+  // Workgroups used: whole dispatch rounds of the `resident` workgroups while
+  // each gets at least 32 R pages (up to kIdxRounds rounds), else one partial
+  // round of shares of at least kIdxMinPagesPerWg pages.
+  int64_t rounds = total / (int64_t(resident) * 32 * R);
+  if (rounds > kIdxRounds) rounds = kIdxRounds;
+  int64_t groups = rounds > 0 ? rounds * resident
+                              : (total + kIdxMinPagesPerWg - 1) / kIdxMinPagesPerWg;
+  if (rounds == 0 && groups > resident) groups = resident;
+  if (groups > int64_t(gridDim.x)) groups = gridDim.x;
+  if (int64_t(blockIdx.x) >= groups) return;
+  const int64_t g0 = int64_t(blockIdx.x) * total / groups;
+  const int64_t g1 = (int64_t(blockIdx.x) + 1) * total / groups;
 
-  // Stage this request's quantised queries and halved head weights in LDS.
-  const uint8_t* q8 = v.q8 + size_t(b) * v.max_rows * kHeads * kDim;
-  const float* wq = v.wq + size_t(b) * v.max_rows * kHeads;
-  for (int i = threadIdx.x; i < R * kHeads * kDim / 16; i += kIdxWaves * kWave)
-    *reinterpret_cast<uint4*>(s_q + (i / (kDim / 16)) * kQStride + (i % (kDim / 16)) * 16) =
-        reinterpret_cast<const uint4*>(q8)[i];
-  for (int i = threadIdx.x; i < R * kHeads; i += kIdxWaves * kWave) s_w[i] = 0.5f * wq[i];
-
-  const int q0 = bt.qpos[b];
   const int g = l >> 4;       // lane group: K chunk of the operands, M rows of the result
   const int n16 = l & 15;     // M row of A / N column of B
+  const int lane_off = n16 * kDim + g * 32;
   float* my_out = s_out + wave * (R * F * kBlock);
 
-  // Invalid pages (flagged above) read page 0 and are written as -inf.
-  const int lane_off = n16 * kDim + g * 32;
-  PageRegs ring[kStages];
+  // Walk the rows 64 at a time: lane l holds row r0 + l, its pages [start, end)
+  // in the sequence; rows meeting [g0, g1) are this workgroup's segments.
+  // Wave 0 lists them in LDS (row, first and end kept position), so that no
+  // per-lane walk state stays live while pages are scored.
+  int64_t base = 0;
+  for (int r0 = 0; r0 < bt.B && base < g1; r0 += kWave) {
+    int nseg;
+    {
+      const int c = (r0 + l < bt.B) ? kept_pages_of(kept_count, r0 + l, bt.max_blocks) : 0;
+      int64_t incl = c;
 #pragma unroll
-  for (int f = 0; f + 1 < kStages; ++f)
-    load_page(ring[f], k_pool, __builtin_amdgcn_readlane(my_p, f), f < npages, lane_off);
-  __syncthreads();
-
-  for (int m0 = 0; m0 < npages; m0 += kStages) {
-#pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int m = m0 + u;
-      if (m >= npages) break;
-      load_page(ring[(u + kStages - 1) % kStages], k_pool,
-                __builtin_amdgcn_readlane(my_p, m + kStages - 1), m + kStages - 1 < npages,
-                lane_off);
-      const int j = __builtin_amdgcn_readlane(my_j, m);
-      const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_sc), m));
-      const int mf = m % F;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float out = -INFINITY;
-        if (j >= 0) {
-          const float val = page_row_score<R>(ring[u], s_q, s_w, r, g, n16);
-          out = (j * kBlock + l <= q0 + r) ? val * sc : -INFINITY;
-        }
-        my_out[(r * F + mf) * kBlock + l] = out;
-        if (page_qmax) {
-          // maxima of the page's four 16-slot quarters (DPP row reduction;
-          // lane 16c + 15 holds quarter c), written as one 16-byte row
-          float x = out;
-          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
-                           __float_as_int(-INFINITY), __float_as_int(x), 0x111, 0xF, 0xF, false)));
-          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
-                           __float_as_int(-INFINITY), __float_as_int(x), 0x112, 0xF, 0xF, false)));
-          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
-                           __float_as_int(-INFINITY), __float_as_int(x), 0x114, 0xF, 0xF, false)));
-          x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
-                           __float_as_int(-INFINITY), __float_as_int(x), 0x118, 0xF, 0xF, false)));
-          if ((l & 15) == 15)
-            page_qmax[((size_t(b) * R + r) * mb + kw + m) * 4 + (l >> 4)] = x;
-        }
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int64_t t = __shfl_up(incl, o, kWave);
+        if (l >= o) incl += t;
       }
-      if (mf == F - 1 || m + 1 == npages) {
-        // Flush pages m-mf .. m of every row: LDS -> one contiguous burst.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int n4 = (mf + 1) * (kBlock / 4);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          v4f* dst = reinterpret_cast<v4f*>(scores + (size_t(b) * R + r) * mb * kBlock +
-                                            size_t(kw + m - mf) * kBlock);
-          const v4f* src = reinterpret_cast<const v4f*>(my_out + r * F * kBlock);
-#pragma unroll
-          for (int i0 = 0; i0 < F * (kBlock / 4); i0 += kWave) {
-            const int i = i0 + l;
-            if (i < n4) {
-#if SPIN_IDX_NT_STORE
-              __builtin_nontemporal_store(src[i], dst + i);
-#else
-              dst[i] = src[i];
-#endif
+      const int64_t end = base + incl, start = end - c;
+      const bool on = c > 0 && start < g1 && end > g0;
+      const uint64_t hit = __ballot(on);
+      nseg = __popcll(hit);
+      __syncthreads();     // the previous list and staged queries are no longer read
+      if (wave == 0 && on) {
+        const int at = ballot_rank(hit);
+        s_seg[3 * at] = r0 + l;
+        s_seg[3 * at + 1] = int((g0 > start ? g0 : start) - start);
+        s_seg[3 * at + 2] = int((g1 < end ? g1 : end) - start);
+      }
+      base += readlane64(incl, kWave - 1);
+      __syncthreads();
+    }
+    for (int si = 0; si < nseg; ++si) {
+      const int b = __builtin_amdgcn_readfirstlane(s_seg[3 * si]);
+      const int k0 = __builtin_amdgcn_readfirstlane(s_seg[3 * si + 1]);
+      const int k1 = __builtin_amdgcn_readfirstlane(s_seg[3 * si + 2]);
+
+      // Stage this row's quantised queries and halved head weights in LDS.
+      if (si > 0) __syncthreads();
+      const uint8_t* q8 = v.q8 + size_t(b) * v.max_rows * kHeads * kDim;
+      const float* wq = v.wq + size_t(b) * v.max_rows * kHeads;
+      for (int x = threadIdx.x; x < R * kHeads * kDim / 16; x += kIdxWaves * kWave)
+        *reinterpret_cast<uint4*>(s_q + (x / (kDim / 16)) * kQStride + (x % (kDim / 16)) * 16) =
+            reinterpret_cast<const uint4*>(q8)[x];
+      for (int x = threadIdx.x; x < R * kHeads; x += kIdxWaves * kWave) s_w[x] = 0.5f * wq[x];
+      __syncthreads();
+
+      const int q0 = bt.qpos[b];
+      const int n = k1 - k0;
+      const int wa = k0 + int(int64_t(n) * wave / kIdxWaves);
+      const int we = k0 + int(int64_t(n) * (wave + 1) / kIdxWaves);
+      for (int kw = wa; kw < we; kw += kPagesPerWaveR) {
+        const int npages = min(kPagesPerWaveR, we - kw);
+
+        // Page metadata of this batch, lane m holding page m (j = -1: invalid).
+        int my_j = -1, my_p = 0;
+        float my_sc = 0.0f;
+        if (l < npages) {
+          const int j = kept[size_t(b) * mb + kw + l];
+          if (j < 0 || j >= bt.max_blocks) {
+            flag_error(v.err, SPIN_ERR_KEPT);
+          } else {
+            const int p = table[size_t(b) * mb + j];
+            if (p < 0 || int64_t(p) >= pool_pages) {
+              flag_error(v.err, SPIN_ERR_PAGE);
+            } else {
+              my_j = j;
+              my_p = p;
+              my_sc = k_scale[p];
             }
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // Invalid pages (flagged above) read page 0 and are written as -inf.
+        PageRegs ring[kStages];
+#pragma unroll
+        for (int f = 0; f + 1 < kStages; ++f)
+          load_page(ring[f], k_pool, __builtin_amdgcn_readlane(my_p, f), f < npages, lane_off);
+
+        for (int m0 = 0; m0 < npages; m0 += kStages) {
+#pragma unroll
+          for (int u = 0; u < kStages; ++u) {
+            const int m = m0 + u;
+            if (m >= npages) break;
+            load_page(ring[(u + kStages - 1) % kStages], k_pool,
+                      __builtin_amdgcn_readlane(my_p, m + kStages - 1), m + kStages - 1 < npages,
+                      lane_off);
+            const int j = __builtin_amdgcn_readlane(my_j, m);
+            const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_sc), m));
+            const int mf = m % F;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              float out = -INFINITY;
+              if (j >= 0) {
+                const float val = page_row_score<R>(ring[u], s_q, s_w, r, g, n16);
+                out = (j * kBlock + l <= q0 + r) ? val * sc : -INFINITY;
+              }
+              my_out[(r * F + mf) * kBlock + l] = out;
+              if (page_qmax) {
+                // maxima of the page's four 16-slot quarters (DPP row reduction;
+                // lane 16c + 15 holds quarter c), written as one 16-byte row
+                float x = out;
+                x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                                 __float_as_int(-INFINITY), __float_as_int(x), 0x111, 0xF, 0xF, false)));
+                x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                                 __float_as_int(-INFINITY), __float_as_int(x), 0x112, 0xF, 0xF, false)));
+                x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                                 __float_as_int(-INFINITY), __float_as_int(x), 0x114, 0xF, 0xF, false)));
+                x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
+                                 __float_as_int(-INFINITY), __float_as_int(x), 0x118, 0xF, 0xF, false)));
+                if ((l & 15) == 15)
+                  page_qmax[((size_t(b) * R + r) * mb + kw + m) * 4 + (l >> 4)] = x;
+              }
+            }
+            if (mf == F - 1 || m + 1 == npages) {
+              // Flush pages m-mf .. m of every row: LDS -> one contiguous burst.
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+              const int n4 = (mf + 1) * (kBlock / 4);
+#pragma unroll
+              for (int r = 0; r < R; ++r) {
+                v4f* dst = reinterpret_cast<v4f*>(scores + (size_t(b) * R + r) * mb * kBlock +
+                                                  size_t(kw + m - mf) * kBlock);
+                const v4f* src = reinterpret_cast<const v4f*>(my_out + r * F * kBlock);
+#pragma unroll
+                for (int i0 = 0; i0 < F * (kBlock / 4); i0 += kWave) {
+                  const int x = i0 + l;
+                  if (x < n4) {
+#if SPIN_IDX_NT_STORE
+                    __builtin_nontemporal_store(src[x], dst + x);
+#else
+                    dst[x] = src[x];
+#endif
+                  }
+                }
+              }
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+          }
+        }
       }
     }
   }
 }
-
 }  // namespace
 
 hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* q_bf16,
@@ -331,29 +428,64 @@ hipError_t launch_quantize(const SpinView& v, const spin_batch& bt, const void* 
   return hipGetLastError();
 }
 
+// Workgroups of one indexer launch: kIdxRounds dispatch rounds of the
+// device's resident k_indexer<R> workgroups (occupancy x compute units, taken
+// once per device), and no more than shares of kIdxMinPagesPerWg pages need;
+// the kernel uses as many of them as the batch's kept pages call for.
+template <int R>
+hipError_t indexer_groups(const spin_batch& bt, unsigned* groups, int* resident_out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> resident[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int cap = (dev >= 0 && dev < kMaxDevices) ? resident[dev].load(std::memory_order_relaxed) : 0;
+  if (cap <= 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_indexer<R>, kIdxWaves * kWave, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cap = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+    if (dev >= 0 && dev < kMaxDevices) resident[dev].store(cap, std::memory_order_relaxed);
+  }
+  const int64_t most =
+      (int64_t(bt.B) * bt.max_blocks + kIdxMinPagesPerWg - 1) / kIdxMinPagesPerWg;
+  int64_t g = int64_t(cap) * kIdxRounds;
+  if (g > most) g = most;
+  *groups = unsigned(g > 0 ? g : 1);
+  *resident_out = cap;
+  return hipSuccess;
+}
+
 hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t* k_pool,
                           const float* k_scale, int64_t pool_pages, const int32_t* table,
                           const int32_t* kept, const int32_t* kept_count, float* scores,
                           float* page_qmax, hipStream_t s) {
-  const int per_wg = kIdxWaves * (bt.R == 1 ? pages_per_wave<1>() : pages_per_wave<2>());
-  const dim3 grid(unsigned((bt.max_blocks + per_wg - 1) / per_wg), unsigned(bt.B));
   const dim3 block(kIdxWaves * kWave);
+  unsigned groups = 1;
+  int resident = 1;
+  hipError_t e = hipSuccess;
   switch (bt.R) {
     case 1:
-      hipLaunchKernelGGL(k_indexer<1>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_qmax);
+      if ((e = indexer_groups<1>(bt, &groups, &resident)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_indexer<1>, dim3(groups), block, 0, s, v, bt, k_pool, k_scale,
+                         pool_pages, table, kept, kept_count, scores, page_qmax, resident);
       break;
     case 2:
-      hipLaunchKernelGGL(k_indexer<2>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_qmax);
+      if ((e = indexer_groups<2>(bt, &groups, &resident)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_indexer<2>, dim3(groups), block, 0, s, v, bt, k_pool, k_scale,
+                         pool_pages, table, kept, kept_count, scores, page_qmax, resident);
       break;
     case 3:
-      hipLaunchKernelGGL(k_indexer<3>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_qmax);
+      if ((e = indexer_groups<3>(bt, &groups, &resident)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_indexer<3>, dim3(groups), block, 0, s, v, bt, k_pool, k_scale,
+                         pool_pages, table, kept, kept_count, scores, page_qmax, resident);
       break;
     case 4:
-      hipLaunchKernelGGL(k_indexer<4>, grid, block, 0, s, v, bt, k_pool, k_scale, pool_pages,
-                         table, kept, kept_count, scores, page_qmax);
+      if ((e = indexer_groups<4>(bt, &groups, &resident)) != hipSuccess) return e;
+      hipLaunchKernelGGL(k_indexer<4>, dim3(groups), block, 0, s, v, bt, k_pool, k_scale,
+                         pool_pages, table, kept, kept_count, scores, page_qmax, resident);
       break;
     default:
       return hipErrorInvalidValue;

@@ -120,6 +120,61 @@ def test_indexer_scores_parity(gpu_lib, R):
     assert rig.state.error() == 0
 
 
+@pytest.mark.parametrize("R", [1, 4])
+def test_indexer_balanced_split_many_short_rows(gpu_lib, R):
+    """The indexer splits the batch's kept pages, row after row, into equal
+    workgroup shares: with 150 rows (three 64-row walk chunks), kept counts
+    from 0 to the maximum and most rows shorter than a share, shares start and
+    end inside rows and span many rows; every row must still match the oracle
+    and nothing past its kept count may be written."""
+    rng = np.random.default_rng(100 + R)
+    B, mb, pages = 150, 24, 400
+    codes, sc = _rand_pool(rng, pages)
+    table = np.stack([rng.permutation(pages)[:mb] for _ in range(B)]).astype(np.int32)
+    qpos = rng.integers(64 * 4, 64 * mb - R, size=B).astype(np.int64)
+    kept = []
+    for b in range(B):
+        n = nblocks(qpos[b] + R - 1)
+        size = [0, 1, 2, 3, n][b % 5] if b % 7 else int(rng.integers(0, n + 1))
+        kept.append(np.sort(rng.choice(n, size=min(size, n), replace=False)))
+    q = (torch.randn(B, R, 64, 128) * 2).to(torch.bfloat16)
+    w = torch.rand(B, R, 64) + 0.5
+    cfg = spin.make_config(1, B, 64 * mb, 2048, max_rows=R)
+    rig = Rig(cfg, B, R, mb)
+    rig.set_qpos(qpos)
+    kt = np.full((B, mb), -1, dtype=np.int32)
+    for b in range(B):
+        kt[b, : len(kept[b])] = kept[b]
+    rig.kept.copy_(torch.as_tensor(kt))
+    rig.kept_count.copy_(torch.as_tensor([len(k) for k in kept], dtype=torch.int32))
+    rig.scores.fill_(12345.0)
+    pq = torch.full((B, R, mb, 4), 777.0, device=DEV)
+    _say("indexer balanced split R", R, "rows", B, "kept pages", sum(len(k) for k in kept))
+    spin.spin_quantize_q(rig.h, rig.batch, q.to(DEV), w.to(DEV))
+    spin.spin_indexer_scores(rig.h, rig.batch, codes.to(DEV), sc.to(DEV),
+                             torch.as_tensor(table).to(DEV), rig.kept, rig.kept_count, rig.scores,
+                             pq)
+    torch.cuda.synchronize()
+    gpq = np_(pq)
+    kv = O.e4m3fn_decode(np_(codes))
+    scv = np_(sc).astype(np.float64)
+    got = np_(rig.scores)
+    for b in range(B):
+        nk = len(kept[b])
+        n = nk * 64
+        assert np.all(got[b, :, n:] == 12345.0), f"b{b}: written past the kept count"
+        assert np.all(gpq[b, :, nk:] == 777.0), f"b{b}"
+        if not nk:
+            continue
+        qv, wv, _, _ = oracle_fp8_operands(q[b], w[b])
+        ref = O.indexer_scores(qv, wv, kv, scv, table[b], kept[b], int(qpos[b]))
+        mag = score_mag(qv, wv, kv, scv, table[b], kept[b])
+        assert_scores_close(got[b, :, :n], ref, mag, f"b{b}")
+        own = got[b, :, :n].reshape(R, nk, 4, 16).max(axis=3)
+        assert np.array_equal(gpq[b, :, :nk], own), f"b{b}"
+    assert rig.state.error() == 0
+
+
 # ------------------------------------------------------------------- top-k
 TOPK_CASES = {
     # name: (rows R, max_blocks, K, pattern); "pm-" cases pass page quarter maxima
