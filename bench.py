@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_DENSE_PEAK_TFLOPS = 5000.0 # MI355X dense fp8 MFMA
 BF16_DENSE_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20         # MI355X Infinity Cache (last-level, memory side)
 PAGE_BYTES = 64 * 128          # fp8 keys of one 64-token page
 # Algorithmic bytes the indexer kernel moves per kept page and row: the page's
 # keys, its scale, its block-table entry, its kept-list entry, 64 fp32 scores
@@ -83,6 +84,9 @@ def _args():
     ap.add_argument("--quantize-on-main", action="store_true",
                     help="run the query quantiser on the main stream after the predictor")
     ap.add_argument("--cpu-requests", type=int, default=160)
+    ap.add_argument("--pools", type=int, default=1,
+                    help="independently drawn key pools, round t reading pool t mod N, so that "
+                         "a small workload's keys do not stay in the 256 MB Infinity Cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--fidelity", choices=("ablation", "budgets", "predictors"), default=None,
@@ -195,12 +199,14 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None, acce
     return upd_done
 
 
-def _run_gpu(wl, keep_bps, steps, warmup, device):
+def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
     import torch
 
-    from workload import acceptances, positions
+    from workload import acceptances, make_pool, positions
 
     spin, pool, cfg, st, bufs, make_queries = _setup(wl, device)
+    # pool i is drawn as layer i's pool would be: same pattern, its own keys
+    pools = [pool] + [make_pool(wl, i, device=device) for i in range(1, n_pools)]
     T = warmup + steps
     if wl.rows == 1:
         qpos_all = (torch.arange(T, dtype=torch.int64) + (wl.ctx - T))[:, None].repeat(1, wl.batch)
@@ -213,7 +219,8 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
         acc = acceptances(wl)
         qpos_all = positions(wl, acc)[:T]
         acc_all = acc[:T].to(torch.int32).to(device)
-    qs = [make_queries(wl, pool, 0, t, qpos_all[t].tolist(), device=device) for t in range(T)]
+    qs = [make_queries(wl, pools[t % n_pools], 0, t, qpos_all[t].tolist(), device=device)
+          for t in range(T)]
     qpos_all = qpos_all.to(torch.int32).to(device)
     torch.cuda.synchronize()
     results = {}
@@ -225,8 +232,8 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
         acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
         for t in range(warmup):
             bufs["qpos"].copy_(qpos_all[t])
-            done = _round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep_bp, side, done,
-                          accepted=acc_of(t))
+            done = _round(spin, st, bufs, pools[t % n_pools], qs[t][0], qs[t][1], keep_bp, side,
+                          done, accepted=acc_of(t))
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
         torch.cuda.synchronize()
@@ -235,8 +242,8 @@ def _run_gpu(wl, keep_bps, steps, warmup, device):
         for t in range(steps):
             bufs["qpos"].copy_(qpos_all[warmup + t])
             q, w = qs[warmup + t]
-            done = _round(spin, st, bufs, pool, q, w, keep_bp, side, done, evs[t],
-                          accepted=acc_of(warmup + t))
+            done = _round(spin, st, bufs, pools[(warmup + t) % n_pools], q, w, keep_bp, side,
+                          done, evs[t], accepted=acc_of(warmup + t))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
@@ -765,7 +772,7 @@ def main():
     keeps = [keep_main] + [k for k in sweep if k != keep_main]
     if a.copy_calibration:
         _copy_calibration(device)
-    res = _run_gpu(wl, keeps, a.steps, a.warmup, device)
+    res = _run_gpu(wl, keeps, a.steps, a.warmup, device, max(1, a.pools))
 
     main_r = res[keep_main]
     per = main_r["per_us"]
@@ -778,6 +785,7 @@ def main():
     idx_flops = main_r["kept_pages"] * 64 * wl.rows * wl.heads * wl.head_dim * 2
     idx_bytes = main_r["kept_pages"] * (IDX_BYTES_PER_PAGE + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW)
     achieved = idx_bytes / (idx_us * 1e-6) / 1e9
+    key_ws = max(1, a.pools) * wl.pool_pages * (64 * wl.head_dim + 4)
     sweep_out = {}
     for k, r in res.items():
         iu = sum(r["per_us"]["indexer"]) / a.steps
@@ -809,7 +817,12 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "ctx": wl.ctx, "pages_per_request": wl.blocks,
                    "heads": wl.heads, "head_dim": wl.head_dim, "topk": wl.topk,
                    "target_sparsity_bp": a.sparsity_bp, "explore_bp": wl.explore_bp,
-                   "rows": wl.rows, "block_table": "shuffled" if wl.shuffle else "identity"},
+                   "rows": wl.rows, "block_table": "shuffled" if wl.shuffle else "identity",
+                   "key_pools": max(1, a.pools)},
+        # the keys the indexer can touch over the run; at or under the 256 MB
+        # Infinity Cache the indexer's figures are cache-resident, not HBM rates
+        "key_working_set_bytes": key_ws,
+        "cache_resident": key_ws <= MALL_BYTES,
         "indexer_tokens_per_s": tokens_per_step / (idx_us * 1e-6),
         "indexer_row_tokens_per_s": wl.rows * tokens_per_step / (idx_us * 1e-6),
         "indexer_roofline_tokens_per_s": HBM_PEAK_GBS * 1e9 / (
