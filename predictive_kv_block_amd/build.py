@@ -32,6 +32,10 @@ FLAGS = [
 ]
 SOURCES = ["spin_abi.cpp", "spin_state.hip", "spin_predict.hip", "spin_indexer.hip",
            "spin_topk.hip", "spin_update.hip", "spin_fidelity.hip", "spin_attention.hip"]
+# HBM probes of the indexer's access pattern (bench.py --ceilings only), a
+# library of their own so that libspin holds the method alone
+PROBE_SOURCES = ["spin_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libspin_probe.so")
 
 
 def _compile(src, build_dir=BUILD, extra=()):
@@ -45,16 +49,16 @@ def _compile(src, build_dir=BUILD, extra=()):
     return obj, errs.strip()
 
 
-def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, defines=()):
+def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, defines=(), sources=SOURCES):
     """Compile every HIP source and link the library (default: libspin.so next to
     this file); `defines` are extra -D macros for tuning experiments."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(build_dir, exist_ok=True)
     extra = [f"-D{d}" for d in defines]
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
+    jobs = jobs or min(len(sources), os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+        results = list(ex.map(lambda src: _compile(src, build_dir, extra), sources))
     for obj, msg in results:
         if msg and verbose:
             print(msg, file=sys.stderr)
@@ -68,9 +72,15 @@ def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, defines=()):
     return out
 
 
+def build_probe(verbose=False):
+    """Compile the HBM probe library (libspin_probe.so next to this file)."""
+    return build(verbose=verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
     a = ap.parse_args()
     print(build(a.jobs, a.verbose))
+    print(build_probe(a.verbose))
