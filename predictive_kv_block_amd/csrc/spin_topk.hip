@@ -211,6 +211,7 @@ struct FusedShared {
   uint32_t skey[kFusedCap];       // survivors in position order
   int spos[kFusedCap];
   int scan[kFusedWaves];
+  int wcount[kFusedWaves];        // survivors found by each wave
 };
 
 // Inverse of ord_key for keys of non-NaN floats (the key of +0 gives +0).
@@ -225,6 +226,16 @@ __device__ __forceinline__ int row_inclusive_sum(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
   x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
   x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave in lane order: the row
+// sums, then the last lane of row 0 added into rows 1 and 3 and the last lane
+// of row 1 into rows 2 and 3 (DPP row broadcasts; lanes of other rows add 0).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x = row_inclusive_sum(x);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
   return x;
 }
 
@@ -265,11 +276,12 @@ __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
   return total;
 }
 
-// Top-min(K, n) of the n entries sh.skey/spos[0..n) (keys > 0, position
-// order), ties to the lower index.  With `out`, their positions are written to
-// out[0..K) ascending and padded with -1; without, they are compacted in place
-// into sh.skey/spos[0..min(K, n)).  n <= kFusedCap.  Returns min(K, n).
-__device__ int lds_topk(FusedShared& sh, int n, int K, int32_t* out) {
+// Top-min(K, live) of the entries sh.skey/spos[0..n) in position order, of
+// which `live` have a key > 0 (key 0 marks an empty entry), ties to the lower
+// index.  With `out`, their positions are written to out[0..K) ascending and
+// padded with -1; without, they are compacted in place into
+// sh.skey/spos[0..min(K, live)).  n <= kFusedCap.  Returns min(K, live).
+__device__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out) {
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   uint32_t key[kFusedPerLane];
   int pos[kFusedPerLane];
@@ -279,9 +291,9 @@ __device__ int lds_topk(FusedShared& sh, int n, int K, int32_t* out) {
     key[i] = (s < n) ? sh.skey[s] : 0u;
     pos[i] = (s < n) ? sh.spos[s] : 0;
   }
-  uint32_t thr = 0;                              // n <= K: every entry
+  uint32_t thr = 0;                              // live <= K: every entry
   int n_eq = 0;
-  if (n > K) {
+  if (live > K) {
     uint32_t smin, smax;
     int tot;
     block_key_stats<kFusedThreads, kFusedPerLane>(key, sh.t, &tot, &smin, &smax);
@@ -327,7 +339,7 @@ __device__ int lds_topk(FusedShared& sh, int n, int K, int32_t* out) {
     eq_base += __popcll(eqb);
     out_base += __popcll(selb);
   }
-  const int m = min(n, K);
+  const int m = min(live, K);
   if (out)
     for (int i = m + tid; i < K; i += kFusedThreads) out[i] = -1;
   __syncthreads();
@@ -403,16 +415,19 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
       lowest = max(t1, 1u);
 
       // 2. candidate pages (maximum >= t1), listed in ascending kept order
-      // (page p = w*1024 + i*64 + l held by lane l)
+      // (page p = w*1024 + i*64 + l held by lane l).  With one value per page
+      // (lm = 0) the registers already hold these page maxima.
+      if (lm != 0) {
 #pragma unroll
-      for (int i = 0; i < kFusedPageLanes; ++i) {
-        const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
-        float v = -INFINITY;
-        if (p < cnt) {
-          const float4 x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
-          v = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+        for (int i = 0; i < kFusedPageLanes; ++i) {
+          const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
+          float v = -INFINITY;
+          if (p < cnt) {
+            const float4 x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
+            v = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
+          }
+          pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
         }
-        pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
       }
       int mine = 0;
 #pragma unroll
@@ -471,6 +486,14 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
             v[i] = *reinterpret_cast<const float4*>(sc + size_t(p) * kBlock + slot0);
           }
         };
+        // One pass counts each page's survivors and appends the survivors to
+        // the wave's slice sh.skey/spos[kSlice w, kSlice (w + 1)) in position
+        // order (lanes are in position order within a load, loads and
+        // batches ascend, and wave ranges follow one another), as long as
+        // they fit.  Gaps left in the slices hold key 0, which lds_topk reads
+        // as empty.
+        constexpr int kSlice = kFusedCap / kFusedWaves;              // 512
+        int wave_n = 0;                                              // this wave's survivors so far
         for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
           float4 v[kLoads];
           load_batch(c0, v);
@@ -478,14 +501,48 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
           for (int i = 0; i < kLoads; ++i) {
             int c, j;
             const int f = survivors(c0, i, v[i], &c, &j);
-            const int tot = row_inclusive_sum(__popc(f));
+            const int n = __popc(f);
+            const int tot = row_inclusive_sum(n);
             if ((l & 15) == 15 && c < c_hi) sh.pcount[c] = tot;
+            const int incl = wave_inclusive_sum(n);
+            int o = wave_n + incl - n;
+            const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              if (f & (1 << k)) {
+                if (o < kSlice) {
+                  sh.skey[kSlice * w + o] = ord_key(vals[k]);
+                  sh.spos[kSlice * w + o] = j * kBlock + slot0 + k;
+                }
+                ++o;
+              }
+            }
+            wave_n += __builtin_amdgcn_readlane(incl, kWave - 1);
           }
         }
+        if (l == 0) sh.wcount[w] = wave_n;
         __syncthreads();
-        const int nsurv = block_exclusive_scan(sh.pcount, ncand, sh.scan);
+        int nsurv = 0;
+        bool spilled = false;
+#pragma unroll
+        for (int i = 0; i < kFusedWaves; ++i) {
+          nsurv += sh.wcount[i];
+          spilled = spilled || sh.wcount[i] > kSlice;
+        }
         if (nsurv <= kFusedCap && nsurv >= K) {
-          // 4. collect them in position order (pages ascending, slots ascending)
+          if (!spilled) {
+            // 4. empty the rest of each slice, then rank the slices' entries
+            for (int x = wave_n + l; x < kSlice; x += kWave) {
+              sh.skey[kSlice * w + x] = 0u;
+              sh.spos[kSlice * w + x] = 0;
+            }
+            __syncthreads();
+            lds_topk(sh, kFusedCap, nsurv, K, out);
+            return;
+          }
+          // 4'. a wave found more than its slice holds: offsets from the
+          // per-page counts, and a second read collects the survivors packed
+          block_exclusive_scan(sh.pcount, ncand, sh.scan);
           for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
             float4 v[kLoads];
             load_batch(c0, v);
@@ -508,7 +565,7 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
           }
           __syncthreads();
           // 5. exact top-K of the survivors, written ascending
-          lds_topk(sh, nsurv, K, out);
+          lds_topk(sh, nsurv, nsurv, K, out);
           return;
         }
       }
@@ -582,9 +639,9 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
     }
     __syncthreads();
     n_run += want;
-    if (n_run > K) n_run = lds_topk(sh, n_run, K, nullptr);
+    if (n_run > K) n_run = lds_topk(sh, n_run, n_run, K, nullptr);
   }
-  lds_topk(sh, n_run, K, out);
+  lds_topk(sh, n_run, n_run, K, out);
 }
 
 // grid (rows, chunks of this level).
