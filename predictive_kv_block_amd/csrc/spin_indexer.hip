@@ -70,7 +70,7 @@ constexpr int kQStride = kDim + SPIN_IDX_QPAD;
 #endif
 constexpr int kFlushRows = SPIN_IDX_FLUSH_ROWS;
 #ifndef SPIN_IDX_FLUSH_ROWS_MR
-#define SPIN_IDX_FLUSH_ROWS_MR 32      // the same with several query rows
+#define SPIN_IDX_FLUSH_ROWS_MR 8       // the same with several query rows (small: 3 workgroups per CU)
 #endif
 constexpr int kFlushRowsMR = SPIN_IDX_FLUSH_ROWS_MR;
 #ifndef SPIN_IDX_MIN_PAGES_PER_WG
