@@ -127,7 +127,9 @@ typedef struct spin_batch {
  *   q8  [max_slots][max_rows][heads][head_dim] uint8   workspace: e4m3fn query codes
  *   wq  [max_slots][max_rows][heads]          workspace: w * 2^e
  *   qexp [max_slots][max_rows][heads] int32   workspace: query exponents e
- *   bscore [max_slots][max_rows][max_blocks]  workspace: block scores S
+ *   bscore [max_slots][max_rows][max_blocks]  workspace: block scores S (when several
+ *                                            rows build their own masks, each row's
+ *                                            block flags once its selection is done)
  *   ukey [max_slots][max_blocks] uint64       workspace: exploration keys
  *   page_qmax [max_slots][max_rows][max_blocks][4] workspace: per-page quarter maxima
  *   topk_ws                                   empty (= total): the state's top-k runs on

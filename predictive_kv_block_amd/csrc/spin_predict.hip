@@ -227,10 +227,15 @@ struct KeptSrc {
 // bit 2 predicted by the current row.  With RESIDENT, the row's block scores
 // and the exploration words also live in LDS (dynamic LDS = 13 B per block);
 // otherwise the selection reads them from the state's workspace.
+// grid (B) with per_row = 0: the workgroup runs every row of its request and
+// writes the union.  grid (B, R) with per_row = 1: workgroup (b, r) runs row r
+// alone and leaves its flags (bit 0 predicted, bit 1 explored; 0 past the
+// row's last block) as bytes in the row's block-score workspace, which it has
+// finished reading; k_select_union then forms the union.
 template <bool RESIDENT>
 __global__ void __launch_bounds__(kSelectThreads)
 k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32_t* kept_count,
-         uint8_t* flags_out) {
+         uint8_t* flags_out, int per_row) {
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
   __shared__ int s_scr[kSelectScratchInts];
   uint64_t* s_u = reinterpret_cast<uint64_t*>(s_dyn);
@@ -244,6 +249,7 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
   int32_t* ko = kept + size_t(b) * bt.max_blocks;
 
   if (!request_ok(v, bt, s, q0)) {
+    if (per_row) return;                         // k_select_union reports it
     for (int j = tid; j < bt.max_blocks; j += kSelectThreads) fo[j] = 0;
     if (tid == 0) {
       kept_count[b] = 0;
@@ -273,8 +279,9 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
   }
   __syncthreads();
 
-  const int mask_rows = v.mask_row0 ? 1 : bt.R;
-  for (int r = 0; r < mask_rows; ++r) {
+  const int r_begin = per_row ? int(blockIdx.y) : 0;
+  const int r_end = per_row ? r_begin + 1 : (v.mask_row0 ? 1 : bt.R);
+  for (int r = r_begin; r < r_end; ++r) {
     const int q = q0 + r;
     const int n = num_blocks_of(q);
     int kb, nexp;
@@ -317,8 +324,62 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
     __syncthreads();
   }
 
+  if (per_row) {
+    uint8_t* rf = reinterpret_cast<uint8_t*>(v.bscore + (size_t(b) * v.max_rows + r_begin) *
+                                                            v.max_blocks);
+    for (int j = tid; j < n_last; j += kSelectThreads) rf[j] = s_flags[j] & 3;
+    return;
+  }
   if (v.mask_row0)      // blocks only the later rows reach (the draft positions)
     for (int j = num_blocks_of(q0) + tid; j < n_last; j += kSelectThreads) s_flags[j] |= 1;
+  __syncthreads();
+  for (int j = tid; j < bt.max_blocks; j += kSelectThreads) {
+    uint8_t f = 0;
+    if (j < n_last) f = (s_flags[j] & 1) ? 1 : ((s_flags[j] & 2) ? 2 : 0);
+    fo[j] = f;
+  }
+  KeptSrc ksrc{s_flags};
+  const int total = ordered_emit<kSelectThreads, 2, uint32_t>(
+      ksrc, n_last, 0u, 0x7fffffff,
+      [&](int j, int rank) {
+        if (rank < bt.max_blocks) ko[rank] = j;
+      },
+      s_scr);
+  if (tid == 0) kept_count[b] = min(total, bt.max_blocks);
+}
+
+// grid (B), kSelectThreads threads, dynamic LDS = max_blocks bytes: the union
+// of the R rows' flags left by k_select in per-row mode (bit 0 predicted by
+// some row, else bit 1 explored), written as the block flags, and the kept
+// list compacted in ascending block order.
+__global__ void __launch_bounds__(kSelectThreads)
+k_select_union(SpinView v, spin_batch bt, int32_t* kept, int32_t* kept_count,
+               uint8_t* flags_out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_flags[];
+  __shared__ int s_scr[kSelectScratchInts];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int s = bt.slot[b];
+  const int q0 = bt.qpos[b];
+  uint8_t* fo = flags_out + size_t(b) * bt.max_blocks;
+  int32_t* ko = kept + size_t(b) * bt.max_blocks;
+  if (!request_ok(v, bt, s, q0)) {
+    for (int j = tid; j < bt.max_blocks; j += kSelectThreads) fo[j] = 0;
+    if (tid == 0) {
+      kept_count[b] = 0;
+      flag_error(v.err, (s < 0 || s >= v.S) ? SPIN_ERR_SLOT : SPIN_ERR_QPOS);
+    }
+    return;
+  }
+  const int n_last = num_blocks_of(q0 + bt.R - 1);
+  const uint8_t* rf = reinterpret_cast<const uint8_t*>(v.bscore + size_t(b) * v.max_rows *
+                                                                      v.max_blocks);
+  const size_t rstride = size_t(v.max_blocks) * 4;     // bytes between rows
+  for (int j = tid; j < n_last; j += kSelectThreads) {
+    uint8_t f = 0;
+    for (int r = 0; r < bt.R; ++r) f |= rf[r * rstride + j];
+    s_flags[j] = f;
+  }
   __syncthreads();
   for (int j = tid; j < bt.max_blocks; j += kSelectThreads) {
     uint8_t f = 0;
@@ -363,12 +424,19 @@ hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, in
       reinterpret_cast<const void*>(&k_select<true>), hipFuncAttributeMaxDynamicSharedMemorySize,
       int(kResidentLdsMax));
   if (resident_lds > 64 * 1024 && lds_opt_in != hipSuccess) return lds_opt_in;
+  // Several rows building their own masks (the union policy) run as one
+  // workgroup per (request, row), then one per request forms the union.
+  const int per_row = (!v.mask_row0 && bt.R > 1) ? 1 : 0;
+  const dim3 grid(unsigned(bt.B), per_row ? unsigned(bt.R) : 1u);
   if (resident_lds <= kResidentLdsMax)
-    hipLaunchKernelGGL(k_select<true>, dim3(bt.B), dim3(kSelectThreads), resident_lds, s, v,
-                       layer, bt, keep_bp, kept, kept_count, flags);
+    hipLaunchKernelGGL(k_select<true>, grid, dim3(kSelectThreads), resident_lds, s, v, layer, bt,
+                       keep_bp, kept, kept_count, flags, per_row);
   else
-    hipLaunchKernelGGL(k_select<false>, dim3(bt.B), dim3(kSelectThreads), size_t(bt.max_blocks),
-                       s, v, layer, bt, keep_bp, kept, kept_count, flags);
+    hipLaunchKernelGGL(k_select<false>, grid, dim3(kSelectThreads), size_t(bt.max_blocks), s, v,
+                       layer, bt, keep_bp, kept, kept_count, flags, per_row);
+  if (per_row)
+    hipLaunchKernelGGL(k_select_union, dim3(bt.B), dim3(kSelectThreads), size_t(bt.max_blocks),
+                       s, v, bt, kept, kept_count, flags);
   return hipGetLastError();
 }
 
