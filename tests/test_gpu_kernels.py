@@ -410,6 +410,36 @@ def test_measure_miss_parity(gpu_lib):
             assert abs(got[b, r] - O.miss_rate(full[b, r], flags[b])) < 1e-6
 
 
+def test_device_errors_flagged_with_per_row_selection(gpu_lib):
+    """Four rows building their own masks take the per-row selection and the
+    union kernel: a request with a bad slot or position is reported, gets no
+    kept blocks and zero flags, and the other request is still selected (its
+    first round keeps every block of its last row)."""
+    R = 4
+    cfg = spin.make_config(1, 2, 4096, 64, max_rows=R)
+    rig = Rig(cfg, 2, R, 64)
+    rig.reset([11, 12])
+    rig.slot.copy_(torch.tensor([0, 7], dtype=torch.int32))        # slot 7 >= max_slots
+    rig.set_qpos([100, 100])
+    _say("predict R=4 with a bad slot")
+    spin.spin_predict_blocks(rig.h, 0, rig.batch, 5000, rig.kept, rig.kept_count, rig.flags)
+    torch.cuda.synchronize()
+    assert rig.state.error() & spin.ERR_SLOT
+    assert int(rig.kept_count[1]) == 0
+    assert int(rig.flags[1].sum()) == 0
+    assert int(rig.kept_count[0]) == nblocks(100 + R - 1)
+    assert np.array_equal(np_(rig.kept[0, : nblocks(100 + R - 1)]), np.arange(nblocks(100 + R - 1)))
+    rig.slot.copy_(torch.tensor([0, 1], dtype=torch.int32))
+    rig.set_qpos([100, 4096 - 2])                                  # rows past max_ctx
+    _say("predict R=4 with a bad position")
+    spin.spin_predict_blocks(rig.h, 0, rig.batch, 5000, rig.kept, rig.kept_count, rig.flags)
+    torch.cuda.synchronize()
+    assert rig.state.error() & spin.ERR_QPOS
+    assert int(rig.kept_count[1]) == 0
+    assert int(rig.flags[1].sum()) == 0
+    assert int(rig.kept_count[0]) == nblocks(100 + R - 1)
+
+
 def test_device_errors_flagged_without_faults(gpu_lib):
     cfg = spin.make_config(1, 2, 4096, 64)
     rig = Rig(cfg, 2, 1, 64)
