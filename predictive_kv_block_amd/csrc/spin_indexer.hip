@@ -222,10 +222,10 @@ __device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
 // so every branch on it is wave-uniform.  Keys stream through a ring of
 // kStages register buffers: while page m is on the MFMAs, pages m+1 ..
 // m+kStages-1 are in flight.  Score rows are staged in LDS and written
-// kFlushRows/R pages at a time as one contiguous burst per row: single
-// 256-byte rows, each written long after its neighbours, reach HBM as
-// scattered partial-row writes that stall the key stream far more than their
-// share of the bytes.
+// kFlushRows pages (one row) or kFlushRowsMR/R pages (R rows) at a time as one
+// contiguous burst per row: single 256-byte rows, each written long after its
+// neighbours, reach HBM as scattered partial-row writes that stall the key
+// stream far more than their share of the bytes.
 template <int R>
 __global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
