@@ -434,9 +434,12 @@ hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, in
   else
     hipLaunchKernelGGL(k_select<false>, grid, dim3(kSelectThreads), size_t(bt.max_blocks), s, v,
                        layer, bt, keep_bp, kept, kept_count, flags, per_row);
-  if (per_row)
+  if (per_row) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_select_union, dim3(bt.B), dim3(kSelectThreads), size_t(bt.max_blocks),
                        s, v, bt, kept, kept_count, flags);
+  }
   return hipGetLastError();
 }
 
