@@ -372,8 +372,11 @@ hipError_t launch_attention(const spin_batch& bt, int topk, const int32_t* topk_
   a.ws_o = p.splits > 1 ? static_cast<uint16_t*>(ws) : nullptr;
   a.ws_lse = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ws_o_bytes) : nullptr;
   hipLaunchKernelGGL(k_attention, dim3(p.splits, p.rows), dim3(kAThreads), 0, s, a);
-  if (p.splits > 1)
+  if (p.splits > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attention_combine, dim3(p.rows, kCombineGroups), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

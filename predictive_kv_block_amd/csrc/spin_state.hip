@@ -54,14 +54,20 @@ unsigned grid_for(size_t n) {
 hipError_t launch_fill_state(const SpinView& v, hipStream_t s) {
   const size_t nv = size_t(v.L) * v.S * v.max_ctx;
   const size_t nb = size_t(v.L) * v.S * v.max_blocks;
-  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(nv)), dim3(256), 0, s, v.V, nv, -INFINITY);
-  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(nv)), dim3(256), 0, s, v.D, nv, -INFINITY);
-  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(nb)), dim3(256), 0, s, v.VB, nb, -INFINITY);
   const size_t ns = size_t(v.L) * v.S;
+  hipError_t e;
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(nv)), dim3(256), 0, s, v.V, nv, -INFINITY);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(nv)), dim3(256), 0, s, v.D, nv, -INFINITY);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_fill_f32, dim3(grid_for(nb)), dim3(256), 0, s, v.VB, nb, -INFINITY);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(ns)), dim3(256), 0, s,
                      reinterpret_cast<uint32_t*>(v.step), ns, 0u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(2 * size_t(v.S))), dim3(256), 0, s,
                      reinterpret_cast<uint32_t*>(v.rid), 2 * size_t(v.S), 0u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, s, reinterpret_cast<uint32_t*>(v.err),
                      size_t(1), 0u);
   return hipGetLastError();

@@ -876,8 +876,10 @@ hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, cons
       hipLaunchKernelGGL((k_topk_level<false, true>), grid, dim3(kTopkThreads), 0, s, a);
     else
       hipLaunchKernelGGL((k_topk_level<false, false>), grid, dim3(kTopkThreads), 0, s, a);
+    const hipError_t e = hipGetLastError();     // a failed level stops the chain
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_miss(const spin_batch& bt, int topk, const int32_t* full_topk,
