@@ -199,7 +199,13 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None, acce
     return upd_done
 
 
-def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
+def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1, modes=(False, True)):
+    """Per keep, and per timing mode in `modes`, `warmup` untimed rounds then
+    `steps` timed rounds.  Mode False (lean) records only the round's start,
+    the top-k's end and the update's end, so the round carries no other event
+    or marker: its step and wall times are the path's own.  Mode True
+    (detailed) brackets every stage with events (8 per round) for the per-stage
+    times.  Returns {keep: {mode: {...}}}."""
     import torch
 
     from workload import acceptances, make_pool, positions
@@ -225,44 +231,51 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
     torch.cuda.synchronize()
     results = {}
     side = torch.cuda.Stream(device=device)          # default priority
+    acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
     for keep_bp in keep_bps:
-        spin.spin_reset_slots(st.handle, bufs["slot"],
-                              torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
-        done = None
-        acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
-        for t in range(warmup):
-            bufs["qpos"].copy_(qpos_all[t])
-            done = _round(spin, st, bufs, pools[t % n_pools], qs[t][0], qs[t][1], keep_bp, side,
-                          done, accepted=acc_of(t))
-        torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        done = None
-        for t in range(steps):
-            bufs["qpos"].copy_(qpos_all[warmup + t])
-            q, w = qs[warmup + t]
-            done = _round(spin, st, bufs, pools[(warmup + t) % n_pools], q, w, keep_bp, side,
-                          done, evs[t], accepted=acc_of(warmup + t))
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
-        for e in evs:
-            per["predict"].append(e[0].elapsed_time(e[1]) * 1e3)       # us
-            per["quantize"].append(e[5].elapsed_time(e[6]) * 1e3)      # beside predict
-            per["indexer"].append(e[2].elapsed_time(e[3]) * 1e3)
-            per["topk"].append(e[3].elapsed_time(e[4]) * 1e3)
-            per["update"].append(e[3].elapsed_time(e[7]) * 1e3)        # from the indexer's end
-        # a round ends when both the top-k (main) and the update (side) are done
-        per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[7])) * 1e3 for e in evs]
-        # critical path to the top-k: predict, the wait for the quantiser, indexer, top-k
-        per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
-        cnt = bufs["cnt"].cpu()
-        kept_pages = int(cnt.sum())
-        if st.error() != 0:
-            raise RuntimeError(f"device error word {st.error()}")
-        results[keep_bp] = dict(wall_s=wall, per_us=per, kept_pages=kept_pages,
-                                blocks=wl.batch * wl.blocks)
+        results[keep_bp] = {}
+        for detail in modes:
+            spin.spin_reset_slots(st.handle, bufs["slot"],
+                                  torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
+            done = None
+            for t in range(warmup):
+                bufs["qpos"].copy_(qpos_all[t])
+                done = _round(spin, st, bufs, pools[t % n_pools], qs[t][0], qs[t][1], keep_bp,
+                              side, done, accepted=acc_of(t))
+            torch.cuda.synchronize()
+            evs = []
+            for _ in range(steps):
+                e = [None] * 8
+                for k in (range(8) if detail else (0, 4, 7)):
+                    e[k] = torch.cuda.Event(enable_timing=True)
+                evs.append(e)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            done = None
+            for t in range(steps):
+                bufs["qpos"].copy_(qpos_all[warmup + t])
+                q, w = qs[warmup + t]
+                done = _round(spin, st, bufs, pools[(warmup + t) % n_pools], q, w, keep_bp, side,
+                              done, evs[t], accepted=acc_of(warmup + t))
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
+            for e in evs if detail else []:
+                per["predict"].append(e[0].elapsed_time(e[1]) * 1e3)       # us
+                per["quantize"].append(e[5].elapsed_time(e[6]) * 1e3)      # beside predict
+                per["indexer"].append(e[2].elapsed_time(e[3]) * 1e3)
+                per["topk"].append(e[3].elapsed_time(e[4]) * 1e3)
+                per["update"].append(e[3].elapsed_time(e[7]) * 1e3)        # from the indexer's end
+            # a round ends when both the top-k (main) and the update (side) are done
+            per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[7])) * 1e3 for e in evs]
+            # critical path to the top-k: predict, the wait for the quantiser, indexer, top-k
+            per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
+            cnt = bufs["cnt"].cpu()
+            kept_pages = int(cnt.sum())
+            if st.error() != 0:
+                raise RuntimeError(f"device error word {st.error()}")
+            results[keep_bp][detail] = dict(wall_s=wall, per_us=per, kept_pages=kept_pages,
+                                            blocks=wl.batch * wl.blocks)
     return results
 
 
@@ -813,14 +826,16 @@ def main():
     keeps = [keep_main] + [k for k in sweep if k != keep_main]
     if a.copy_calibration:
         _copy_calibration(device)
-    res = _run_gpu(wl, keeps, a.steps, a.warmup, device, max(1, a.pools))
+    both = _run_gpu(wl, keeps, a.steps, a.warmup, device, max(1, a.pools))
+    res = {k: v[True] for k, v in both.items()}          # detailed: per-stage times
+    lean = both[keep_main][False]                        # lean: step, latency and wall
 
     main_r = res[keep_main]
     per = main_r["per_us"]
-    step_us = per["step"]
-    pit = per["to_topk"]
-    ms_per_step = main_r["wall_s"] * 1e3 / a.steps
-    tokens_per_step = main_r["kept_pages"] * 64
+    step_us = lean["per_us"]["step"]
+    pit = lean["per_us"]["to_topk"]
+    ms_per_step = lean["wall_s"] * 1e3 / a.steps
+    tokens_per_step = lean["kept_pages"] * 64
     value = tokens_per_step / (ms_per_step / 1e3)
     idx_us = sum(per["indexer"]) / a.steps
     idx_flops = main_r["kept_pages"] * 64 * wl.rows * wl.heads * wl.head_dim * 2
@@ -833,7 +848,7 @@ def main():
         sweep_out[str(10000 - k)] = {
             "kept_share": r["kept_pages"] / r["blocks"],
             "indexer_us": round(iu, 2),
-            "step_us_median": round(_median(r["per_us"]["step"]), 2),
+            "step_us_median": round(_median(both[k][False]["per_us"]["step"]), 2),
         }
     if "0" in sweep_out:
         base = sweep_out["0"]["indexer_us"]
@@ -878,6 +893,15 @@ def main():
                if n not in ("step", "to_topk")},
             "quantize_overlaps_predict": QUANTIZE_ON_SIDE,
             "update_overlaps_topk": True,
+            # the median, p10, p90, whole step and ms_per_step come from rounds
+            # that record 3 events each; the stage means, the sweep's indexer
+            # times and the roofline from the same rounds timed again with 8
+            # events each, whose own figures follow
+            "detailed_pass": {
+                "ms_per_step": round(main_r["wall_s"] * 1e3 / a.steps, 4),
+                "predict_index_topk_median": round(_median(per["to_topk"]), 2),
+                "whole_step_median": round(_median(per["step"]), 2),
+            },
         },
         "realized_block_sparsity": 1.0 - main_r["kept_pages"] / main_r["blocks"],
         "roofline": {"bound": "hbm", "kernel": "k_indexer", "achieved": round(achieved, 1),
