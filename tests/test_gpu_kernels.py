@@ -269,6 +269,8 @@ POOL_NAMES = {spin.SPIN_POOL_MAX: O.POOL_MAX, spin.SPIN_POOL_MEAN: O.POOL_MEAN,
     (1, 0, 500, 4, 200, 0), (2, 9990, 500, 5, 200, 0),
     # past the LDS-resident limit of the selection kernel: the workspace path
     (1, 5000, 500, 3, 12000, 0), (4, 6000, 1000, 2, 12000, 0),
+    # the MTP shape: 4 rows over 4096 blocks, each row selected by its own workgroup
+    (4, 5000, 1000, 2, 4096, 0),
     # the pages' ablation variants: Mean / Top-4 pooling, row-0 mask
     (1, 6000, 500, 3, 200, spin.SPIN_POOL_MEAN), (1, 5000, 1000, 2, 200, spin.SPIN_POOL_TOP4),
     (4, 5000, 1000, 2, 200, spin.SPIN_MASK_ROW0),
