@@ -240,6 +240,7 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   __shared__ float s_w[R * kHeads];
   __shared__ __attribute__((aligned(16))) float s_out[kIdxWaves * R * F * kBlock];
   __shared__ int s_seg[3 * kWave];
+  __shared__ __attribute__((aligned(16))) float s_qm[R == 1 ? kIdxWaves * F * 4 : 4];
 
   const int l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -274,6 +275,7 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   const int n16 = l & 15;     // M row of A / N column of B
   const int lane_off = n16 * kDim + g * 32;
   float* my_out = s_out + wave * (R * F * kBlock);
+  float* my_qm = s_qm + wave * (R * F * 4);
 
   // Walk the rows 64 at a time: lane l holds row r0 + l, its pages [start, end)
   // in the sequence; rows meeting [g0, g1) are this workgroup's segments.
@@ -372,7 +374,8 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
               my_out[(r * F + mf) * kBlock + l] = out;
               if (page_qmax) {
                 // maxima of the page's four 16-slot quarters (DPP row reduction;
-                // lane 16c + 15 holds quarter c), written as one 16-byte row
+                // lane 16c + 15 holds quarter c), one 16-byte row (staged in LDS
+                // with one query row)
                 float x = out;
                 x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
                                  __float_as_int(-INFINITY), __float_as_int(x), 0x111, 0xF, 0xF, false)));
@@ -382,12 +385,17 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
                                  __float_as_int(-INFINITY), __float_as_int(x), 0x114, 0xF, 0xF, false)));
                 x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(
                                  __float_as_int(-INFINITY), __float_as_int(x), 0x118, 0xF, 0xF, false)));
-                if ((l & 15) == 15)
-                  page_qmax[((size_t(b) * R + r) * mb + kw + m) * 4 + (l >> 4)] = x;
+                if ((l & 15) == 15) {
+                  if (R == 1)
+                    my_qm[(r * F + mf) * 4 + (l >> 4)] = x;
+                  else
+                    page_qmax[((size_t(b) * R + r) * mb + kw + m) * 4 + (l >> 4)] = x;
+                }
               }
             }
             if (mf == F - 1 || m + 1 == npages) {
-              // Flush pages m-mf .. m of every row: LDS -> one contiguous burst.
+              // Flush pages m-mf .. m of every row: LDS -> one contiguous burst of
+              // scores and one of quarter maxima.
               __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
               __builtin_amdgcn_wave_barrier();
               __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -407,6 +415,15 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
                     dst[x] = src[x];
 #endif
                   }
+                }
+                if (R == 1 && page_qmax && l <= mf) {
+                  // the pages' quarter maxima, one 16-byte row per page, written
+                  // together: with one query row, single 16-byte rows stored page
+                  // by page cost the key stream about 2% more (with several rows
+                  // the flushes come every few pages and the rows go out directly)
+                  v4f* qd = reinterpret_cast<v4f*>(page_qmax +
+                                                   ((size_t(b) * R + r) * mb + kw + m - mf) * 4);
+                  qd[l] = reinterpret_cast<const v4f*>(my_qm + r * F * 4)[l];
                 }
               }
               __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
