@@ -10,8 +10,9 @@
 //   - the 32 cache rows are gathered into LDS twice: row-major (the A
 //     operand of S^T = K Q^T) and transposed, with the tokens of each lane's
 //     MFMA k-group stored contiguously (the A operand of O^T += V^T P^T);
-//   - S^T comes out of 36 v_mfma_f32_32x32x16_bf16 with Q^T held in
-//     registers, so each lane holds 16 scores of one head;
+//   - S^T comes out of 36 v_mfma_f32_32x32x16_bf16 with Q^T held by each
+//     lane (28 of its 36 k-steps in registers, 8 in the lane's own LDS
+//     slots), so each lane holds 16 scores of one head;
 //   - the online softmax (base 2) turns them into bf16 weights that are
 //     already in the B-operand layout of the 32 PV MFMAs (registers 8ks..8ks+7
 //     are k-step ks), with no shuffle;
@@ -40,6 +41,12 @@ constexpr int kVRow = kAT + 8;                        // bf16 per transposed (ch
 constexpr int kChunks = kAttnDim / 8;                 // 16-byte chunks per cache row
 constexpr int kItems = (kAT / 4) * kChunks;           // (token quad, chunk) staging items
 constexpr int kItemsPerThread = (kItems + 255) / 256;
+constexpr int kQChunks = kAttnDim / 16;               // Q^T operand chunks (k-steps) per lane
+#ifndef SPIN_ATT_QREG
+#define SPIN_ATT_QREG 28
+#endif
+constexpr int kQReg = SPIN_ATT_QREG;                  // chunks held in registers, the rest in LDS
+constexpr int kQLds = kQChunks - kQReg;
 constexpr int kMaxShare = 4096;                       // top-k entries per share (<= topk)
 constexpr int kMaxShares = 16;                        // shares per row at most
 constexpr double kMergeCostPerShare = 0.008;          // merge cost of one share-row, in tile-times
@@ -89,6 +96,7 @@ k_attention(AttnArgs a) {
   __shared__ __align__(16) uint16_t s_vt[kAttnValueDim * kVRow];
   __shared__ int s_tok[kMaxShare];          // pool row of each entry of the share, -1 = skipped
   __shared__ uint32_t s_mask[kMaxShare / kAT];
+  __shared__ __align__(16) uint16_t s_q[kAWaves * (kQLds > 0 ? kQLds : 1) * kWave * 8];
 
   const int split = blockIdx.x, row = blockIdx.y;
   const int b = row / a.bt.R, r = row - b * a.bt.R;
@@ -100,12 +108,21 @@ k_attention(AttnArgs a) {
   const int e0 = split * a.chunk;
   const int e1 = min(a.K, e0 + a.chunk);
 
-  // Q^T operand: chunk c holds dims 16c + 8hg .. 16c + 8hg + 7 of this lane's head
-  bf16x8 qv[kAttnDim / 16];
+  // Q^T operand: chunk c holds dims 16c + 8hg .. 16c + 8hg + 7 of this lane's head.
+  // The first kQReg chunks stay in registers; each lane parks the others in
+  // its own 16-byte LDS slots.  Without that the kernel spills to scratch, and
+  // a scratch reload waits on the same in-order counter as the next tile's
+  // gather, which then never overlaps the MFMAs.
+  bf16x8 qv[kQReg];
   const uint16_t* qrow = a.q + (size_t(row) * kAttnHeads + head) * kAttnDim;
 #pragma unroll
-  for (int c = 0; c < kAttnDim / 16; ++c)
-    qv[c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * hg);
+  for (int c = 0; c < kQChunks; ++c) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * hg);
+    if (c < kQReg)
+      qv[c] = x;
+    else
+      *reinterpret_cast<bf16x8*>(&s_q[((w * kQLds + c - kQReg) * kWave + l) * 8]) = x;
+  }
 
   f32x16 acc[kAttnValueDim / 32];
 #pragma unroll
@@ -174,6 +191,10 @@ k_attention(AttnArgs a) {
     }
   };
 
+  // Every load so far (Q, the top-k entries, the block table) is complete
+  // before the tile loop, so that no wait inside it on one of them (in-order
+  // vmcnt) can also wait for the next tile's gather.
+  __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0); expcnt, lgkmcnt unchanged
   if (n_share > 0) issue(0);
   for (int t0 = 0; t0 < n_share; t0 += kAT) {
     const uint32_t vmask = s_mask[t0 / kAT];
@@ -185,9 +206,12 @@ k_attention(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = 0.0f;
 #pragma unroll
-      for (int c = 0; c < kAttnDim / 16; ++c) {
+      for (int c = 0; c < kQChunks; ++c) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&s_k[n * kKRow + 16 * c + 8 * hg]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qv[c], s, 0, 0, 0);
+        const bf16x8 qb =
+            c < kQReg ? qv[c < kQReg ? c : 0]
+                      : *reinterpret_cast<const bf16x8*>(&s_q[((w * kQLds + c - kQReg) * kWave + l) * 8]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, s, 0, 0, 0);
         if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
       }
 
