@@ -47,6 +47,10 @@ constexpr int kQChunks = kAttnDim / 16;               // Q^T operand chunks (k-s
 #endif
 constexpr int kQReg = SPIN_ATT_QREG;                  // chunks held in registers, the rest in LDS
 constexpr int kQLds = kQChunks - kQReg;
+#ifndef SPIN_ATT_MFMA_GROUP
+#define SPIN_ATT_MFMA_GROUP 6
+#endif
+constexpr int kMfmaGroup = SPIN_ATT_MFMA_GROUP;       // MFMAs between scheduling fences
 constexpr int kMaxShare = 4096;                       // top-k entries per share (<= topk)
 constexpr int kMaxShares = 16;                        // shares per row at most
 constexpr double kMergeCostPerShare = 0.008;          // merge cost of one share-row, in tile-times
@@ -212,7 +216,7 @@ k_attention(AttnArgs a) {
             c < kQReg ? qv[c < kQReg ? c : 0]
                       : *reinterpret_cast<const bf16x8*>(&s_q[((w * kQLds + c - kQReg) * kWave + l) * 8]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, s, 0, 0, 0);
-        if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
+        if (c % kMfmaGroup == kMfmaGroup - 1) __builtin_amdgcn_sched_barrier(0);   // bound the reads in flight
       }
 
       // online softmax in base 2; register i holds token 8(i/4) + 4hg + i%4
@@ -254,7 +258,7 @@ k_attention(AttnArgs a) {
           const bf16x8 va =
               *reinterpret_cast<const bf16x8*>(&s_vt[(32 * ct + n) * kVRow + 16 * ks + 8 * hg]);
           acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks], acc[ct], 0, 0, 0);
-          if (ks == 1 && (ct & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+          if ((2 * ct + ks) % kMfmaGroup == kMfmaGroup - 1) __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();              // the next tile overwrites s_k and s_vt
