@@ -708,9 +708,7 @@ def _ceilings(device, reps=10):
     of 4 GiB (a sum, row sums, and a matrix-vector product), a device copy
     (2 GiB read + 2 GiB written), and a gather of random 8 KB pages into a
     fresh output (the indexer's read pattern, with a write stream beside
-    it); then the probe kernels of libspin_probe.so, which gather the same
-    pages in the indexer's own layout and grid, with and without its score
-    write stream.  GB/s of bytes moved."""
+    it).  GB/s of bytes moved."""
     import torch
 
     def timed(fn):
@@ -743,46 +741,7 @@ def _ceilings(device, reps=10):
     t = timed(lambda: pages.index_select(0, idx))
     out["page_gather_GBps"] = round(2 * idx.numel() * 8192 / t / 1e9, 1)
     out["page_gather_read_GBps"] = round(idx.numel() * 8192 / t / 1e9, 1)
-    out.update(_probe_ceilings(pages, idx, timed))
     return out
-
-
-def _probe_ceilings(pages, idx, timed):
-    """The indexer's page gather alone, in its lane layout and grid
-    (libspin_probe.so): 393216 random 8 KB pages of the 6 GiB pool, read only,
-    then with one streaming 256-byte row written per page (the score write
-    stream, 3% of the bytes)."""
-    import ctypes
-
-    import torch
-
-    from predictive_kv_block_amd.build import PROBE_LIB
-
-    lib = ctypes.CDLL(PROBE_LIB)
-    fn = lib.spin_probe_page_read
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
-                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                   ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p]
-    fn.restype = ctypes.c_int
-    lst = idx.to(torch.int32).contiguous()
-    n = lst.numel()
-    rows = torch.empty(n, 64, dtype=torch.float32, device=pages.device)
-    sink = torch.empty(1 << 20, dtype=torch.float32, device=pages.device)
-    waves = ctypes.c_int64()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-
-    def run(with_rows):
-        rc = fn(ctypes.c_void_p(pages.data_ptr()), pages.shape[0], ctypes.c_void_p(lst.data_ptr()),
-                n, ctypes.c_void_p(rows.data_ptr() if with_rows else None),
-                ctypes.c_void_p(sink.data_ptr()), sink.numel(), ctypes.byref(waves), stream)
-        if rc != 0:
-            raise RuntimeError(f"spin_probe_page_read: HIP error {rc}")
-
-    t_read = timed(lambda: run(False))
-    t_rw = timed(lambda: run(True))
-    return {"probe_page_read_GBps": round(n * 8192 / t_read / 1e9, 1),
-            "probe_page_read_plus_rows_GBps": round(n * (8192 + 256) / t_rw / 1e9, 1),
-            "probe_pages": n, "probe_waves": int(waves.value)}
 
 
 def _copy_calibration(device):

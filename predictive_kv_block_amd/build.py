@@ -32,10 +32,6 @@ FLAGS = [
 ]
 SOURCES = ["spin_abi.cpp", "spin_state.hip", "spin_predict.hip", "spin_indexer.hip",
            "spin_topk.hip", "spin_update.hip", "spin_fidelity.hip", "spin_attention.hip"]
-# HBM probes of the indexer's access pattern (bench.py --ceilings only), a
-# library of their own so that libspin holds the method alone
-PROBE_SOURCES = ["spin_probe.hip"]
-PROBE_LIB = os.path.join(PKG, "libspin_probe.so")
 
 
 def _compile(src, build_dir=BUILD, extra=()):
@@ -72,15 +68,9 @@ def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, defines=(), source
     return out
 
 
-def build_probe(verbose=False):
-    """Compile the HBM probe library (libspin_probe.so next to this file)."""
-    return build(verbose=verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
-
-
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
     a = ap.parse_args()
     print(build(a.jobs, a.verbose))
-    print(build_probe(a.verbose))

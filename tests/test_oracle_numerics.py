@@ -101,3 +101,82 @@ def test_ema_weights_are_fp32_values():
     assert a == float(np.float32(0.9)) and b == float(np.float32(np.float32(1) - np.float32(0.9)))
     assert abs(a + b - 1.0) < 1e-7
     assert math.isclose(b, 0.1, rel_tol=1e-6)
+
+
+def _plain_scores(qv, wv, keys):
+    """sum_h wv[h] * max(0, sum_d qv[h][d] * keys[t][d]) for every token t, in
+    plain Python loops (the DSA indexer formula written out)."""
+    out = []
+    for t in range(len(keys)):
+        s = 0.0
+        for h in range(len(qv)):
+            dot = 0.0
+            for d in range(len(keys[t])):
+                dot += float(qv[h][d]) * float(keys[t][d])
+            s += float(wv[h]) * max(dot, 0.0)
+        out.append(s)
+    return np.array(out)
+
+
+def _smallest_exponent(amax):
+    """Smallest integer k with amax * 2**-k <= 448, in exact rational arithmetic."""
+    from fractions import Fraction
+    a = Fraction(amax)
+    k = -200
+    while a / Fraction(2) ** k > 448:
+        k += 1
+    assert a / Fraction(2) ** (k - 1) > 448 or a == 0
+    return k
+
+
+def test_fp8_query_operands_exponent_weights_and_scores():
+    """fp8_query_operands returns the decoded codes q8 and w' = w * 2**e with e
+    the per-(row, head) exponent of the query quantisation: the score of
+    (q8, w') must equal that of (q8 * 2**e, w) -- the queries at their own
+    scale -- and stay within the e4m3fn rounding bound of the bf16-query
+    score.  A sign slip in e (w * 2**-e) would move every score by 2**(2e)."""
+    rng = np.random.default_rng(11)
+    R, H, d, T = 2, 6, 16, 9
+    q = rng.standard_normal((R, H, d))
+    # head magnitudes 2**-30 .. 2**30 so no exponent is 0; one head with a
+    # single large entry (the others fall into the e4m3fn subnormals)
+    q *= np.exp2(rng.integers(-30, 31, (R, H, 1)).astype(np.float64))
+    q[1, 2, :] *= 1e-3
+    q[1, 2, 5] = 3.0e4
+    q = torch.tensor(q, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    w = rng.uniform(-1.5, 1.5, (R, H))
+    w = w.astype(np.float32).astype(np.float64)
+    keys = rng.standard_normal((T, d))
+
+    q8, wv, codes, e = O.fp8_query_operands(q, w)
+    assert q8.shape == q.shape and wv.shape == w.shape and e.shape == w.shape
+    for r in range(R):
+        for h in range(H):
+            k = _smallest_exponent(np.abs(q[r, h]).max())
+            assert e[r, h] == k != 0
+            assert wv[r, h] / w[r, h] == 2.0 ** k           # exact: w' = w * 2**e
+            # the codes are the RNE e4m3fn codes of q * 2**-e, and q8 their values
+            assert np.array_equal(codes[r, h], _torch_e4m3(q[r, h] * 2.0 ** -k))
+            assert np.array_equal(q8[r, h], O.E4M3FN[codes[r, h]])
+            # rounding bound of e4m3fn at scale 2**e: half an ulp of a normal
+            # (2**-4 relative) or of the subnormal spacing (2**-10 absolute)
+            err = np.abs(q8[r, h] * 2.0 ** k - q[r, h])
+            assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(q[r, h]), 2.0 ** (k - 10)))
+
+    for r in range(R):
+        scaled_q = q8[r] * np.exp2(e[r].astype(np.float64))[:, None]
+        a = _plain_scores(q8[r], wv[r], keys)
+        b = _plain_scores(scaled_q, w[r], keys)
+        assert np.allclose(a, b, rtol=1e-12, atol=0)
+        # against the bf16-query score: ReLU is 1-Lipschitz, so the gap is at
+        # most sum_h |w_h| sum_d |q8*2**e - q| |k|
+        exact = _plain_scores(q[r], w[r], keys)
+        bound = np.array([sum(abs(w[r, h]) * np.dot(np.abs(scaled_q[h] - q[r, h]), np.abs(keys[t]))
+                              for h in range(H)) for t in range(T)])
+        assert np.all(np.abs(a - exact) <= bound * (1 + 1e-9) + 1e-300)
+        # the oracle's indexer formula on these operands gives the same scores
+        table = np.arange(1)
+        kv = np.zeros((1, 64, d))
+        kv[0, :T] = keys
+        s = O.indexer_scores(q8[r][None], wv[r][None], kv, np.ones(1), table, [0], 63)
+        assert np.allclose(s[0, :T], a, rtol=1e-12, atol=1e-300)
