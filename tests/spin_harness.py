@@ -132,3 +132,36 @@ def pool_values(pool, pages=None):
     codes = pool.key_codes if pages is None else pool.key_codes[pages]
     sc = pool.key_scale if pages is None else pool.key_scale[pages]
     return O.e4m3fn_decode(np_(codes)), np_(sc).astype(np.float64)
+
+
+def sync_from_oracle(rig, layer, b, ost, lockstep=False):
+    """Set GPU slot b of `layer` to the oracle's state rounded to fp32 (V, D,
+    VB = block max of V, step).  Data flows oracle -> GPU only.  With
+    `lockstep` the oracle's own state is rounded to the same fp32 values, so
+    both sides start the next round from identical numbers."""
+    V32 = ost.V.astype(np.float32)
+    D32 = ost.D.astype(np.float32)
+    if lockstep:
+        ost.V[:] = V32.astype(np.float64)
+        ost.D[:] = D32.astype(np.float64)
+    rig.inject(layer, b, V32, D32, ost.step)
+
+
+def predicted_sets_tie_only(ost_before, q, R, keep_bp, explore_bp, gpu_pred, ref_pred, rel=2e-3):
+    """True if the predicted block sets differ and every block in their
+    symmetric difference lies, for at least one row r, within `rel` of that
+    row's predicted-set threshold (the P-th largest block score from the
+    oracle's state before the round): an fp32-vs-fp64 tie, not an error."""
+    from oracle import spin_oracle as O
+    gp, rp = set(gpu_pred), set(ref_pred)
+    if gp == rp:
+        return False
+    near = set()
+    for r in range(R):
+        S = O.block_scores(ost_before.V, ost_before.D, q + r)
+        kb, ne, p = O.budget(keep_bp, len(S), explore_bp)
+        if kb >= len(S) or p == 0:
+            continue
+        theta = np.sort(S)[::-1][p - 1]
+        near |= {j for j in gp ^ rp if j < len(S) and abs(S[j] - theta) <= rel * abs(theta)}
+    return near == gp ^ rp

@@ -1,0 +1,169 @@
+"""Full-size MTP parity: 4 query rows, batch 32, 256K context, in the launch
+configuration the benchmark times for that workload (the 4-row indexer on the
+resident-clamped grid with its page quarter maxima, the quarter-maxima top-k,
+the prefix-valid replay), two layers with their own keys and state.  Sampled
+requests are checked against the oracle, which runs the same rounds from its
+own state: a warm-up round, then two rounds at 50% target sparsity with the
+workload's seeded acceptances.
+
+When a sampled request meets a tolerated tie at the selection threshold, the
+oracle's state rounded to fp32 is written into that GPU slot (data flows
+oracle -> GPU only) and the request stays in the comparison.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import predictive_kv_block_amd as spin
+from oracle import spin_oracle as O
+from tests.spin_harness import (assert_scores_close, assert_topk_tie_aware, np_,
+                                oracle_fp8_operands, predicted_sets_tie_only, score_mag,
+                                score_tol, sync_from_oracle)
+from workload import WORKLOADS, acceptances, make_pool, make_queries, positions
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SAMPLE = (0, 17, 31)
+LAYERS = 2
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+class _RigView:
+    """The pieces of a state that sync_from_oracle writes (V, D, VB, step)."""
+
+    def __init__(self, st):
+        self.state = st
+
+    def inject(self, layer, b, V, D, step):
+        Vs, Ds, VBs, St = self.state.V(), self.state.D(), self.state.VB(), self.state.step()
+        Vs[layer, b] = torch.as_tensor(V, dtype=torch.float32)
+        Ds[layer, b] = torch.as_tensor(D, dtype=torch.float32)
+        nb = self.state.layout["max_blocks"]
+        VBs[layer, b] = Vs[layer, b].view(nb, 64).amax(dim=1)
+        St[layer, b] = int(step)
+
+
+def _request_slice(pool, b):
+    """Request b's own pages decoded (fp64), their scales and its remapped table."""
+    pages = np_(pool.block_table[b]).astype(np.int64)
+    used = np.unique(pages)
+    sel = torch.as_tensor(used, device=DEV)
+    kv = O.e4m3fn_decode(np_(pool.key_codes[sel]))
+    sc = np_(pool.key_scale[sel]).astype(np.float64)
+    remap = np.full(int(pages.max()) + 1, -1, dtype=np.int64)
+    remap[used] = np.arange(len(used))
+    return kv, sc, remap[pages]
+
+
+@pytest.mark.timeout(900)
+def test_mtp_ctx256k_b32_sampled(gpu_lib):
+    wl = dataclasses.replace(WORKLOADS["mtp-ctx256k-b32"], layers=LAYERS)
+    B, R, nb = wl.batch, wl.rows, wl.blocks
+    acc = np_(acceptances(wl))
+    qp = np_(positions(wl, torch.as_tensor(acc)))
+    cfg = spin.make_config(LAYERS, B, wl.ctx, wl.topk, max_rows=R, explore_bp=wl.explore_bp,
+                           alpha=wl.alpha)
+    st = spin.SpinState(cfg)
+    slot = torch.arange(B, dtype=torch.int32, device=DEV)
+    rids = torch.arange(B, dtype=torch.int64, device=DEV) + 3000
+    spin.spin_reset_slots(st.handle, slot, rids)
+    qpos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    batch = spin.make_batch(slot, qpos, R, nb)
+    kept = torch.zeros(B, nb, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(B, dtype=torch.int32, device=DEV)
+    flags = torch.zeros(B, nb, dtype=torch.uint8, device=DEV)
+    scores = torch.empty(B, R, nb * 64, device=DEV)
+    pq = torch.empty(B, R, nb, 4, device=DEV)
+    topk = torch.empty(B, R, wl.topk, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(256, spin.spin_topk_workspace_bytes(batch, wl.topk)), dtype=torch.uint8,
+                     device=DEV)
+    view = _RigView(st)
+
+    pools, slices = [], []
+    for layer in range(LAYERS):
+        _say("generating the 256K x 32 pool of layer", layer)
+        pools.append(make_pool(wl, layer, device=DEV))
+        slices.append({b: _request_slice(pools[layer], b) for b in SAMPLE})
+    osts = [{b: O.RequestState(wl.ctx, request_id=3000 + b) for b in SAMPLE}
+            for _ in range(LAYERS)]
+    mag_max = [{b: 0.0 for b in SAMPLE} for _ in range(LAYERS)]
+    compared = ties = 0
+    for t, keep_bp in enumerate((10000, 5000, 5000)):
+        qpos.copy_(torch.as_tensor(qp[t].astype(np.int32)))
+        a_dev = torch.as_tensor(acc[t].astype(np.int32), device=DEV)
+        for layer in range(LAYERS):
+            pool = pools[layer]
+            qb, w = make_queries(wl, pool, layer, t, qp[t], device=DEV)
+            _say("round", t, "layer", layer, "keep_bp", keep_bp)
+            spin.spin_predict_blocks(st.handle, layer, batch, keep_bp, kept, cnt, flags)
+            spin.spin_quantize_q(st.handle, batch, qb, w)
+            spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale,
+                                     pool.block_table, kept, cnt, scores, pq)
+            spin.spin_topk_scores(batch, wl.topk, scores, kept, cnt, topk, ws, pq)
+            # the replay reads the scores and kept lists and writes only the state
+            spin.spin_mtp_replay(st.handle, layer, batch, a_dev, scores, kept, cnt)
+            torch.cuda.synchronize()
+            g_cnt = np_(cnt)
+            g_topk = np_(topk)
+            if keep_bp == 5000:
+                # the union of the 4 rows' masks keeps at least row 0's
+                # K_b = ceil(0.5 N_0) blocks and at most the last row's N
+                n0 = qp[t] // 64 + 1
+                n_last = (qp[t] + R - 1) // 64 + 1
+                assert np.all(g_cnt >= (5000 * n0 + 9999) // 10000) and np.all(g_cnt <= n_last)
+            for b in SAMPLE:
+                kv, sc, table = slices[layer][b]
+                qv, wv, _, _ = oracle_fp8_operands(qb[b], w[b])
+                before = osts[layer][b].copy()
+                ref = O.decode_round(osts[layer][b], int(qp[t, b]), R, keep_bp, wl.explore_bp,
+                                     cfg.seed, layer, qv, wv, kv, sc, table, wl.topk, wl.alpha,
+                                     accepted=int(acc[t, b]))
+                n = int(g_cnt[b])
+                gk = np_(kept[b, :n]).astype(np.int64)
+                gflags = np_(flags[b])[: len(ref["flags"])]
+                if not (np.array_equal(gk, ref["kept"]) and np.array_equal(gflags, ref["flags"])):
+                    # fp32 vs fp64 state: only a tie at a row's predicted-set threshold
+                    gp = set(np.nonzero(gflags == 1)[0].tolist())
+                    rp = set(np.nonzero(ref["flags"] == 1)[0].tolist())
+                    assert gp != rp, f"round {t} layer {layer} b{b}: exploration differs"
+                    assert predicted_sets_tie_only(before, int(qp[t, b]), R, keep_bp,
+                                                   wl.explore_bp, gp, rp), \
+                        f"round {t} layer {layer} b{b}: kept differ beyond a tie"
+                    _say("tolerated threshold tie", t, layer, b, "-> oracle state synced")
+                    sync_from_oracle(view, layer, b, osts[layer][b])
+                    ties += 1
+                    continue
+                mag = score_mag(qv, wv, kv, sc, table, gk)
+                mag_max[layer][b] = max(mag_max[layer][b], float(mag.max()))
+                gs = np_(scores[b, :, : n * 64]).astype(np.float64)
+                assert_scores_close(gs, ref["scores"], mag, f"round {t} layer {layer} b{b}")
+                slots = (gk[:, None] * 64 + np.arange(64)).reshape(-1)
+                for r in range(R):
+                    rs = dict(zip(slots.tolist(), ref["scores"][r].tolist()))
+                    mg = dict(zip(slots.tolist(), mag[r].tolist()))
+                    assert_topk_tie_aware(g_topk[b, r], ref["topk"][r], lambda x: rs[x],
+                                          lambda x: score_tol(rs[x], mg[x]),
+                                          f"round {t} layer {layer} b{b} row {r}")
+                    # quarter maxima the indexer wrote are those of its own scores
+                    own = np_(scores[b, r, : n * 64]).reshape(n, 4, 16).max(axis=2)
+                    assert np.array_equal(np_(pq[b, r, :n]), own)
+                compared += 1
+            for b in SAMPLE:
+                o = osts[layer][b]
+                scale = max(float(np.max(np.abs(o.V[np.isfinite(o.V)]))), mag_max[layer][b])
+                for name, g, r in (("V", np_(st.V()[layer, b]), o.V), ("D", np_(st.D()[layer, b]), o.D)):
+                    g = g.astype(np.float64)
+                    fin = np.isfinite(r)
+                    assert np.array_equal(fin, np.isfinite(g)), (name, t, layer, b)
+                    assert np.all(np.abs(g[fin] - r[fin]) <= np.maximum(1e-3 * np.abs(r[fin]),
+                                                                        1e-5 * scale)), \
+                        (name, t, layer, b)
+                assert int(st.step()[layer, b]) == o.step
+    assert st.error() == 0
+    _say("requests compared", compared, "ties", ties)
+    assert compared + ties == 3 * LAYERS * len(SAMPLE) and compared >= 2 * LAYERS * len(SAMPLE)

@@ -1,10 +1,18 @@
-"""Whole SPIN rounds on the GPU against the oracle, free-running.
+"""Whole SPIN rounds on the GPU against the oracle.
 
-The GPU and the oracle each evolve their own state from the same generated
-inputs (the oracle never takes a value from the GPU).  Each round compares
-kept blocks (exact, or a tie at the selection threshold within tolerance, after
-which the trajectories legitimately part and the comparison stops), indexer
-scores, top-k (tie-aware) and the EMA state.
+Free-running: the GPU and the oracle each evolve their own state from the same
+generated inputs.  Each round compares kept blocks (exact, or a tie at the
+selection threshold within tolerance), indexer scores, top-k (tie-aware) and
+the EMA state.  After a tolerated tie the two trajectories legitimately part:
+the oracle's state, rounded to fp32, is then written into that GPU slot and
+the comparison goes on from the next round.
+
+Lockstep: before every round the oracle's state is rounded to fp32 on both
+sides, so the predictor starts from identical values and its block selection
+must match exactly in every round.
+
+Data only ever flows oracle -> GPU; the oracle never takes a value from the
+GPU.
 """
 import dataclasses
 
@@ -15,7 +23,8 @@ import torch
 import predictive_kv_block_amd as spin
 from oracle import spin_oracle as O
 from tests.spin_harness import (NEG, Rig, assert_scores_close, assert_topk_tie_aware, nblocks,
-                                np_, oracle_fp8_operands, score_mag, score_tol)
+                                np_, oracle_fp8_operands, predicted_sets_tie_only, score_mag,
+                                score_tol, sync_from_oracle)
 from workload import WORKLOADS, acceptances, make_pool, make_queries, positions
 
 pytestmark = pytest.mark.gpu
@@ -35,21 +44,10 @@ def _state_close(g, r, scale, what):
 
 
 def _predicted_sets_tie_only(ost_before, q, R, keep_bp, explore_bp, gpu_flags, ref_flags):
-    """True if every predicted-set difference sits within tolerance of the threshold."""
-    gp = set(np.nonzero(gpu_flags == 1)[0].tolist())
-    rp = set(np.nonzero(ref_flags == 1)[0].tolist())
-    if gp == rp:
-        return False
-    for r in range(R):
-        S = O.block_scores(ost_before.V, ost_before.D, q + r)
-        kb, ne, p = O.budget(keep_bp, len(S), explore_bp)
-        if kb >= len(S) or p == 0:
-            continue
-        theta = np.sort(S)[::-1][p - 1]
-        for j in gp ^ rp:
-            if j < len(S) and abs(S[j] - theta) > 2e-3 * abs(theta):
-                return False
-    return True
+    """True if every predicted-set difference sits within tolerance of a row's threshold."""
+    return predicted_sets_tie_only(ost_before, q, R, keep_bp, explore_bp,
+                                   np.nonzero(gpu_flags == 1)[0].tolist(),
+                                   np.nonzero(ref_flags == 1)[0].tolist())
 
 
 # ---------------------------------------------------------------- tiny 4K
@@ -68,7 +66,7 @@ def test_tiny4k_trajectory_with_oracle_scores(gpu_lib):
     rig.reset([7])
     ost = O.RequestState(wl.ctx, request_id=7)
     qp = np_(positions(wl))[:, 0]
-    compared = 0
+    compared = ties = 0
     for t in range(wl.steps):
         q = int(qp[t])
         qf, w = make_queries(wl, pool, 0, t, [q])
@@ -85,7 +83,10 @@ def test_tiny4k_trajectory_with_oracle_scores(gpu_lib):
             assert _predicted_sets_tie_only(before, q, 1, kb, wl.explore_bp,
                                             np_(rig.flags[0])[: len(ref["flags"])], ref["flags"]), \
                 f"round {t}: kept blocks differ beyond a threshold tie"
-            break
+            _say("tolerated threshold tie: round", t, "-> oracle state synced")
+            sync_from_oracle(rig, 0, 0, ost)
+            ties += 1
+            continue
         sc = np.full((1, 1, wl.blocks * 64), NEG, dtype=np.float32)
         sc[0, 0, : len(gk) * 64] = ref["scores"][0].astype(np.float32)
         rig.scores.copy_(torch.as_tensor(sc))
@@ -103,12 +104,13 @@ def test_tiny4k_trajectory_with_oracle_scores(gpu_lib):
         _state_close(gD, ost.D, scale, f"D round {t}")
         assert gstep == ost.step
         compared += 1
-    _say("tiny4k rounds compared", compared)
-    assert compared >= 8
+    _say("tiny4k rounds compared", compared, "ties", ties)
+    assert compared + ties == wl.steps and compared >= 21
 
 
 # ------------------------------------------------------- 9.7K fp8 indexer
-def _run_rounds(wl, keep_bps, n_rounds, B=None, layer=0, check_state=True):
+def _run_rounds(wl, keep_bps, n_rounds, B=None, layer=0, check_state=True, lockstep=False):
+    """Returns (rounds compared in full, tolerated ties)."""
     B = B or wl.batch
     wl = dataclasses.replace(wl, batch=B)
     pool = make_pool(wl, layer, device=DEV)
@@ -120,14 +122,16 @@ def _run_rounds(wl, keep_bps, n_rounds, B=None, layer=0, check_state=True):
     rids = [500 + b for b in range(B)]
     rig.reset(rids)
     osts = [O.RequestState(wl.ctx, request_id=rids[b]) for b in range(B)]
-    live = [True] * B
     qp = np_(positions(wl))
-    compared = 0
+    compared = ties = 0
     for t in range(n_rounds):
         kb = keep_bps[t % len(keep_bps)] if t > 0 else 10000
         q = qp[t]
         qb, w = make_queries(wl, pool, layer, t, q, device=DEV)
         rig.set_qpos(q)
+        if lockstep and t > 0:
+            for b in range(B):
+                sync_from_oracle(rig, layer, b, osts[b], lockstep=True)
         spin.spin_predict_blocks(rig.h, layer, rig.batch, kb, rig.kept, rig.kept_count, rig.flags)
         spin.spin_indexer_topk(rig.h, rig.batch, qb, w, pool.key_codes, pool.key_scale,
                                pool.block_table, rig.kept, rig.kept_count, rig.scores, rig.topk)
@@ -137,19 +141,20 @@ def _run_rounds(wl, keep_bps, n_rounds, B=None, layer=0, check_state=True):
         spin.spin_update(rig.h, layer, rig.batch, rig.scores, rig.kept, rig.kept_count)
         torch.cuda.synchronize()
         for b in range(B):
-            if not live[b]:
-                continue
             qv, wv, _, _ = oracle_fp8_operands(qb[b], w[b])
             before = osts[b].copy()
             ref = O.decode_round(osts[b], int(q[b]), 1, kb, wl.explore_bp, cfg.seed, layer, qv,
                                  wv, kv, scv, tables[b], wl.topk, wl.alpha)
             gk = rig.kept_list(b)
-            if not np.array_equal(gk, ref["kept"]):
+            gflags = np_(rig.flags[b])[: len(ref["flags"])]
+            if not (np.array_equal(gk, ref["kept"]) and np.array_equal(gflags, ref["flags"])):
+                assert not lockstep, f"round {t} b{b}: kept blocks differ from identical states"
                 assert _predicted_sets_tie_only(before, int(q[b]), 1, kb, wl.explore_bp,
                                                 np_(rig.flags[b])[: len(ref["flags"])],
                                                 ref["flags"]), f"round {t} b{b}: kept differ"
-                _say("tolerated threshold tie: round", t, "request", b)
-                live[b] = False
+                _say("tolerated threshold tie: round", t, "request", b, "-> oracle state synced")
+                sync_from_oracle(rig, layer, b, osts[b])
+                ties += 1
                 continue
             n = len(gk) * 64
             mag = score_mag(qv, wv, kv, scv, tables[b], gk)
@@ -167,21 +172,35 @@ def _run_rounds(wl, keep_bps, n_rounds, B=None, layer=0, check_state=True):
                 assert gstep == osts[b].step
             compared += 1
     assert rig.state.error() == 0
-    return compared
+    return compared, ties
 
 
 def test_ctx9k_trajectory(gpu_lib):
     wl = WORKLOADS["ctx9k-b1"]
     _say("ctx9k-b1 rounds at 20/30/40/50%")
-    n = _run_rounds(wl, [8000, 7000, 6000, 5000], 12)
-    assert n >= 6
+    n, ties = _run_rounds(wl, [8000, 7000, 6000, 5000], 12)
+    assert n + ties == 12 and n >= 8
+
+
+def test_ctx9k_trajectory_lockstep(gpu_lib):
+    wl = WORKLOADS["ctx9k-b1"]
+    _say("ctx9k-b1 lockstep rounds at 20/30/40/50%")
+    n, ties = _run_rounds(wl, [8000, 7000, 6000, 5000], 16, lockstep=True)
+    assert n == 16 and ties == 0
 
 
 def test_ctx94k_trajectory_two_requests(gpu_lib):
     wl = WORKLOADS["ctx94k-b8"]
     _say("ctx94k two requests, 50%")
-    n = _run_rounds(wl, [5000], 4, B=2)
-    assert n >= 4
+    n, ties = _run_rounds(wl, [5000], 6, B=2)
+    assert n + ties == 12 and n >= 8
+
+
+def test_ctx94k_lockstep_three_requests(gpu_lib):
+    wl = WORKLOADS["ctx94k-b8"]
+    _say("ctx94k three requests lockstep, 30/50%")
+    n, ties = _run_rounds(wl, [3000, 5000], 6, B=3, lockstep=True)
+    assert n == 18 and ties == 0
 
 
 def test_determinism_bit_identical(gpu_lib):
@@ -212,8 +231,9 @@ def test_determinism_bit_identical(gpu_lib):
 
 
 # --------------------------------------------------------------------- MTP
-def test_mtp_union_and_replay_rounds(gpu_lib):
-    """4 query rows, 2 layers with their own keys and state, prefix-valid replay."""
+def _mtp_rounds(lockstep):
+    """4 query rows, 2 layers with their own keys and state, prefix-valid
+    replay.  Returns (request-layer rounds compared in full, tolerated ties)."""
     base = WORKLOADS["mtp-ctx256k-b32"]
     wl = dataclasses.replace(base, batch=3, ctx=64 * 260, layers=2, steps=6)
     acc = np_(acceptances(wl))
@@ -228,14 +248,16 @@ def test_mtp_union_and_replay_rounds(gpu_lib):
     scs = [np_(p.key_scale).astype(np.float64) for p in pools]
     osts = [[O.RequestState(wl.ctx, request_id=rids[b]) for b in range(wl.batch)]
             for _ in range(wl.layers)]
-    live = np.ones((wl.layers, wl.batch), dtype=bool)
-    compared = 0
+    compared = ties = 0
     keep = [10000, 5000, 4500, 6000, 5000, 5000]
     for t in range(wl.steps):
         rig.set_qpos(qp[t])
         a_dev = torch.as_tensor(acc[t].astype(np.int32), device=DEV)
         for layer in range(wl.layers):
             pool = pools[layer]
+            if lockstep and t > 0:
+                for b in range(wl.batch):
+                    sync_from_oracle(rig, layer, b, osts[layer][b], lockstep=True)
             qb, w = make_queries(wl, pool, layer, t, qp[t], device=DEV)
             kb = keep[t]
             spin.spin_predict_blocks(rig.h, layer, rig.batch, kb, rig.kept, rig.kept_count, rig.flags)
@@ -247,21 +269,22 @@ def test_mtp_union_and_replay_rounds(gpu_lib):
             torch.cuda.synchronize()
             tables = np_(pool.block_table)
             for b in range(wl.batch):
-                if not live[layer, b]:
-                    continue
                 qv, wv, _, _ = oracle_fp8_operands(qb[b], w[b])
                 before = osts[layer][b].copy()
                 ref = O.decode_round(osts[layer][b], int(qp[t, b]), wl.rows, kb, wl.explore_bp,
                                      cfg.seed, layer, qv, wv, kvs[layer], scs[layer], tables[b],
                                      wl.topk, wl.alpha, accepted=int(acc[t, b]))
                 gk = rig.kept_list(b)
-                if not np.array_equal(gk, ref["kept"]):
+                gflags = np_(rig.flags[b])[: len(ref["flags"])]
+                if not (np.array_equal(gk, ref["kept"]) and np.array_equal(gflags, ref["flags"])):
+                    assert not lockstep, f"t{t} l{layer} b{b}: kept differ from identical states"
                     assert _predicted_sets_tie_only(before, int(qp[t, b]), wl.rows, kb,
                                                     wl.explore_bp, np_(rig.flags[b])[: len(ref["flags"])],
                                                     ref["flags"]), f"t{t} l{layer} b{b}: kept differ"
-                    live[layer, b] = False
+                    _say("tolerated threshold tie", t, layer, b, "-> oracle state synced")
+                    sync_from_oracle(rig, layer, b, osts[layer][b])
+                    ties += 1
                     continue
-                assert np.array_equal(np_(rig.flags[b])[: len(ref["flags"])], ref["flags"])
                 n = len(gk) * 64
                 mag = score_mag(qv, wv, kvs[layer], scs[layer], tables[b], gk)
                 assert_scores_close(g_scores[b, :, :n], ref["scores"], mag, f"t{t} l{layer} b{b}")
@@ -278,5 +301,15 @@ def test_mtp_union_and_replay_rounds(gpu_lib):
                 assert gstep == osts[layer][b].step
                 compared += 1
     assert rig.state.error() == 0
-    _say("mtp rounds compared", compared)
-    assert compared >= 12
+    _say("mtp rounds compared", compared, "ties", ties)
+    return compared, ties
+
+
+def test_mtp_union_and_replay_rounds(gpu_lib):
+    n, ties = _mtp_rounds(lockstep=False)
+    assert n + ties == 36 and n >= 24
+
+
+def test_mtp_union_and_replay_lockstep(gpu_lib):
+    n, ties = _mtp_rounds(lockstep=True)
+    assert n == 36 and ties == 0
