@@ -9,9 +9,10 @@
 //   quarters, which let the top-k discard most candidates before ranking them.  Heads form the M side of v_mfma_scale_f32_16x16x128_f8f6f4 and
 //   tokens the N side, so one MFMA does 16 heads x 16 tokens over the whole
 //   head dim; a page is 4 head tiles x 4 token tiles per row.  ReLU, the head
-//   weights and the head sum run on the accumulator registers, the 4 lane
-//   groups are folded with two cross-lane adds, and every lane then holds the
-//   score of token `lane`; rows are staged in LDS and written in bursts.
+//   weights and the head sum run on the accumulator registers (the epilogue of
+//   one head tile beside the MFMAs of the next), the 4 lane groups are folded
+//   with permlane swaps, and every lane then holds the score of token `lane`;
+//   rows are staged in LDS and written in bursts.
 #include <atomic>
 
 #include "spin_device.h"
@@ -41,7 +42,7 @@ constexpr int kDim = 128;
 #define SPIN_IDX_NT_STORE 1            // streaming (non-temporal) score stores
 #endif
 #ifndef SPIN_IDX_WAVES_PER_EU
-#define SPIN_IDX_WAVES_PER_EU 0        // occupancy target for the register allocator (0: none)
+#define SPIN_IDX_WAVES_PER_EU 3        // occupancy target for the register allocator (0: none)
 #endif
 #if SPIN_IDX_WAVES_PER_EU > 0
 #define SPIN_IDX_OCCUPANCY __attribute__((amdgpu_waves_per_eu(SPIN_IDX_WAVES_PER_EU)))
@@ -155,42 +156,100 @@ __device__ __forceinline__ void load_page(PageRegs& dst, const uint8_t* k_pool, 
 // weights are staged halved, so (w/2)(x + |x|) is bit-identical to w max(x, 0).
 __device__ __forceinline__ float relu2(float x) { return x + fabsf(x); }
 
-// Scores of one page for query row r: 16 MFMAs (4 head tiles x 4 token tiles),
-// ReLU and head weights on the accumulators (one add and one FMA per head and
-// token), lane groups folded; returns the raw (unscaled) score of token `lane`.
-// s_w holds the halved head weights.
+// Sum of the four lane groups' partials for token `lane`: lane group g
+// (lanes 16g..16g+15) holds, for each token tile tt, its partial sum of token
+// 16 tt + (lane & 15); the result of lane l is the full sum for token l.  Two
+// half-wave swaps (lanes l and l + 32) fold tiles (0, 2) and (1, 3), then one
+// row swap (lanes l and l + 16 within each half) folds the rest: three
+// permlane swaps and three adds, no LDS traffic.
+__device__ __forceinline__ float fold_lane_groups(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]),
+                                                  false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]),
+                                                  false, false);
+  // lanes 0..31: tiles 0 and 1; lanes 32..63: tiles 2 and 3
+  const float x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float y = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false,
+                                                  false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Raw (unscaled) scores of token `lane` of one page for every query row r:
+// 4R steps of (row, head tile), each 4 MFMAs (one per token tile) into one of
+// two accumulator sets, software-pipelined so that the ReLU / head-weight
+// epilogue of step i - 1 (32 VALU operations on the other set) issues while
+// the MFMAs of step i run.  ReLU is x + |x| against halved head weights (s_w),
+// bit-identical to w max(x, 0).
 template <int R>
-__device__ __forceinline__ float page_row_score(const PageRegs& kb, const uint8_t* s_q,
-                                                const float* s_w, int r, int g, int n16) {
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void page_scores(const PageRegs& kb, const uint8_t* s_q,
+                                            const float* s_w, int g, int n16, float (&res)[R]) {
+  constexpr int T = 4 * R;
+  float part[R][4];
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht) {
-    const v8i qa = *reinterpret_cast<const v8i*>(s_q + (r * kHeads + ht * 16 + n16) * kQStride + g * 32);
-    const float4 wv = *reinterpret_cast<const float4*>(s_w + r * kHeads + ht * 16 + g * 4);
-    v4f acc[4];
+  for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const v4f zero = {0.f, 0.f, 0.f, 0.f};
-      acc[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb.t[tt], zero, 0, 0, 0, 127, 0, 127);
+    for (int tt = 0; tt < 4; ++tt) part[r][tt] = 0.0f;
+  v4f acc[2][4];
+  v8i qa[2];
+  float4 wv[2];
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // query operand of step i: row i / 4, head tile i % 4
+  auto q_of = [&](int i) {
+    return *reinterpret_cast<const v8i*>(s_q + ((i / 4) * kHeads + (i % 4) * 16 + n16) * kQStride +
+                                         g * 32);
+  };
+  auto w_of = [&](int i) {
+    return *reinterpret_cast<const float4*>(s_w + (i / 4) * kHeads + (i % 4) * 16 + g * 4);
+  };
+  // With several rows the LDS operands are read one step ahead (the next
+  // step's query tile, this step's head weights for its epilogue in the next
+  // step), so the MFMAs do not wait on LDS; with one row the kernel is bound
+  // by HBM and keeps the registers instead (3 waves per SIMD either way).
+  constexpr bool kAhead = R > 1;
+  if (kAhead) qa[0] = q_of(0);
+#pragma unroll
+  for (int i = 0; i <= T; ++i) {
+    if (i < T) {
+      if (kAhead) {
+        if (i + 1 < T) qa[(i + 1) & 1] = q_of(i + 1);
+      } else {
+        qa[i & 1] = q_of(i);
+      }
+      wv[i & 1] = w_of(i);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        acc[i & 1][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[i & 1], kb.t[tt], zero,
+                                                                          0, 0, 0, 127, 0, 127);
     }
+    if (i > 0) {
+      const int r = (i - 1) / 4;
+      const float4 w = wv[(i - 1) & 1];
+      const v4f* a = acc[(i - 1) & 1];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      part[tt] = fmaf(wv.x, relu2(acc[tt][0]), part[tt]);
-      part[tt] = fmaf(wv.y, relu2(acc[tt][1]), part[tt]);
-      part[tt] = fmaf(wv.z, relu2(acc[tt][2]), part[tt]);
-      part[tt] = fmaf(wv.w, relu2(acc[tt][3]), part[tt]);
+      for (int tt = 0; tt < 4; ++tt) {
+        part[r][tt] = fmaf(w.x, relu2(a[tt][0]), part[r][tt]);
+        part[r][tt] = fmaf(w.y, relu2(a[tt][1]), part[r][tt]);
+        part[r][tt] = fmaf(w.z, relu2(a[tt][2]), part[r][tt]);
+        part[r][tt] = fmaf(w.w, relu2(a[tt][3]), part[r][tt]);
+        // keep this step's epilogue inside its scheduling region (beside the
+        // next step's MFMAs) instead of letting it sink to the end of the page
+        asm volatile("" : "+v"(part[r][tt]));
+      }
     }
-    // One head tile's epilogue at a time: without this fence the scheduler
-    // gathers the ReLU terms of all 64 accumulators ahead of their FMAs and
-    // the kernel no longer fits 3 waves per SIMD.
+    if (i < T) {
+      // the LDS reads first, then one MFMA and 8 epilogue operations, four times
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    part[tt] += __shfl_xor(part[tt], 16, kWave);
-    part[tt] += __shfl_xor(part[tt], 32, kWave);
-  }
-  return g == 0 ? part[0] : g == 1 ? part[1] : g == 2 ? part[2] : part[3];
+  for (int r = 0; r < R; ++r) res[r] = fold_lane_groups(part[r]);
 }
 
 // Count of kept pages of row b as the kernels use it: negative counts read as
@@ -364,13 +423,11 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
             const int j = __builtin_amdgcn_readlane(my_j, m);
             const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_sc), m));
             const int mf = m % F;
+            float val[R];
+            if (j >= 0) page_scores<R>(ring[u], s_q, s_w, g, n16, val);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-              float out = -INFINITY;
-              if (j >= 0) {
-                const float val = page_row_score<R>(ring[u], s_q, s_w, r, g, n16);
-                out = (j * kBlock + l <= q0 + r) ? val * sc : -INFINITY;
-              }
+              const float out = (j >= 0 && j * kBlock + l <= q0 + r) ? val[r] * sc : -INFINITY;
               my_out[(r * F + mf) * kBlock + l] = out;
               if (page_qmax) {
                 // maxima of the page's four 16-slot quarters (DPP row reduction;
