@@ -79,8 +79,6 @@ def _args():
     ap.add_argument("--sparsity-bp", type=int, default=5000)
     ap.add_argument("--sweep", default="0,4000", help="extra sparsities (bp) timed for scaling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--spacer-cycles", type=int, default=4000,
-                    help="device-clock cycles of spin before the update on the side stream")
     ap.add_argument("--quantize-on-main", action="store_true",
                     help="run the query quantiser on the main stream after the predictor")
     ap.add_argument("--cpu-requests", type=int, default=160)
@@ -131,40 +129,39 @@ def _setup(wl, device):
 
 
 QUANTIZE_ON_SIDE = True
-SPACER_CYCLES = 0
 
 
-def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None, accepted=None):
+def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_end, ev=None, accepted=None,
+           tail="beside"):
     """One SPIN round.
 
-    Main stream: predict -> indexer -> top-k.  `side` runs the query
-    quantisation beside the predictor (both start once the previous round's
-    update is done; they touch disjoint memory), then, once the indexer is
-    done, the EMA update beside the top-k (both only read the scores and kept
-    lists and write disjoint outputs).  The top-k goes first on the stream that
-    ran the indexer, so its workgroups are resident before the update's fill
-    the GPU.  The round starts after the previous round's update
-    (`prev_update`): the predictor reads the EMAs it writes, and this round
-    overwrites the kept lists, scores and quantised queries it reads.
-    `ev` = 8 timing events (5 on the main stream around predict, indexer and
-    top-k plus the wait for the quantiser; 3 on `side` around quantise and
-    update), or None.  `accepted` (int32 [B], device): MTP acceptances, whose
-    prefix-valid replay replaces the single-row update.  Returns the event that
-    marks this round's update as done.
+    Main stream: predict -> indexer -> the round's tail (spin_topk_update).
+    `side` runs the query quantisation beside the predictor (both start once
+    the previous round is done; they touch disjoint memory) and, with
+    tail="beside", the EMA update beside the top-k, behind the library's gate
+    (it opens once every top-k workgroup has started).  tail="behind" runs the
+    update on the main stream after the top-k.  `ev` = 8 timing events (0-4
+    on the main stream around predict, the wait for the quantiser, indexer and
+    top-k; 5-6 on the quantiser's stream around it; 7 at the update's end), or
+    None.  `accepted` (int32 [B], device): MTP acceptances, whose
+    prefix-valid replay replaces the single-row update.  Returns the event
+    that marks the round's end.
     """
     import torch
 
     b = bufs
     main = torch.cuda.current_stream()
-    if prev_update is not None:
-        main.wait_event(prev_update)
+    if prev_end is not None:
+        main.wait_event(prev_end)
     ev = ev or [None] * 8
     rec = lambda e, s: e.record(s) if e is not None else None
     rec(ev[0], main)
     spin.spin_predict_blocks(st.handle, 0, b["batch"], keep_bp, b["kept"], b["cnt"], b["flags"])
     rec(ev[1], main)
-    # quantiser on the side stream (already ordered after the previous update)
+    # quantiser on the side stream, ordered after the previous round
     qs = side if QUANTIZE_ON_SIDE else main
+    if QUANTIZE_ON_SIDE and prev_end is not None:
+        side.wait_event(prev_end)
     rec(ev[5], qs)
     spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
     rec(ev[6], qs)
@@ -175,37 +172,44 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_update, ev=None, acce
     rec(ev[2], main)
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
                              pool.block_table, b["kept"], b["cnt"], b["scores"], b["pq"])
-    idx_done = torch.cuda.Event()
-    idx_done.record(main)
     rec(ev[3], main)
-    spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
-                          b["topk_ws"], b["pq"])
-    rec(ev[4], main)
-    side.wait_event(idx_done)
-    if SPACER_CYCLES:
-        # a few microseconds of one-workgroup spin on the side stream, so the
-        # top-k's 96 full-CU workgroups are dispatched before the update's fill
-        # the GPU (both become ready when the indexer ends)
-        with torch.cuda.stream(side):
-            torch.cuda._sleep(SPACER_CYCLES)
-    if accepted is None:
-        spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"], stream=side)
-    else:
-        spin.spin_mtp_replay(st.handle, 0, b["batch"], accepted, b["scores"], b["kept"], b["cnt"],
-                             stream=side)
-    rec(ev[7], side)
-    upd_done = torch.cuda.Event()
-    upd_done.record(side)
-    return upd_done
+    # the library's tail: the top-k on the main stream, the EMA update (or
+    # the replay) beside it on `side` (tail="beside", gated by the library so
+    # that it never takes the top-k's CUs) or behind it on main ("behind")
+    spin.spin_topk_update(st.handle, 0, b["batch"], b["scores"], b["pq"], b["kept"], b["cnt"],
+                          b["topk"], accepted, update_stream=side if tail == "beside" else None)
+    rec(ev[4], main)                      # the top-k's end (with "behind", the update's)
+    us = side if tail == "beside" else main
+    rec(ev[7], us)
+    end = torch.cuda.Event()
+    end.record(us)
+    if tail == "beside":
+        # the round ends when the top-k (main) and the update (side) are done
+        main_done = torch.cuda.Event()
+        main_done.record(main)
+        side.wait_event(main_done)
+        end = torch.cuda.Event()
+        end.record(side)
+    return end
 
 
-def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1, modes=(False, True)):
-    """Per keep, and per timing mode in `modes`, `warmup` untimed rounds then
-    `steps` timed rounds.  Mode False (lean) records only the round's start,
-    the top-k's end and the update's end, so the round carries no other event
-    or marker: its step and wall times are the path's own.  Mode True
-    (detailed) brackets every stage with events (8 per round) for the per-stage
-    times.  Returns {keep: {mode: {...}}}."""
+# timing passes: (name, tail, events recorded per round)
+PASSES = (("lean", "beside", (0, 4, 7)), ("serial", "behind", (0, 7)),
+          ("detailed", "beside", tuple(range(8))))
+
+
+def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
+    """Per keep and per timing pass of PASSES, `warmup` untimed rounds then
+    `steps` timed rounds, all from the same state reset and inputs:
+      lean      the library's round with the update beside the top-k, 3
+                events per round (its start, the top-k's end, the update's
+                end): value, ms_per_step, the predict + index + top-k latency
+                and the whole step.
+      serial    the same round with the update behind the top-k on one stream
+                (2 events): the whole step without the overlap.
+      detailed  the lean round with events around every stage (8 per round):
+                the stage times, the sweep's indexer times and the roofline.
+    Returns {keep: {pass name: {...}}}."""
     import torch
 
     from workload import acceptances, make_pool, positions
@@ -234,19 +238,19 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1, modes=(False, True)
     acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
     for keep_bp in keep_bps:
         results[keep_bp] = {}
-        for detail in modes:
+        for name, tail, recorded in PASSES:
             spin.spin_reset_slots(st.handle, bufs["slot"],
                                   torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
             done = None
             for t in range(warmup):
                 bufs["qpos"].copy_(qpos_all[t])
                 done = _round(spin, st, bufs, pools[t % n_pools], qs[t][0], qs[t][1], keep_bp,
-                              side, done, accepted=acc_of(t))
+                              side, done, accepted=acc_of(t), tail=tail)
             torch.cuda.synchronize()
             evs = []
             for _ in range(steps):
                 e = [None] * 8
-                for k in (range(8) if detail else (0, 4, 7)):
+                for k in recorded:
                     e[k] = torch.cuda.Event(enable_timing=True)
                 evs.append(e)
             torch.cuda.synchronize()
@@ -256,26 +260,30 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1, modes=(False, True)
                 bufs["qpos"].copy_(qpos_all[warmup + t])
                 q, w = qs[warmup + t]
                 done = _round(spin, st, bufs, pools[(warmup + t) % n_pools], q, w, keep_bp, side,
-                              done, evs[t], accepted=acc_of(warmup + t))
+                              done, evs[t], accepted=acc_of(warmup + t), tail=tail)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
-            per = {"predict": [], "quantize": [], "indexer": [], "topk": [], "update": []}
-            for e in evs if detail else []:
-                per["predict"].append(e[0].elapsed_time(e[1]) * 1e3)       # us
-                per["quantize"].append(e[5].elapsed_time(e[6]) * 1e3)      # beside predict
-                per["indexer"].append(e[2].elapsed_time(e[3]) * 1e3)
-                per["topk"].append(e[3].elapsed_time(e[4]) * 1e3)
-                per["update"].append(e[3].elapsed_time(e[7]) * 1e3)        # from the indexer's end
-            # a round ends when both the top-k (main) and the update (side) are done
-            per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[7])) * 1e3 for e in evs]
-            # critical path to the top-k: predict, the wait for the quantiser, indexer, top-k
-            per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
+            per = {"step": [e[0].elapsed_time(e[7]) * 1e3 for e in evs]}      # us
+            if 4 in recorded:
+                # critical path to the top-k: predict, the wait for the quantiser, indexer, top-k
+                per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
+            if 4 in recorded:
+                # a round ends when both the top-k and the update are done
+                per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[7])) * 1e3
+                               for e in evs]
+            if name == "detailed":
+                per["predict"] = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+                per["quantize"] = [e[5].elapsed_time(e[6]) * 1e3 for e in evs]  # beside predict
+                per["indexer"] = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+                per["topk"] = [e[3].elapsed_time(e[4]) * 1e3 for e in evs]
+                # the update beside the top-k: from the indexer's end to its own
+                per["update"] = [e[3].elapsed_time(e[7]) * 1e3 for e in evs]
             cnt = bufs["cnt"].cpu()
             kept_pages = int(cnt.sum())
             if st.error() != 0:
                 raise RuntimeError(f"device error word {st.error()}")
-            results[keep_bp][detail] = dict(wall_s=wall, per_us=per, kept_pages=kept_pages,
-                                            blocks=wl.batch * wl.blocks)
+            results[keep_bp][name] = dict(wall_s=wall, per_us=per, kept_pages=kept_pages,
+                                          blocks=wl.batch * wl.blocks)
     return results
 
 
@@ -767,9 +775,8 @@ def main():
     wl = WORKLOADS[a.workload]
     device = "cuda:0"
     torch.cuda.set_device(0)
-    global QUANTIZE_ON_SIDE, SPACER_CYCLES
+    global QUANTIZE_ON_SIDE
     QUANTIZE_ON_SIDE = not a.quantize_on_main
-    SPACER_CYCLES = a.spacer_cycles
     if a.fidelity:
         _fidelity(a.fidelity, wl, device, [int(x) for x in a.fid_targets.split(",")])
         return
@@ -786,8 +793,9 @@ def main():
     if a.copy_calibration:
         _copy_calibration(device)
     both = _run_gpu(wl, keeps, a.steps, a.warmup, device, max(1, a.pools))
-    res = {k: v[True] for k, v in both.items()}          # detailed: per-stage times
-    lean = both[keep_main][False]                        # lean: step, latency and wall
+    res = {k: v["detailed"] for k, v in both.items()}    # per-stage times
+    lean = both[keep_main]["lean"]                       # library round: latency, step, wall
+    ser = both[keep_main]["serial"]                      # the update behind the top-k
 
     main_r = res[keep_main]
     per = main_r["per_us"]
@@ -807,7 +815,7 @@ def main():
         sweep_out[str(10000 - k)] = {
             "kept_share": r["kept_pages"] / r["blocks"],
             "indexer_us": round(iu, 2),
-            "step_us_median": round(_median(both[k][False]["per_us"]["step"]), 2),
+            "step_us_median": round(_median(both[k]["lean"]["per_us"]["step"]), 2),
         }
     if "0" in sweep_out:
         base = sweep_out["0"]["indexer_us"]
@@ -843,19 +851,24 @@ def main():
         "indexer_roofline_tokens_per_s": HBM_PEAK_GBS * 1e9 / (
             IDX_BYTES_PER_PAGE / 64 + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW / 64),
         "per_step_us": {
+            # lean pass: the library's round, the update beside the top-k
             "predict_index_topk_median": round(_median(pit), 2),
             "predict_index_topk_p10": round(_pct(pit, 10), 2),
             "predict_index_topk_p90": round(_pct(pit, 90), 2),
-            "update_median": round(_median(per["update"]), 2),
             "whole_step_median": round(_median(step_us), 2),
+            "update_median": round(_median(per["update"]), 2),
             **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items()
                if n not in ("step", "to_topk")},
             "quantize_overlaps_predict": QUANTIZE_ON_SIDE,
-            "update_overlaps_topk": True,
-            # the median, p10, p90, whole step and ms_per_step come from rounds
-            # that record 3 events each; the stage means, the sweep's indexer
-            # times and the roofline from the same rounds timed again with 8
-            # events each, whose own figures follow
+            "tail": "spin_topk_update: top-k on the main stream, EMA update beside it behind "
+                    "the library's gate",
+            # the same round with the update behind the top-k on one stream
+            "serial_pass": {
+                "ms_per_step": round(ser["wall_s"] * 1e3 / a.steps, 4),
+                "whole_step_median": round(_median(ser["per_us"]["step"]), 2),
+            },
+            # every stage bracketed by events (8 per round): the stage means,
+            # the sweep's indexer times and the roofline
             "detailed_pass": {
                 "ms_per_step": round(main_r["wall_s"] * 1e3 / a.steps, 4),
                 "predict_index_topk_median": round(_median(per["to_topk"]), 2),

@@ -25,7 +25,11 @@
  *     and returns without synchronising.  No call allocates device memory; the
  *     caller owns every buffer, including the state buffer.
  *   - A state is used from one stream at a time: calls that overlap on one
- *     state race on its workspace.
+ *     state race on its workspace.  The exceptions, which touch disjoint
+ *     state regions: spin_quantize_q (q8, wq, qexp) may run beside
+ *     spin_predict_blocks (V, D, VB, step, bscore, ukey) once both are
+ *     ordered after the previous round's update, and spin_topk_scores (no
+ *     state) may run beside spin_update / spin_mtp_replay.
  *   - Return value: SPIN_OK (0) or a negative SPIN_E* code; no C++ exception
  *     crosses this boundary.  Arguments that live in host memory are checked
  *     before anything is enqueued.  Values that live in device arrays (slot,
@@ -124,6 +128,8 @@ typedef struct spin_batch {
  *   step [num_layers][max_slots] int32       completed rounds of each (layer, slot)
  *   request_id [max_slots] uint64            Philox counter word 2
  *   error int32                              SPIN_ERR_* bits, sticky until spin_state_init
+ *   tail_gate uint64                         top-k workgroups started by two-stream
+ *                                            spin_topk_update calls (never reset)
  *   q8  [max_slots][max_rows][heads][head_dim] uint8   workspace: e4m3fn query codes
  *   wq  [max_slots][max_rows][heads]          workspace: w * 2^e
  *   qexp [max_slots][max_rows][heads] int32   workspace: query exponents e
@@ -136,8 +142,8 @@ typedef struct spin_batch {
  *                                             the page quarter maxima and needs no workspace
  * Workspace arrays are indexed by batch position b, not by slot. */
 typedef struct spin_state_layout {
-  size_t V, D, VB, step, request_id, error, q8, wq, qexp, bscore, ukey, page_qmax, topk_ws,
-      total;
+  size_t V, D, VB, step, request_id, error, tail_gate, q8, wq, qexp, bscore, ukey, page_qmax,
+      topk_ws, total;
   int32_t max_blocks;     /* ceil(max_ctx / 64) */
   int32_t reserved;
 } spin_state_layout;
@@ -263,6 +269,28 @@ int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf1
  * the scores are ignored (with R > 1 this is the row-0 update policy). */
 int spin_update(spin_state* st, int layer, const spin_batch* batch, const float* scores,
                 const int32_t* kept_blocks, const int32_t* kept_count, hipStream_t stream);
+
+/* The round's tail: spin_topk_scores (K = the state's topk, with page_qmax
+ * when given, else without it, no workspace) and spin_update (accepted ==
+ * NULL) or spin_mtp_replay (accepted: device int32 [B]), scheduled by the
+ * library.  With update_stream NULL or equal to stream, both run on stream,
+ * the update behind the top-k.  With a second stream, the top-k runs on
+ * `stream` and the update on `update_stream`, beside it: update_stream first
+ * waits for the work enqueued on `stream` before this call (the indexer that
+ * wrote the scores), then for a gate that opens once every top-k workgroup
+ * has started (a one-wave kernel polling the state's tail_gate counter, which
+ * each top-k workgroup of such a call increments; the wait gives up after
+ * 2 ms of device time, so it cannot hang).  The update's many small
+ * workgroups therefore never take the compute units the top-k's one
+ * workgroup per row needs, whatever the caller's streams do.  The top-k's
+ * completion is ordered on `stream`, the update's on update_stream: the
+ * next round (whose predictor reads the EMAs) must wait for both.  Results
+ * are those of the two calls made one after the other.  scores and
+ * page_qmax: 16-byte aligned. */
+int spin_topk_update(spin_state* st, int layer, const spin_batch* batch, const float* scores,
+                     const float* page_qmax, const int32_t* kept_blocks,
+                     const int32_t* kept_count, int32_t* topk_out, const int32_t* accepted,
+                     hipStream_t stream, hipStream_t update_stream);
 
 /* Prefix-valid MTP replay (ai4snews digest, "arXiv深度剖析"; v1 Table 7,
  * row-local union + prefix-valid update): with a = accepted[b] in 0..R-1,

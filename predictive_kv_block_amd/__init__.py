@@ -13,8 +13,8 @@ __all__ = [
     "spin_state_bytes", "spin_state_layout_of", "spin_state_init", "spin_state_destroy",
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
-    "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
-    "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
+    "spin_mtp_replay", "spin_topk_update", "spin_measure_miss", "spin_allocate_budgets",
+    "spin_status_string", "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
     "spin_attention_workspace_bytes", "spin_sparse_attention", "EXPORTS",
 ]
 
@@ -24,8 +24,8 @@ EXPORTS = [
     "spin_state_bytes", "spin_state_layout_of", "spin_state_init", "spin_state_destroy",
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
-    "spin_mtp_replay", "spin_measure_miss", "spin_allocate_budgets", "spin_status_string",
-    "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
+    "spin_mtp_replay", "spin_topk_update", "spin_measure_miss", "spin_allocate_budgets",
+    "spin_status_string", "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
     "spin_attention_workspace_bytes", "spin_sparse_attention",
 ]
 
@@ -53,8 +53,8 @@ class SpinBatch(ctypes.Structure):
 
 class SpinLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("V", "D", "VB", "step", "request_id", "error", "q8", "wq", "qexp",
-                 "bscore", "ukey", "page_qmax", "topk_ws", "total")] + [
+                ("V", "D", "VB", "step", "request_id", "error", "tail_gate", "q8", "wq",
+                 "qexp", "bscore", "ukey", "page_qmax", "topk_ws", "total")] + [
         ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
@@ -82,6 +82,8 @@ _SIGS = {
                           _vp, _vp, _vp],
     "spin_update": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp],
     "spin_mtp_replay": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp, _vp],
+    "spin_topk_update": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                         _vp],
     "spin_measure_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
     "spin_allocate_budgets": [_i32, ctypes.POINTER(ctypes.c_double), _i32,
                               ctypes.POINTER(ctypes.c_int32)],
@@ -230,6 +232,17 @@ def spin_update(h, layer, batch, scores, kept_blocks, kept_count, stream=None):
 def spin_mtp_replay(h, layer, batch, accepted, scores, kept_blocks, kept_count, stream=None):
     _check(load().spin_mtp_replay(h, int(layer), ctypes.byref(batch), _p(accepted), _p(scores),
                                   _p(kept_blocks), _p(kept_count), _stream(stream)))
+
+
+def spin_topk_update(h, layer, batch, scores, page_qmax, kept_blocks, kept_count, topk_out,
+                     accepted=None, stream=None, update_stream=None):
+    """The round's tail: the top-k on `stream` and the EMA update (or the
+    prefix-valid replay with `accepted`) behind it, or beside it on
+    `update_stream`, ordered by the library's gate."""
+    us = None if update_stream is None else ctypes.c_void_p(update_stream.cuda_stream)
+    _check(load().spin_topk_update(h, int(layer), ctypes.byref(batch), _p(scores), _p(page_qmax),
+                                   _p(kept_blocks), _p(kept_count), _p(topk_out), _p(accepted),
+                                   _stream(stream), us))
 
 
 def spin_measure_miss(batch, topk, full_topk, block_flags, miss, stream=None):

@@ -50,6 +50,7 @@ spin_state_layout make_layout(const spin_config* c) {
   l.step = off;       off = align_up(off + L * S * 4);
   l.request_id = off; off = align_up(off + S * 8);
   l.error = off;      off = align_up(off + 4);
+  l.tail_gate = off;  off = align_up(off + 8);
   l.q8 = off;         off = align_up(off + S * R * H * d);
   l.wq = off;         off = align_up(off + S * R * H * 4);
   l.qexp = off;       off = align_up(off + S * R * H * 4);
@@ -124,6 +125,9 @@ int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes, hipSt
   v.step = reinterpret_cast<int32_t*>(st->base + lay.step);
   v.rid = reinterpret_cast<uint64_t*>(st->base + lay.request_id);
   v.err = reinterpret_cast<int32_t*>(st->base + lay.error);
+  v.gate = reinterpret_cast<unsigned long long*>(st->base + lay.tail_gate);
+  st->gate_target = 0;
+  st->tail_event = nullptr;
   v.q8 = reinterpret_cast<uint8_t*>(st->base + lay.q8);
   v.wq = reinterpret_cast<float*>(st->base + lay.wq);
   v.qexp = reinterpret_cast<int32_t*>(st->base + lay.qexp);
@@ -157,6 +161,7 @@ int spin_state_init(const spin_config* cfg, void* state_mem, size_t bytes, hipSt
 
 int spin_state_destroy(spin_state* st) {
   if (!st) return SPIN_EINVAL;
+  if (st->tail_event) (void)hipEventDestroy(st->tail_event);
   delete st;
   return SPIN_OK;
 }
@@ -260,6 +265,48 @@ int spin_update(spin_state* st, int layer, const spin_batch* batch, const float*
     return SPIN_EINVAL;
   return hip_status(spin::launch_update(st->view, layer, *batch, nullptr, scores, kept_blocks,
                                         kept_count, stream));
+}
+
+int spin_topk_update(spin_state* st, int layer, const spin_batch* batch, const float* scores,
+                     const float* page_qmax, const int32_t* kept_blocks,
+                     const int32_t* kept_count, int32_t* topk_out, const int32_t* accepted,
+                     hipStream_t stream, hipStream_t update_stream) {
+  int rc = check_batch(st, batch);
+  if (rc) return rc;
+  if (layer < 0 || layer >= st->cfg.num_layers || !scores || !kept_blocks || !kept_count ||
+      !topk_out)
+    return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(page_qmax) % 16 != 0)
+    return SPIN_EINVAL;
+  const spin_batch& bt = *batch;
+  const int K = st->cfg.topk;
+  if (update_stream == nullptr || update_stream == stream) {
+    // one stream: the top-k, then the update behind it
+    rc = hip_status(spin::launch_topk_gated(bt, K, scores, page_qmax, kept_blocks, kept_count,
+                                            topk_out, nullptr, stream));
+    if (rc) return rc;
+    return hip_status(spin::launch_update(st->view, layer, bt, accepted, scores, kept_blocks,
+                                          kept_count, stream));
+  }
+  if (!st->tail_event) {
+    rc = hip_status(hipEventCreateWithFlags(&st->tail_event, hipEventDisableTiming));
+    if (rc) return rc;
+  }
+  // the update's stream waits for what `stream` did before this call (the
+  // indexer), then for the gate that opens once every top-k workgroup runs
+  rc = hip_status(hipEventRecord(st->tail_event, stream));
+  if (rc) return rc;
+  rc = hip_status(spin::launch_topk_gated(bt, K, scores, page_qmax, kept_blocks, kept_count,
+                                          topk_out, st->view.gate, stream));
+  if (rc) return rc;
+  st->gate_target += static_cast<unsigned long long>(bt.B) * bt.R;
+  rc = hip_status(hipStreamWaitEvent(update_stream, st->tail_event, 0));
+  if (rc) return rc;
+  rc = hip_status(spin::launch_gate(st->view.gate, st->gate_target, update_stream));
+  if (rc) return rc;
+  return hip_status(spin::launch_update(st->view, layer, bt, accepted, scores, kept_blocks,
+                                        kept_count, update_stream));
 }
 
 int spin_mtp_replay(spin_state* st, int layer, const spin_batch* batch, const int32_t* accepted,

@@ -13,6 +13,7 @@ struct SpinView {
   int32_t* step;     // [L][S]
   uint64_t* rid;     // [S]
   int32_t* err;      // [1]
+  unsigned long long* gate;  // [1] top-k workgroups started by gated launches, ever
   uint8_t* q8;       // [S][max_rows][H][d]
   float* wq;         // [S][max_rows][H]
   int32_t* qexp;     // [S][max_rows][H]
@@ -33,6 +34,8 @@ struct spin_state {
   spin_state_layout lay;
   char* base;
   SpinView view;
+  unsigned long long gate_target;  // value of view.gate once the last gated top-k has started
+  hipEvent_t tail_event;           // orders a gated update after the indexer (made on first use)
 };
 
 namespace spin {
@@ -62,6 +65,15 @@ hipError_t launch_indexer(const SpinView& v, const spin_batch& bt, const uint8_t
                           float* page_qmax, hipStream_t s);
 hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, const float* page_qmax,
                        const int32_t* kept, const int32_t* kept_count, int32_t* out, void* ws,
+                       hipStream_t s);
+// The round's tail on two streams: the top-k launch (one workgroup per row,
+// each adding 1 to `arrivals` as it starts) and a gate that waits until
+// `arrivals` reaches `target`, which the update's launch then follows.
+hipError_t launch_topk_gated(const spin_batch& bt, int topk, const float* scores,
+                             const float* page_qmax, const int32_t* kept,
+                             const int32_t* kept_count, int32_t* out,
+                             unsigned long long* arrivals, hipStream_t s);
+hipError_t launch_gate(const unsigned long long* arrivals, unsigned long long target,
                        hipStream_t s);
 hipError_t launch_update(const SpinView& v, int layer, const spin_batch& bt,
                          const int32_t* accepted, const float* scores, const int32_t* kept,

@@ -70,6 +70,9 @@ hipError_t launch_fill_state(const SpinView& v, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, s, reinterpret_cast<uint32_t*>(v.err),
                      size_t(1), 0u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(256), 0, s, reinterpret_cast<uint32_t*>(v.gate),
+                     size_t(2), 0u);
   return hipGetLastError();
 }
 

@@ -8,9 +8,9 @@
 // 16-slot quarter of a page), k_topk_fused answers every row in one launch
 // (one workgroup per row): t1 = the K-th largest of the pages' top quarter
 // maxima.  Those are scores of distinct slots, so the row's K-th largest score
-// is >= t1 and every score < t1 can be dropped; only pages whose maximum is
-// >= t1 can hold such scores.  Those pages are read, their scores >= t1
-// gathered in position order and ranked exactly.  A row that does not fit
+// is >= t1 and every score < t1 can be dropped; only 16-slot quarters whose
+// maximum is >= t1 can hold such scores.  Those quarters are read, their
+// scores >= t1 gathered in position order and ranked exactly.  A row that does not fit
 // those buffers is walked in chunks by the same workgroup, keeping a running
 // top-K.
 //
@@ -193,21 +193,20 @@ constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kFusedPageLanes = 16;                          // page maxima per lane
 constexpr int kFusedMaxPages = kFusedThreads * kFusedPageLanes;   // 16384
-constexpr int kFusedCandPages = 4096;                        // listed candidate pages
+constexpr int kFusedCandQ = 8192;                            // listed candidate quarters
 constexpr int kFusedCap = 8192;                              // survivors held in LDS
 constexpr int kFusedPerLane = kFusedCap / kFusedThreads;     // 8
 
 #ifndef SPIN_TOPK_BATCH
-#define SPIN_TOPK_BATCH 32
+#define SPIN_TOPK_BATCH 256
 #endif
-static_assert(SPIN_TOPK_BATCH % 4 == 0 && SPIN_TOPK_BATCH <= 64, "4 pages per load");
-constexpr int kFusedBatch = SPIN_TOPK_BATCH;                 // pages per wave step
+static_assert(SPIN_TOPK_BATCH % 16 == 0 && SPIN_TOPK_BATCH <= 256, "16 quarters per load");
+constexpr int kFusedBatch = SPIN_TOPK_BATCH;                 // quarters per wave step
 
 struct FusedShared {
   TopkShared t;
-  int pages[kFusedCandPages];     // kept index of each candidate page, ascending
-  int pagej[kFusedCandPages];     // its block index (kept entry)
-  int pcount[kFusedCandPages];    // survivors per candidate page, then their offsets
+  int cq[kFusedCandQ];            // candidate quarters (4 kept index + quarter), ascending
+  int qcount[kFusedCandQ];        // survivors per candidate quarter, then their offsets
   uint32_t skey[kFusedCap];       // survivors in position order
   int spos[kFusedCap];
   int scan[kFusedWaves];
@@ -239,9 +238,9 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
   return x;
 }
 
-// Exclusive prefix sum over n <= kFusedCandPages ints in LDS; returns the total.
+// Exclusive prefix sum over n <= kFusedCandQ ints in LDS; returns the total.
 __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
-  constexpr int per = kFusedCandPages / kFusedThreads;         // 4
+  constexpr int per = kFusedCandQ / kFusedThreads;             // 8
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   int loc[per], sum = 0;
 #pragma unroll
@@ -349,21 +348,19 @@ __device__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out) {
 // grid (rows), 1024 threads: the whole top-k of a row.
 // Fast path (at most 16384 kept pages and at least K finite quarter maxima
 // among the ones used): t1 = the K-th largest of the pages' top-m quarter
-// maxima (m = 1, 2 or 4); only pages whose maximum is >= t1 can hold scores
-// >= t1, and those scores (at least K of them) are collected in position order
-// and ranked exactly.
-// Fallback (fewer than K finite quarter maxima, more than kFusedCandPages
-// candidate pages or more than kFusedCap survivors): the row is walked in
+// maxima (m = 1, 2 or 4); only 16-slot quarters whose maximum is >= t1 can
+// hold scores >= t1, and those scores (at least K of them) are collected in
+// position order and ranked exactly.
+// Fallback (fewer than K finite quarter maxima, more than kFusedCandQ
+// candidate quarters or more than kFusedCap survivors): the row is walked in
 // chunks of 16384 slots (wave w: pages 16w .. 16w+15 of the chunk, lane l:
 // slot l); each chunk's top-K (scores >= t1 when t1 is known) is appended in
 // position order to the running result in LDS, which is cut back to its top K
 // whenever it holds more.  Every element of the answer is in its chunk's
 // top-K, so nothing of it is lost.
-__global__ void __launch_bounds__(kFusedThreads)
-k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
-             const int32_t* kept, const int32_t* kept_count, int32_t* topk_out) {
-  __shared__ FusedShared sh;
-  const int row = blockIdx.x;
+__device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_batch& bt, int K,
+                         const float* scores, const float* page_qmax, const int32_t* kept,
+                         const int32_t* kept_count, int32_t* topk_out) {
   const int b = row / bt.R, r = row % bt.R;
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   const size_t mb = size_t(bt.max_blocks);
@@ -414,27 +411,27 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
       }
       lowest = max(t1, 1u);
 
-      // 2. candidate pages (maximum >= t1), listed in ascending kept order
-      // (page p = w*1024 + i*64 + l held by lane l).  With one value per page
-      // (lm = 0) the registers already hold these page maxima.
-      if (lm != 0) {
-#pragma unroll
-        for (int i = 0; i < kFusedPageLanes; ++i) {
-          const int p = w * (kFusedPageLanes * kWave) + i * kWave + l;
-          float v = -INFINITY;
-          if (p < cnt) {
-            const float4 x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
-            v = fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w));
-          }
-          pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
-        }
-      }
+      // 2. candidate quarters (quarter maximum >= t1), listed in ascending
+      // position order: lane l of wave w checks the 16 consecutive pages
+      // p = 1024 w + 16 l + i, and each page's quarters c with a maximum
+      // >= t1 become entries 4p + c, so one scan of the lanes' counts places
+      // every lane's entries.  Only those quarters can hold scores >= t1.
+      const float f1 = key_to_float(t1);
+      const int p_first = w * (kFusedPageLanes * kWave) + kFusedPageLanes * l;
+      int qbits[kFusedPageLanes];
       int mine = 0;
 #pragma unroll
-      for (int i = 0; i < kFusedPageLanes; ++i) mine += (pk[i] != 0u && pk[i] >= t1) ? 1 : 0;
-      mine = wave_sum(mine);
+      for (int i = 0; i < kFusedPageLanes; ++i) {
+        const int p = p_first + i;
+        float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (p < cnt) x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
+        qbits[i] = int(x.x >= f1) | (int(x.y >= f1) << 1) | (int(x.z >= f1) << 2) |
+                   (int(x.w >= f1) << 3);
+        mine += __popc(qbits[i]);
+      }
+      const int incl = wave_inclusive_sum(mine);
       __syncthreads();
-      if (l == 0) sh.scan[w] = mine;
+      if (l == kWave - 1) sh.scan[w] = incl;
       __syncthreads();
       int before = 0, ncand = 0;
 #pragma unroll
@@ -442,68 +439,69 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
         before += (i < w) ? sh.scan[i] : 0;
         ncand += sh.scan[i];
       }
-      if (ncand <= kFusedCandPages) {
+      if (ncand <= kFusedCandQ) {
+        int o = before + incl - mine;
 #pragma unroll
-        for (int i = 0; i < kFusedPageLanes; ++i) {
-          const bool sel = pk[i] != 0u && pk[i] >= t1;
-          const uint64_t bal = __ballot(sel);
-          if (sel)
-            sh.pages[before + ballot_rank(bal)] = w * (kFusedPageLanes * kWave) + i * kWave + l;
-          before += __popcll(bal);
-        }
-        __syncthreads();
-        // kept entries of the candidate pages, looked up in parallel
-        for (int c = tid; c < ncand; c += kFusedThreads) sh.pagej[c] = kb[sh.pages[c]];
+        for (int i = 0; i < kFusedPageLanes; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (qbits[i] & (1 << c)) sh.cq[o++] = 4 * (p_first + i) + c;
         __syncthreads();
 
-        // 3. survivors per candidate page.  Wave w scans the contiguous
-        // candidate range [c_lo, c_hi), kFusedBatch pages per step.  Each
-        // 16-lane row of the wave takes one page per load (lane l: slots
-        // 4(l%16) .. 4(l%16)+3 as one 16-byte load), so one load instruction
-        // covers 4 pages.  A slot survives if it is valid, causal and its
-        // score is >= t1 (compared as floats: the key order and the float
-        // order agree, with -0 = +0).
+        // 3. survivors per candidate quarter.  Wave w scans the contiguous
+        // candidate range [c_lo, c_hi), kFusedBatch quarters per step; each
+        // group of 4 lanes takes one quarter per load (lane l: slots
+        // 4(l%4) .. 4(l%4)+3 of it as one 16-byte load), so one load
+        // instruction covers 16 quarters.  A slot survives if it is valid,
+        // causal and its score is >= t1 (compared as floats: the key order
+        // and the float order agree, with -0 = +0).
         const int per_wave = (ncand + kFusedWaves - 1) / kFusedWaves;
         const int c_lo = min(ncand, w * per_wave), c_hi = min(ncand, c_lo + per_wave);
-        const float f1 = key_to_float(t1);
-        const int slot0 = 4 * (l & 15);
-        constexpr int kLoads = kFusedBatch / 4;
-        // lane's survivor flags (4 bits) for load i of the batch at c0
-        auto survivors = [&](int c0, int i, const float4& v, int* c_out, int* j_out) {
-          const int c = c0 + 4 * i + (l >> 4);
-          const int j = (c < c_hi) ? sh.pagej[c] : -1;
+        const int sub = 4 * (l & 3);
+        constexpr int kLoads = kFusedBatch / 16;
+        // lane's survivor flags (4 bits) for load i of the batch at c0, with
+        // the slot of its first element
+        auto survivors = [&](int c0, int i, const float4& v, int j, int* c_out, int* s_out) {
+          const int c = c0 + 16 * i + (l >> 2);
           *c_out = c;
-          *j_out = j;
-          const int lim = (j >= 0 && j < bt.max_blocks) ? qr - j * kBlock - slot0 : -1;
+          const int e = (c < c_hi) ? sh.cq[c] : 0;
+          const int slot = j * kBlock + 16 * (e & 3) + sub;
+          *s_out = slot;
+          const int lim = (c < c_hi && j >= 0 && j < bt.max_blocks) ? qr - slot : -1;
           return int(v.x >= f1 && lim >= 0) | (int(v.y >= f1 && lim >= 1) << 1) |
                  (int(v.z >= f1 && lim >= 2) << 2) | (int(v.w >= f1 && lim >= 3) << 3);
         };
-        auto load_batch = [&](int c0, float4* v) {
+        // scores and kept entries of a batch, all loads issued together
+        auto load_batch = [&](int c0, float4* v, int* jv) {
 #pragma unroll
           for (int i = 0; i < kLoads; ++i) {
-            const int c = c0 + 4 * i + (l >> 4);
-            const int p = (c < c_hi) ? sh.pages[c] : 0;
-            v[i] = *reinterpret_cast<const float4*>(sc + size_t(p) * kBlock + slot0);
+            const int c = c0 + 16 * i + (l >> 2);
+            const int e = (c < c_hi) ? sh.cq[c] : 0;
+            v[i] = *reinterpret_cast<const float4*>(sc + size_t(e >> 2) * kBlock + 16 * (e & 3) + sub);
+            jv[i] = kb[e >> 2];
           }
         };
-        // One pass counts each page's survivors and appends the survivors to
-        // the wave's slice sh.skey/spos[kSlice w, kSlice (w + 1)) in position
-        // order (lanes are in position order within a load, loads and
-        // batches ascend, and wave ranges follow one another), as long as
-        // they fit.  Gaps left in the slices hold key 0, which lds_topk reads
-        // as empty.
+        // One pass counts each quarter's survivors and appends the survivors
+        // to the wave's slice sh.skey/spos[kSlice w, kSlice (w + 1)) in
+        // position order (lanes are in position order within a load, loads
+        // and batches ascend, and wave ranges follow one another), as long
+        // as they fit.  Gaps left in the slices hold key 0, which lds_topk
+        // reads as empty.
         constexpr int kSlice = kFusedCap / kFusedWaves;              // 512
         int wave_n = 0;                                              // this wave's survivors so far
         for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
           float4 v[kLoads];
-          load_batch(c0, v);
+          int jv[kLoads];
+          load_batch(c0, v, jv);
 #pragma unroll
           for (int i = 0; i < kLoads; ++i) {
-            int c, j;
-            const int f = survivors(c0, i, v[i], &c, &j);
+            int c, slot;
+            const int f = survivors(c0, i, v[i], jv[i], &c, &slot);
             const int n = __popc(f);
-            const int tot = row_inclusive_sum(n);
-            if ((l & 15) == 15 && c < c_hi) sh.pcount[c] = tot;
+            // survivors of the quarter: sum over its 4 lanes (quad DPP)
+            int q = n + __builtin_amdgcn_update_dpp(0, n, kDppXor1, 0xF, 0xF, false);
+            q += __builtin_amdgcn_update_dpp(0, q, kDppXor2, 0xF, 0xF, false);
+            if ((l & 3) == 3 && c < c_hi) sh.qcount[c] = q;
             const int incl = wave_inclusive_sum(n);
             int o = wave_n + incl - n;
             const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -512,7 +510,7 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
               if (f & (1 << k)) {
                 if (o < kSlice) {
                   sh.skey[kSlice * w + o] = ord_key(vals[k]);
-                  sh.spos[kSlice * w + o] = j * kBlock + slot0 + k;
+                  sh.spos[kSlice * w + o] = slot + k;
                 }
                 ++o;
               }
@@ -541,23 +539,31 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
             return;
           }
           // 4'. a wave found more than its slice holds: offsets from the
-          // per-page counts, and a second read collects the survivors packed
-          block_exclusive_scan(sh.pcount, ncand, sh.scan);
+          // per-quarter counts, and a second read collects the survivors packed
+          block_exclusive_scan(sh.qcount, ncand, sh.scan);
           for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
             float4 v[kLoads];
-            load_batch(c0, v);
+            int jv[kLoads];
+            load_batch(c0, v, jv);
 #pragma unroll
             for (int i = 0; i < kLoads; ++i) {
-              int c, j;
-              const int f = survivors(c0, i, v[i], &c, &j);
+              int c, slot;
+              const int f = survivors(c0, i, v[i], jv[i], &c, &slot);
               const int n = __popc(f);
-              int o = row_inclusive_sum(n) - n + ((c < c_hi) ? sh.pcount[c] : 0);
+              // survivors of the earlier lanes of the same quarter (the DPP
+              // reads run on every lane, then each lane keeps its own terms)
+              const int d1 = __builtin_amdgcn_update_dpp(0, n, 0x111, 0xF, 0xF, true);  // row_shr:1
+              const int d2 = __builtin_amdgcn_update_dpp(0, n, 0x112, 0xF, 0xF, true);  // row_shr:2
+              const int d3 = __builtin_amdgcn_update_dpp(0, n, 0x113, 0xF, 0xF, true);  // row_shr:3
+              const int qi = l & 3;
+              const int pre = (qi >= 1 ? d1 : 0) + (qi >= 2 ? d2 : 0) + (qi == 3 ? d3 : 0);
+              int o = pre + ((c < c_hi) ? sh.qcount[c] : 0);
               const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 if (f & (1 << k)) {
                   sh.skey[o] = ord_key(vals[k]);
-                  sh.spos[o] = j * kBlock + slot0 + k;
+                  sh.spos[o] = slot + k;
                   ++o;
                 }
               }
@@ -642,6 +648,35 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
     if (n_run > K) n_run = lds_topk(sh, n_run, n_run, K, nullptr);
   }
   lds_topk(sh, n_run, n_run, K, out);
+}
+
+// grid (rows), 1024 threads: the whole top-k of row blockIdx.x.  With
+// `arrivals`, each workgroup first adds 1 to it (the gate of the round's
+// tail waits for every one of them).
+__global__ void __launch_bounds__(kFusedThreads)
+k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
+             const int32_t* kept, const int32_t* kept_count, int32_t* topk_out,
+             unsigned long long* arrivals) {
+  __shared__ FusedShared sh;
+  if (arrivals && threadIdx.x == 0)
+    __hip_atomic_fetch_add(arrivals, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  topk_row(sh, blockIdx.x, bt, K, scores, page_qmax, kept, kept_count, topk_out);
+}
+
+// One wave that waits until `arrivals` reaches `target` (every workgroup of
+// the gated top-k launch has started), polling the device-scope counter with
+// vector loads, or until max_ticks of the 100 MHz device clock have passed;
+// the update queued behind it on another stream then never takes the CUs
+// the top-k needs.  The wait is bounded, so a top-k that cannot start only
+// delays the update.
+__global__ void __launch_bounds__(kWave)
+k_gate(const unsigned long long* arrivals, unsigned long long target, uint64_t max_ticks) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = wall_clock64();
+  while (__hip_atomic_load(arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (wall_clock64() - t0 > max_ticks) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // grid (rows, chunks of this level).
@@ -847,7 +882,7 @@ hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, cons
   }
   if (page_qmax) {
     hipLaunchKernelGGL(k_topk_fused, dim3(rows), dim3(kFusedThreads), 0, s, bt, topk, scores,
-                       page_qmax, kept, kept_count, out);
+                       page_qmax, kept, kept_count, out, nullptr);
     return hipGetLastError();
   }
   LevelArgs a;
@@ -880,6 +915,22 @@ hipError_t launch_topk(const spin_batch& bt, int topk, const float* scores, cons
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_topk_gated(const spin_batch& bt, int topk, const float* scores,
+                             const float* page_qmax, const int32_t* kept,
+                             const int32_t* kept_count, int32_t* out,
+                             unsigned long long* arrivals, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk_fused, dim3(bt.B * bt.R), dim3(kFusedThreads), 0, s, bt, topk,
+                     scores, page_qmax, kept, kept_count, out, arrivals);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(const unsigned long long* arrivals, unsigned long long target,
+                       hipStream_t s) {
+  // at most 2 ms of the 100 MHz device clock
+  hipLaunchKernelGGL(k_gate, dim3(1), dim3(kWave), 0, s, arrivals, target, uint64_t(200000));
+  return hipGetLastError();
 }
 
 hipError_t launch_miss(const spin_batch& bt, int topk, const int32_t* full_topk,

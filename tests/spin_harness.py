@@ -165,3 +165,20 @@ def predicted_sets_tie_only(ost_before, q, R, keep_bp, explore_bp, gpu_pred, ref
         theta = np.sort(S)[::-1][p - 1]
         near |= {j for j in gp ^ rp if j < len(S) and abs(S[j] - theta) <= rel * abs(theta)}
     return near == gp ^ rp
+
+
+class StateView:
+    """The injectable parts (V, D, VB, step) of a bound SpinState, for
+    sync_from_oracle outside a Rig."""
+
+    def __init__(self, st):
+        self.state = st
+
+    def inject(self, layer, b, V, D, step):
+        Vs, Ds, VBs, St = self.state.V(), self.state.D(), self.state.VB(), self.state.step()
+        Vs[layer, b] = torch.as_tensor(V, dtype=torch.float32)
+        Ds[layer, b] = torch.as_tensor(D, dtype=torch.float32)
+        nb = self.state.layout["max_blocks"]
+        pad = torch.full((nb * BLOCK - Vs.shape[2],), NEG, device=Vs.device)
+        VBs[layer, b] = torch.cat([Vs[layer, b], pad]).view(nb, BLOCK).amax(dim=1)
+        St[layer, b] = int(step)

@@ -1,5 +1,6 @@
 """Full-size parity: the 512K-token, batch-96 serving round in the launch
-configuration the benchmark times, with sampled requests checked against the
+configuration the benchmark times (the tail is spin_topk_update: the top-k
+and the EMA update in one launch), with sampled requests checked against the
 oracle (which runs the same two rounds from its own state)."""
 import numpy as np
 import pytest
@@ -8,7 +9,8 @@ import torch
 import predictive_kv_block_amd as spin
 from oracle import spin_oracle as O
 from tests.spin_harness import (assert_scores_close, assert_topk_tie_aware, np_,
-                                oracle_fp8_operands, score_mag, score_tol)
+                                oracle_fp8_operands, predicted_sets_tie_only, score_mag,
+                                score_tol, StateView, sync_from_oracle)
 from workload import WORKLOADS, make_pool, make_queries
 
 pytestmark = pytest.mark.gpu
@@ -27,8 +29,8 @@ def _round(st, bufs, pool, q, w, keep_bp):
     spin.spin_quantize_q(st.handle, b["batch"], q, w)
     spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
                              pool.block_table, b["kept"], b["cnt"], b["scores"], b["pq"])
-    spin.spin_topk_scores(b["batch"], st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
-                          b["topk_ws"], b["pq"])
+    spin.spin_topk_update(st.handle, 0, b["batch"], b["scores"], b["pq"], b["kept"], b["cnt"],
+                          b["topk"])
 
 
 @pytest.mark.timeout(600)
@@ -54,7 +56,9 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
                                   dtype=torch.uint8, device=DEV)
     q0 = wl.ctx - 2
     osts = {b: O.RequestState(wl.ctx, request_id=1000 + b) for b in SAMPLE}
-    live = set(SAMPLE)
+    view = StateView(st)
+    synced = set()
+    compared = 0
     tables = np_(pool.block_table)
     for t, keep_bp in enumerate((10000, 5000)):
         q = q0 + t
@@ -67,7 +71,8 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
         cnt = np_(bufs["cnt"])
         if keep_bp == 5000:
             assert np.all(cnt == 4096)                       # ceil(0.5 * 8192)
-        for b in sorted(live):
+        synced.clear()
+        for b in SAMPLE:
             n = int(cnt[b])
             gk = np_(bufs["kept"][b, :n]).astype(np.int64)
             pages = tables[b]
@@ -83,18 +88,20 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
             before = osts[b].copy()
             ref = O.decode_round(osts[b], q, 1, keep_bp, wl.explore_bp, cfg.seed, 0, qv, wv,
                                  kv_small, sc_small, table_small, wl.topk, wl.alpha)
-            if not np.array_equal(gk, ref["kept"]):
-                # fp32 vs fp64 state: accepted only as a tie at the predicted-set threshold
-                S = O.block_scores(before.V, before.D, q)
-                kb_, ne_, p_ = O.budget(keep_bp, len(S), wl.explore_bp)
-                theta = np.sort(S)[::-1][p_ - 1]
-                gp = set(np.nonzero(np_(bufs["flags"][b]) == 1)[0].tolist())
+            gflags = np_(bufs["flags"][b])[: len(ref["flags"])]
+            if not (np.array_equal(gk, ref["kept"]) and np.array_equal(gflags, ref["flags"])):
+                # fp32 vs fp64 state: accepted only as a tie at the predicted-set
+                # threshold; the oracle's state (rounded to fp32) is then
+                # written into the GPU slot and the request stays compared
+                gp = set(np.nonzero(gflags == 1)[0].tolist())
                 rp = set(np.nonzero(ref["flags"] == 1)[0].tolist())
-                assert gp != rp and all(abs(S[j] - theta) <= 2e-3 * abs(theta) for j in gp ^ rp), \
+                assert predicted_sets_tie_only(before, q, 1, keep_bp, wl.explore_bp, gp, rp), \
                     f"round {t} b{b}: kept blocks differ beyond a threshold tie"
-                _say("tolerated threshold tie", t, b)
-                live.discard(b)
+                _say("tolerated threshold tie", t, b, "-> oracle state synced")
+                sync_from_oracle(view, 0, b, osts[b])
+                synced.add(b)
                 continue
+            compared += 1
             gs = np_(g_scores[b, :, : n * 64]).astype(np.float64)
             mag = score_mag(qv, wv, kv_small, sc_small, table_small, gk)
             assert_scores_close(gs, ref["scores"], mag, f"round {t} b{b}")
@@ -107,9 +114,7 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
             pt = np_(bufs["pq"][b, 0, :n])
             own = np_(g_scores[b, 0, : n * 64]).reshape(n, 4, 16).max(axis=2)
             assert np.array_equal(pt, own)
-        spin.spin_update(st.handle, 0, bufs["batch"], bufs["scores"], bufs["kept"], bufs["cnt"])
-        torch.cuda.synchronize()
-        for b in sorted(live):
+        for b in SAMPLE:
             V = np_(st.V()[0, b]).astype(np.float64)
             D = np_(st.D()[0, b]).astype(np.float64)
             scale = float(np.nanmax(np.abs(osts[b].V[np.isfinite(osts[b].V)])))
@@ -119,4 +124,4 @@ def test_ctx512k_b96_two_rounds_sampled(gpu_lib):
                 assert np.all(np.abs(g[fin] - r[fin]) <= np.maximum(1e-3 * np.abs(r[fin]),
                                                                     1e-5 * scale)), (name, t, b)
     assert st.error() == 0
-    assert len(live) >= 2
+    assert compared >= 4

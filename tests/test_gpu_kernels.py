@@ -247,15 +247,20 @@ def test_topk_exact_on_identical_scores(gpu_lib, case):
                 v = np.where(slot <= qpos[b] + r, sc[b, r, : nk * 64].reshape(nk, 64), -np.inf)
                 pmh[b, r, :nk] = v.reshape(nk, 4, 16).max(axis=2)
         pm = torch.as_tensor(pmh, device=DEV)
-    _say("topk", case)
-    spin.spin_topk_scores(bt, K, torch.as_tensor(sc, device=DEV), kept_d, cnt_d, out, ws, pm)
-    torch.cuda.synchronize()
-    got = np_(out)
-    for b in range(B):
-        for r in range(R):
-            ref = O.topk_positions(sc[b, r, : len(kept[b]) * 64].astype(np.float64), kept[b],
-                                   int(qpos[b]) + r, K)
-            assert np.array_equal(got[b, r], ref), (case, b, r)
+    refs = {(b, r): O.topk_positions(sc[b, r, : len(kept[b]) * 64].astype(np.float64), kept[b],
+                                     int(qpos[b]) + r, K) for b in range(B) for r in range(R)}
+    # with quarter maxima: the collected path (rows spread over workgroups,
+    # survivors in the workspace) and the one-workgroup-per-row path
+    for workspace in ((ws, None) if pm is not None else (ws,)):
+        _say("topk", case, "workspace" if workspace is not None else "no workspace")
+        out.fill_(-7)
+        spin.spin_topk_scores(bt, K, torch.as_tensor(sc, device=DEV), kept_d, cnt_d, out,
+                              workspace, pm)
+        torch.cuda.synchronize()
+        got = np_(out)
+        for b in range(B):
+            for r in range(R):
+                assert np.array_equal(got[b, r], refs[(b, r)]), (case, b, r, workspace is None)
 
 
 # --------------------------------------------------------------- predictor

@@ -1,8 +1,12 @@
-"""The benchmark's overlapped round (quantiser beside the predictor, EMA update
-beside the top-k on a second stream, a spin before the update) against the same
-calls issued one after another on one stream: every output and the whole
-state must be bit-identical, round after round.  A missing dependency between
-the two streams would show up here as a difference."""
+"""The benchmark's round (quantiser beside the predictor on a second stream,
+the library's spin_topk_update tail with the EMA update beside the top-k on
+that stream, behind the library's gate) against the same calls issued one
+after another on one stream: every output and the whole state must be
+bit-identical, round after round, with a host synchronisation after every
+round and without any (the rounds' outputs then copied on the stream).  A
+missing dependency between the streams or between rounds would show up here
+as a difference.  Also: spin_topk_update equals spin_topk_scores followed by
+spin_update / spin_mtp_replay, bit for bit."""
 import dataclasses
 
 import numpy as np
@@ -12,7 +16,7 @@ import torch
 import bench
 import predictive_kv_block_amd as spin
 from tests.spin_harness import np_
-from workload import WORKLOADS, make_queries, positions
+from workload import WORKLOADS, acceptances, make_queries, positions
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,12 +32,18 @@ def _serial_round(st, b, pool, q, w, keep_bp):
     spin.spin_update(st.handle, 0, b["batch"], b["scores"], b["kept"], b["cnt"])
 
 
-def _snapshot(st, b):
-    n = np_(b["cnt"]).copy()
-    return dict(kept=np_(b["kept"]).copy(), cnt=n, flags=np_(b["flags"]).copy(),
-                scores=np_(b["scores"]).copy(), pq=np_(b["pq"]).copy(),
-                topk=np_(b["topk"]).copy(), V=np_(st.V()).copy(), D=np_(st.D()).copy(),
-                VB=np_(st.VB()).copy(), step=np_(st.step()).copy())
+_KEYS = ("kept", "cnt", "flags", "scores", "pq", "topk")
+
+
+def _snapshot_dev(st, b):
+    """Copies of a round's outputs and the state, enqueued on the current stream."""
+    d = {k: b[k].clone() for k in _KEYS}
+    d.update(V=st.V().clone(), D=st.D().clone(), VB=st.VB().clone(), step=st.step().clone())
+    return d
+
+
+def _host(d):
+    return {k: np_(v).copy() for k, v in d.items()}
 
 
 def _masked_scores(s, cnt):
@@ -44,35 +54,97 @@ def _masked_scores(s, cnt):
     return out
 
 
-def test_overlapped_round_equals_serial(gpu_lib):
+def _same(a, b, t):
+    assert np.array_equal(a["cnt"], b["cnt"]), t
+    for k in ("kept", "flags", "topk", "V", "D", "VB", "step"):
+        assert np.array_equal(a[k], b[k]), (t, k)
+    assert np.array_equal(_masked_scores(a["scores"], a["cnt"]),
+                          _masked_scores(b["scores"], b["cnt"])), (t, "scores")
+    for bi, c in enumerate(a["cnt"]):
+        assert np.array_equal(a["pq"][bi, :, : int(c)], b["pq"][bi, :, : int(c)]), (t, "pq")
+
+
+def test_benchmark_round_equals_serial(gpu_lib):
     wl = dataclasses.replace(WORKLOADS["ctx94k-b8"], steps=6)
     qp = np_(positions(wl))
-    runs = []
-    for mode in ("serial", "overlapped"):
+    runs = {}
+    for mode in ("serial", "bench-synced", "bench-unsynced"):
         print("[case] stream plan", mode, flush=True)
         spin_, pool, cfg, st, bufs, _ = bench._setup(wl, DEV)
         side = torch.cuda.Stream(device=DEV)
-        bench.SPACER_CYCLES = 4000
+        qs = [make_queries(wl, pool, 0, t, qp[t].tolist(), device=DEV) for t in range(wl.steps)]
+        qpos = [torch.as_tensor(qp[t].astype(np.int32), device=DEV) for t in range(wl.steps)]
+        torch.cuda.synchronize()
         done = None
         snaps = []
         for t in range(wl.steps):
             keep = 10000 if t == 0 else 5000
-            bufs["qpos"].copy_(torch.as_tensor(qp[t].astype(np.int32), device=DEV))
-            qb, w = make_queries(wl, pool, 0, t, qp[t].tolist(), device=DEV)
+            bufs["qpos"].copy_(qpos[t])
             if mode == "serial":
-                _serial_round(st, bufs, pool, qb, w, keep)
+                _serial_round(st, bufs, pool, qs[t][0], qs[t][1], keep)
             else:
-                done = bench._round(spin, st, bufs, pool, qb, w, keep, side, done)
-            torch.cuda.synchronize()
-            snaps.append(_snapshot(st, bufs))
+                done = bench._round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep, side, done)
+            if mode == "bench-unsynced":
+                snaps.append(_snapshot_dev(st, bufs))     # on the stream, no host wait
+            else:
+                torch.cuda.synchronize()
+                snaps.append(_host(_snapshot_dev(st, bufs)))
+        torch.cuda.synchronize()
+        if mode == "bench-unsynced":
+            snaps = [_host(d) for d in snaps]
         assert st.error() == 0
-        runs.append(snaps)
-        bench.SPACER_CYCLES = 0
-    for t, (a, b) in enumerate(zip(*runs)):
-        assert np.array_equal(a["cnt"], b["cnt"]), t
-        for k in ("kept", "flags", "topk", "V", "D", "VB", "step"):
-            assert np.array_equal(a[k], b[k]), (t, k)
-        assert np.array_equal(_masked_scores(a["scores"], a["cnt"]),
-                              _masked_scores(b["scores"], b["cnt"])), (t, "scores")
-        for bi, c in enumerate(a["cnt"]):
-            assert np.array_equal(a["pq"][bi, :, : int(c)], b["pq"][bi, :, : int(c)]), (t, "pq")
+        runs[mode] = snaps
+    for mode in ("bench-synced", "bench-unsynced"):
+        for t, (a, b) in enumerate(zip(runs["serial"], runs[mode])):
+            _same(a, b, (mode, t))
+
+
+@pytest.mark.parametrize("R", [1, 4])
+def test_topk_update_equals_separate_calls(gpu_lib, R):
+    base = WORKLOADS["ctx94k-b8"] if R == 1 else WORKLOADS["mtp-ctx256k-b32"]
+    wl = dataclasses.replace(base, batch=3, ctx=64 * 300, steps=4, layers=1)
+    acc = np_(acceptances(wl)) if R > 1 else None
+    qp = np_(positions(wl, torch.as_tensor(acc) if acc is not None else None))
+    outs = {}
+    side = torch.cuda.Stream(device=DEV)
+    for mode in ("separate", "one stream", "two streams"):
+        print("[case] tail", mode, "R", R, flush=True)
+        spin_, pool, cfg, st, bufs, _ = bench._setup(wl, DEV)
+        outs[mode] = []
+        for t in range(wl.steps):
+            keep = 10000 if t == 0 else 5000
+            bufs["qpos"].copy_(torch.as_tensor(qp[t].astype(np.int32), device=DEV))
+            q, w = make_queries(wl, pool, 0, t, qp[t].tolist(), device=DEV)
+            a_dev = (torch.as_tensor(acc[t].astype(np.int32), device=DEV) if acc is not None
+                     else None)
+            spin.spin_predict_blocks(st.handle, 0, bufs["batch"], keep, bufs["kept"], bufs["cnt"],
+                                     bufs["flags"])
+            spin.spin_quantize_q(st.handle, bufs["batch"], q, w)
+            spin.spin_indexer_scores(st.handle, bufs["batch"], pool.key_codes, pool.key_scale,
+                                     pool.block_table, bufs["kept"], bufs["cnt"], bufs["scores"],
+                                     bufs["pq"])
+            if mode == "separate":
+                spin.spin_topk_scores(bufs["batch"], cfg.topk, bufs["scores"], bufs["kept"],
+                                      bufs["cnt"], bufs["topk"], bufs["topk_ws"], bufs["pq"])
+                if a_dev is None:
+                    spin.spin_update(st.handle, 0, bufs["batch"], bufs["scores"], bufs["kept"],
+                                     bufs["cnt"])
+                else:
+                    spin.spin_mtp_replay(st.handle, 0, bufs["batch"], a_dev, bufs["scores"],
+                                         bufs["kept"], bufs["cnt"])
+            else:
+                spin.spin_topk_update(st.handle, 0, bufs["batch"], bufs["scores"], bufs["pq"],
+                                      bufs["kept"], bufs["cnt"], bufs["topk"], a_dev,
+                                      update_stream=side if mode == "two streams" else None)
+            torch.cuda.synchronize()
+            outs[mode].append((np_(bufs["topk"]).copy(), np_(st.V()).copy(), np_(st.D()).copy(),
+                               np_(st.VB()).copy(), np_(st.step()).copy()))
+        assert st.error() == 0
+        if mode == "two streams":
+            # every gated top-k workgroup was counted: B * R per round
+            gate = int(st.region("tail_gate", torch.int64, (1,)).item())
+            assert gate == wl.steps * wl.batch * R
+    for mode in ("one stream", "two streams"):
+        for t, (x, y) in enumerate(zip(outs["separate"], outs[mode])):
+            for i, name in enumerate(("topk", "V", "D", "VB", "step")):
+                assert np.array_equal(x[i], y[i]), (R, mode, t, name)
