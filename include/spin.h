@@ -58,7 +58,8 @@ enum {
   SPIN_EINVAL = -1,       /* null pointer, bad size, layer/rows out of range */
   SPIN_EUNSUPPORTED = -2, /* valid configuration this library does not build */
   SPIN_EHIP = -3,         /* a HIP launch failed; see spin_status_string */
-  SPIN_ESTATE = -4        /* state buffer too small or config mismatch */
+  SPIN_ESTATE = -4,       /* state buffer too small or config mismatch */
+  SPIN_ESCRATCH = -5      /* needs more than the library's static device scratch */
 };
 
 /* Bits of the device error word. */
@@ -251,6 +252,21 @@ int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
                      const float* page_qmax, const int32_t* kept_blocks, const int32_t* kept_count,
                      int32_t* topk_out, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * spin_topk_scores without a workspace argument.  The chunked path (no
+ * page_qmax) keeps its survivors in a static device array of the library,
+ * 32 MiB per device, held by each device the library runs on until the
+ * process ends; a batch whose chunked path needs more (see
+ * spin_topk_workspace_bytes) is rejected with SPIN_ESCRATCH before anything
+ * is enqueued.  With page_qmax the top-k needs no scratch.  Every call on a
+ * device shares that device's array: calls that overlap on one device (on
+ * different streams, or from different threads) race and must not be made.
+ * Results are those of spin_topk_scores. */
+int spin_topk_scores_noalloc(const spin_batch* batch, int topk, const float* scores,
+                             const float* page_qmax, const int32_t* kept_blocks,
+                             const int32_t* kept_count, int32_t* topk_out, hipStream_t stream);
 
 /* spin_quantize_q + spin_indexer_scores + spin_topk_scores with the state's
  * top-k K, the state's page-max and top-k workspaces.  `scores` must stay alive until spin_update / spin_mtp_replay

@@ -15,7 +15,8 @@ __all__ = [
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_topk_update", "spin_measure_miss", "spin_allocate_budgets",
     "spin_status_string", "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
-    "spin_attention_workspace_bytes", "spin_sparse_attention", "EXPORTS",
+    "spin_attention_workspace_bytes", "spin_sparse_attention", "spin_topk_scores_noalloc",
+    "EXPORTS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so")
@@ -26,10 +27,10 @@ EXPORTS = [
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_topk_update", "spin_measure_miss", "spin_allocate_budgets",
     "spin_status_string", "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
-    "spin_attention_workspace_bytes", "spin_sparse_attention",
+    "spin_attention_workspace_bytes", "spin_sparse_attention", "spin_topk_scores_noalloc",
 ]
 
-SPIN_OK, SPIN_EINVAL, SPIN_EUNSUPPORTED, SPIN_EHIP, SPIN_ESTATE = 0, -1, -2, -3, -4
+SPIN_OK, SPIN_EINVAL, SPIN_EUNSUPPORTED, SPIN_EHIP, SPIN_ESTATE, SPIN_ESCRATCH = 0, -1, -2, -3, -4, -5
 ERR_QPOS, ERR_SLOT, ERR_KEPT, ERR_PAGE, ERR_ACCEPT = 1, 2, 4, 8, 16
 
 
@@ -78,6 +79,7 @@ _SIGS = {
                             _vp],
     "spin_topk_scores": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "spin_topk_workspace_bytes": [ctypes.POINTER(SpinBatch), _i32, ctypes.POINTER(_sz)],
+    "spin_topk_scores_noalloc": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "spin_indexer_topk": [_vp, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                           _vp, _vp, _vp],
     "spin_update": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp, _vp, _vp],
@@ -214,6 +216,14 @@ def spin_topk_scores(batch, topk, scores, kept_blocks, kept_count, topk_out, wor
     _check(load().spin_topk_scores(ctypes.byref(batch), int(topk), _p(scores), _p(page_qmax),
                                    _p(kept_blocks), _p(kept_count), _p(topk_out), _p(workspace),
                                    nbytes, _stream(stream)))
+
+
+def spin_topk_scores_noalloc(batch, topk, scores, kept_blocks, kept_count, topk_out,
+                             page_qmax=None, stream=None):
+    """spin_topk_scores with the library's static device scratch (no workspace)."""
+    _check(load().spin_topk_scores_noalloc(ctypes.byref(batch), int(topk), _p(scores),
+                                           _p(page_qmax), _p(kept_blocks), _p(kept_count),
+                                           _p(topk_out), _stream(stream)))
 
 
 def spin_indexer_topk(h, batch, q_bf16, w, k_pool, k_scale, block_table, kept_blocks,

@@ -239,6 +239,33 @@ int spin_topk_scores(const spin_batch* batch, int topk, const float* scores,
                                       topk_out, workspace, stream));
 }
 
+int spin_topk_scores_noalloc(const spin_batch* batch, int topk, const float* scores,
+                             const float* page_qmax, const int32_t* kept_blocks,
+                             const int32_t* kept_count, int32_t* topk_out, hipStream_t stream) {
+  int rc = check_plain_batch(batch);
+  if (rc) return rc;
+  if (topk < 1 || topk > 4096 || topk % 4 != 0 || !scores || !kept_blocks || !kept_count ||
+      !topk_out)
+    return SPIN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(page_qmax) % 16 != 0)
+    return SPIN_EINVAL;
+  void* ws = nullptr;
+  size_t cap = 0;
+  rc = hip_status(spin::noalloc_scratch(&ws, &cap));
+  if (rc) return rc;
+  const spin::TopkPlan p = spin::topk_plan(batch->B * batch->R, batch->max_blocks, topk);
+  if (!page_qmax && p.levels > 1 && p.bytes > cap) {
+    snprintf(g_status, sizeof(g_status),
+             "spin_topk_scores_noalloc: this batch needs %zu bytes of scratch, more than the "
+             "%zu bytes of the library's static scratch",
+             p.bytes, cap);
+    return SPIN_ESCRATCH;
+  }
+  return hip_status(spin::launch_topk(*batch, topk, scores, page_qmax, kept_blocks, kept_count,
+                                      topk_out, ws, stream));
+}
+
 int spin_indexer_topk(spin_state* st, const spin_batch* batch, const void* q_bf16, const float* w,
                       const uint8_t* k_pool, const float* k_scale, int64_t pool_pages,
                       const int32_t* block_table, const int32_t* kept_blocks,
@@ -461,6 +488,8 @@ const char* spin_status_string(int status) {
     case SPIN_EUNSUPPORTED: return "unsupported configuration (block 64, 64 heads x 128, rows <= 4)";
     case SPIN_EHIP: return g_status[0] ? g_status : "HIP error";
     case SPIN_ESTATE: return "state buffer too small or mismatched";
+    case SPIN_ESCRATCH:
+      return g_status[0] ? g_status : "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

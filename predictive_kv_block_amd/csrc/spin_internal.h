@@ -52,6 +52,9 @@ struct TopkPlan {
 };
 TopkPlan topk_plan(int rows, int max_blocks, int K);
 
+// This device's static scratch of spin_topk_scores_noalloc and its size.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 hipError_t launch_fill_state(const SpinView& v, hipStream_t s);
 hipError_t launch_reset_slots(const SpinView& v, int n, const int32_t* slots,
                               const uint64_t* rids, hipStream_t s);

@@ -26,6 +26,8 @@
 //    that level writes the answer ascending, padded with -1.
 //
 // k_miss: share of an all-keep top-k that falls in skipped blocks.
+#include <atomic>
+
 #include "spin_device.h"
 #include "spin_internal.h"
 
@@ -838,7 +840,35 @@ k_miss(spin_batch bt, int K, const int32_t* full, const uint8_t* flags, float* m
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Device scratch of spin_topk_scores_noalloc (the chunked levels' survivor
+// buffers), for callers that cannot allocate.  Each device holds its own copy
+// for the life of the process.  In host code `scratch` only names the array:
+// its device address comes from hipGetSymbolAddress, per device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 }  // namespace
+
+// Device address of this device's `scratch`, looked up on the first call on
+// each device (with that device current) and kept.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  *bytes = kNoAllocScratchBytes;
+  return hipSuccess;
+}
 
 TopkPlan topk_plan(int rows, int max_blocks, int K) {
   TopkPlan p;
