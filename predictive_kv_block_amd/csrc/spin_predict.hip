@@ -7,11 +7,16 @@
 //       S_j = max over existing slots i of block j of max(V_i, D_{q-i}).
 //       For a block wholly at or before q this equals max(VB_j, max of the
 //       D window), where VB_j (the block max of V) is kept exact by the update
-//       kernel; the partial last block reads V directly.
-//   k_select        (one 1024-thread workgroup per request)
-//       per row: budget, radix-select of the top-P blocks (ties -> lower j),
-//       radix-select of the n_exp explored blocks with the smallest Philox
-//       words among the rest; union over rows; ascending compaction.
+//       kernel; the partial last block reads V directly.  The row-0
+//       workgroups also write the request's Philox exploration words (ALU work
+//       under the D loads).
+//   k_select_regs   (one 1024-thread workgroup per request, or per (request,
+//                    row) under the union policy; up to 16384 blocks)
+//       each thread holds NPL blocks' keys in registers: radix-select of the
+//       top-P blocks (ties -> lower j), radix-select of the n_exp explored
+//       blocks with the smallest Philox words among the rest, ballot
+//       compaction of the kept list.  k_select does the same from global
+//       memory for longer contexts.
 #include "spin_device.h"
 #include "spin_internal.h"
 #include "spin_select.h"
@@ -28,7 +33,7 @@ constexpr int kScoreBatchesPerWave = SPIN_SCORE_BATCHES;
 constexpr int kScoreBlocksPerWave = kScoreBatch * kScoreBatchesPerWave;   // 128
 static_assert(kScoreBatchesPerWave % 2 == 0, "double-buffered batches");
 constexpr int kSelectThreads = 1024;
-constexpr size_t kResidentLdsMax = 150 * 1024;   // dynamic LDS for the resident selection
+constexpr int kSelectRegsMax = 16 * kSelectThreads;   // blocks the register-resident selection holds
 
 __device__ __forceinline__ void budget(int keep_bp, int n, int explore_bp, int* kb, int* nexp) {
   const int k = int((int64_t(keep_bp) * n + 9999) / 10000);
@@ -43,12 +48,29 @@ __device__ __forceinline__ bool request_ok(const SpinView& v, const spin_batch& 
          num_blocks_of(q0 + bt.R - 1) <= bt.max_blocks && bt.max_blocks <= v.max_blocks;
 }
 
+// Exploration words, shared by every row of a request:
+// u_j = Philox(counter (j/4, step, request id, 0), key (seed, layer)) word j%4,
+// for j < n_last.  A wave writes blocks [j0, j0 + count) (j0 and count
+// multiples of 4), lane g taking group j0/4 + g.
+__device__ __forceinline__ void explore_words(const SpinView& v, int layer, int b, int s, int step,
+                                              int j0, int count, int n_last) {
+  const int g = j0 / 4 + lane_id();
+  if (lane_id() >= count / 4 || 4 * g >= n_last) return;
+  const Philox4x64 p = philox4x64_10(uint64_t(g), uint64_t(step), v.rid[s], 0ull, v.seed,
+                                     uint64_t(layer));
+  uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (4 * g + k < n_last) u[4 * g + k] = p.w[k];
+}
+
 // grid (ceil(max_blocks / (W * kScoreBlocksPerWave)), B, R), W waves: wave w
 // of workgroup x scores the kScoreBlocksPerWave consecutive blocks from
 // (x*W + w) * kScoreBlocksPerWave, in batches of kScoreBatch with the next
 // batch's loads in flight while the current one is reduced.  Every batch
 // issues the same loads (blocks past the last full one are masked).  The
 // partial block holding q (if any) is scored apart from V and D directly.
+// Row-0 waves also write the exploration words of their blocks.
 __global__ void __launch_bounds__(kScoreWaves * kWave)
 k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int b = blockIdx.y, r = blockIdx.z;
@@ -56,15 +78,20 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int q0 = bt.qpos[b];
   if (!request_ok(v, bt, s, q0)) return;
   const size_t row = size_t(layer) * v.S + s;
-  if (v.step[row] < v.warmup || keep_bp >= 10000) return;
+  const int step = v.step[row];
+  if (step < v.warmup || keep_bp >= 10000) return;
   const int q = q0 + r;
   const int n = num_blocks_of(q);
+  const int n_last = num_blocks_of(q0 + bt.R - 1);
   int kb, nexp;
   budget(keep_bp, n, v.explore_bp, &kb, &nexp);
-  if (kb >= n) return;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int jw = (blockIdx.x * kScoreWaves + wave) * kScoreBlocksPerWave;
-  if (jw >= n) return;
+  const bool words = r == 0 && v.explore_bp > 0 && jw < n_last;
+  if (kb >= n || jw >= n) {
+    if (words) explore_words(v, layer, b, s, step, jw, kScoreBlocksPerWave, n_last);
+    return;
+  }
 
   const float* V = v.V + row * v.max_ctx;
   const float* D = v.D + row * v.max_ctx;
@@ -116,6 +143,8 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
 #pragma unroll
   for (int t = 0; t < kScoreBatchesPerWave; t += 2) {
     issue(1, t + 1);
+    // the exploration words while the first two batches are in flight
+    if (t == 0 && words) explore_words(v, layer, b, s, step, jw, kScoreBlocksPerWave, n_last);
     reduce(0, t);
     if (t + 2 < kScoreBatchesPerWave) issue(0, t + 2);
     reduce(1, t + 1);
@@ -155,9 +184,14 @@ k_block_scores_pool(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int q0 = bt.qpos[b];
   if (!request_ok(v, bt, s, q0)) return;
   const size_t row = size_t(layer) * v.S + s;
-  if (v.step[row] < v.warmup || keep_bp >= 10000) return;
+  const int step = v.step[row];
+  if (step < v.warmup || keep_bp >= 10000) return;
   const int q = q0 + r;
   const int n = num_blocks_of(q);
+  const int n_last = num_blocks_of(q0 + bt.R - 1);
+  const int jw = (blockIdx.x * kScoreWaves + threadIdx.x / kWave) * kPoolBlocksPerWave;
+  if (r == 0 && v.explore_bp > 0 && jw < n_last)
+    explore_words(v, layer, b, s, step, jw, kPoolBlocksPerWave, n_last);
   int kb, nexp;
   budget(keep_bp, n, v.explore_bp, &kb, &nexp);
   if (kb >= n) return;
@@ -165,7 +199,6 @@ k_block_scores_pool(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const float* D = v.D + row * v.max_ctx;
   float* out = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
   const int l = lane_id();
-  const int jw = (blockIdx.x * kScoreWaves + threadIdx.x / kWave) * kPoolBlocksPerWave;
   for (int m = 0; m < kPoolBlocksPerWave; ++m) {
     const int j = jw + m;
     if (j >= n) break;
@@ -223,84 +256,183 @@ struct KeptSrc {
   }
 };
 
-// Flags in LDS: bit 0 predicted by some row, bit 1 explored by some row,
-// bit 2 predicted by the current row.  With RESIDENT, the row's block scores
-// and the exploration words also live in LDS (dynamic LDS = 13 B per block);
-// otherwise the selection reads them from the state's workspace.
-// grid (B) with per_row = 0: the workgroup runs every row of its request and
-// writes the union.  grid (B, R) with per_row = 1: workgroup (b, r) runs row r
-// alone and leaves its flags (bit 0 predicted, bit 1 explored; 0 past the
-// row's last block) as bytes in the row's block-score workspace, which it has
-// finished reading; k_select_union then forms the union.
-template <bool RESIDENT>
+// Invalid request arguments: the whole-request workgroup clears its outputs
+// and flags the error (the per-row workgroups leave that to k_select_union).
+__device__ bool reject_request(const SpinView& v, const spin_batch& bt, int s, int q0,
+                               int per_row, uint8_t* fo, int32_t* kept_count, int b) {
+  if (request_ok(v, bt, s, q0)) return false;
+  if (per_row) return true;
+  for (int j = threadIdx.x; j < bt.max_blocks; j += blockDim.x) fo[j] = 0;
+  if (threadIdx.x == 0) {
+    kept_count[b] = 0;
+    flag_error(v.err, (s < 0 || s >= v.S) ? SPIN_ERR_SLOT : SPIN_ERR_QPOS);
+  }
+  return true;
+}
+
+// The `want` largest valid keys of a register-resident selection (0 < want <
+// number valid), ties to the lower element; returns this thread's bits.
+template <int NPL, typename K>
+__device__ uint32_t select_largest(const K (&key)[NPL], uint32_t valid, int want,
+                                   RegsSelectShared& sh, int& pass, int* s_i) {
+  K thr;
+  int neq;
+  regs_threshold<kSelectThreads, NPL, K>(key, valid, want, sh, pass, &thr, &neq);
+  return regs_selected<kSelectThreads, NPL, K>(key, valid, thr, neq, s_i);
+}
+
+// Register-resident selection of one row, 1024 threads, max_blocks <=
+// 1024 * NPL.  Thread (wave w, lane l) holds blocks j = w * 64 NPL + 64 i + l,
+// i < NPL: their block scores for the top-P pass, then the exploration words
+// of the blocks not predicted.  grid (B) with per_row = 0: one row (row 0;
+// under the row-0 mask the blocks only the later rows reach are added as
+// predicted), flags and the kept list written.  grid (B, R) with per_row = 1:
+// workgroup (b, r) selects row r and leaves its flags (bit 0 predicted, bit 1
+// explored; 0 past the row's last block) as bytes in the row's block-score
+// workspace, which it has finished reading; k_select_union forms the union.
+template <int NPL>
+__global__ void __launch_bounds__(kSelectThreads)
+k_select_regs(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept,
+              int32_t* kept_count, uint8_t* flags_out, int per_row) {
+  constexpr int NW = kSelectThreads / kWave;
+  __shared__ RegsSelectShared sh;
+  __shared__ int s_i[NW];      // tie counts of the selections
+  __shared__ int s_c[NW];      // kept counts of the compaction
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave, l = lane_id();
+  const int s = bt.slot[b];
+  const int q0 = bt.qpos[b];
+  uint8_t* fo = flags_out + size_t(b) * bt.max_blocks;
+  if (reject_request(v, bt, s, q0, per_row, fo, kept_count, b)) return;
+  const size_t row = size_t(layer) * v.S + s;
+  const int step = v.step[row];
+  const int r = per_row ? int(blockIdx.y) : 0;
+  const int n = num_blocks_of(q0 + r);
+  const int n_last = num_blocks_of(q0 + bt.R - 1);
+  const int e0 = w * (NPL * kWave) + l;        // block of step i: e0 + 64 i
+  uint32_t in_row = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) in_row |= (e0 + kWave * i < n) ? (1u << i) : 0u;
+  int kb, nexp;
+  budget(keep_bp, n, v.explore_bp, &kb, &nexp);
+  const int pcount = kb - nexp;
+  const bool budgeted = keep_bp < 10000 && kb < n;
+
+  // scores and exploration words are loaded beside the step count (a request
+  // still warming up selects every block and leaves them unused)
+  // (every lane loads, from block 0 when past the row or when the values go
+  // unused, so that all loads are issued together rather than one branch and
+  // wait each)
+  const bool load_s = budgeted && pcount > 0, load_u = budgeted && nexp > 0;
+  const uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
+  const float* S_row = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
+  float xs[NPL];
+  uint64_t xu[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = (in_row >> i & 1u) ? e0 + kWave * i : 0;
+    xu[i] = u[j];
+    xs[i] = S_row[j];
+  }
+  uint32_t key[NPL];
+  uint64_t ukey[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const uint32_t m = 0u - (in_row >> i & 1u);
+    key[i] = load_s ? ord_key(xs[i]) & m : 0u;
+    ukey[i] = load_u ? ~xu[i] & (uint64_t(0) - uint64_t(m & 1u)) : 0ull;
+  }
+  regs_select_init<kSelectThreads>(sh);
+  __syncthreads();
+
+  uint32_t pred = 0, expl = 0;
+  if (!budgeted || step < v.warmup) {
+    pred = in_row;
+  } else {
+    int pass = 0;
+    if (pcount > 0) pred = select_largest<NPL, uint32_t>(key, in_row, pcount, sh, pass, s_i);
+    if (nexp > 0)      // smallest word first among the blocks not predicted (nexp < their count)
+      expl = select_largest<NPL, uint64_t>(ukey, in_row & ~pred, nexp, sh, pass, s_i);
+  }
+
+  if (per_row) {
+    uint8_t* rf = reinterpret_cast<uint8_t*>(v.bscore + (size_t(b) * v.max_rows + r) *
+                                                            v.max_blocks);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int j = e0 + kWave * i;
+      if (j < n_last) rf[j] = uint8_t((pred >> i & 1u) | ((expl >> i & 1u) << 1));
+    }
+    return;
+  }
+  if (v.mask_row0) {     // blocks only the later rows reach (the draft positions)
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int j = e0 + kWave * i;
+      if (j >= n && j < n_last) pred |= 1u << i;
+    }
+  }
+  const uint32_t keep = pred | expl;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = e0 + kWave * i;
+    if (j < bt.max_blocks)
+      fo[j] = (pred >> i & 1u) ? uint8_t(1) : ((expl >> i & 1u) ? uint8_t(2) : uint8_t(0));
+  }
+  // ascending compaction: per-wave counts, then ballot ranks
+  const int mine = wave_sum(__popc(keep));
+  if (l == 0) s_c[w] = mine;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    base += x < w ? s_c[x] : 0;
+    total += s_c[x];
+  }
+  int32_t* ko = kept + size_t(b) * bt.max_blocks;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool k = (keep >> i & 1u) != 0;
+    const uint64_t kb_ = __ballot(k);
+    if (k) ko[base + ballot_rank(kb_)] = e0 + kWave * i;
+    base += __popcll(kb_);
+  }
+  if (tid == 0) kept_count[b] = total;
+}
+
+// Flags in LDS (dynamic, max_blocks bytes): bit 0 predicted by some row, bit
+// 1 explored by some row, bit 2 predicted by the current row; block scores and
+// exploration words read from the state's workspace.  For requests longer than
+// the register-resident selection holds; grid and per_row as k_select_regs.
 __global__ void __launch_bounds__(kSelectThreads)
 k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32_t* kept_count,
          uint8_t* flags_out, int per_row) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_flags[];
   __shared__ int s_scr[kSelectScratchInts];
-  uint64_t* s_u = reinterpret_cast<uint64_t*>(s_dyn);
-  float* s_S = reinterpret_cast<float*>(s_dyn + size_t(bt.max_blocks) * 8);
-  uint8_t* s_flags = RESIDENT ? s_dyn + size_t(bt.max_blocks) * 12 : s_dyn;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int s = bt.slot[b];
   const int q0 = bt.qpos[b];
   uint8_t* fo = flags_out + size_t(b) * bt.max_blocks;
   int32_t* ko = kept + size_t(b) * bt.max_blocks;
-
-  if (!request_ok(v, bt, s, q0)) {
-    if (per_row) return;                         // k_select_union reports it
-    for (int j = tid; j < bt.max_blocks; j += kSelectThreads) fo[j] = 0;
-    if (tid == 0) {
-      kept_count[b] = 0;
-      flag_error(v.err, (s < 0 || s >= v.S) ? SPIN_ERR_SLOT : SPIN_ERR_QPOS);
-    }
-    return;
-  }
+  if (reject_request(v, bt, s, q0, per_row, fo, kept_count, b)) return;
   const size_t row = size_t(layer) * v.S + s;
-  const int step = v.step[row];
-  const uint64_t rid = v.rid[s];
-  const bool warm = step < v.warmup || keep_bp >= 10000;
+  const bool warm = v.step[row] < v.warmup || keep_bp >= 10000;
   const int n_last = num_blocks_of(q0 + bt.R - 1);
-
   for (int j = tid; j < n_last; j += kSelectThreads) s_flags[j] = 0;
-
-  // Exploration words, shared by every row: u_j = Philox(counter (j/4, step,
-  // request id, 0), key (seed, layer)) word j%4.
-  uint64_t* u = RESIDENT ? s_u : v.ukey + size_t(b) * v.max_blocks;
-  if (!warm && v.explore_bp > 0) {
-    for (int g = tid; g < (n_last + 3) / 4; g += kSelectThreads) {
-      const Philox4x64 p = philox4x64_10(uint64_t(g), uint64_t(step), rid, 0ull, v.seed,
-                                         uint64_t(layer));
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (4 * g + k < n_last) u[4 * g + k] = p.w[k];
-    }
-  }
   __syncthreads();
 
-  const int r_begin = per_row ? int(blockIdx.y) : 0;
-  const int r_end = per_row ? r_begin + 1 : (v.mask_row0 ? 1 : bt.R);
-  for (int r = r_begin; r < r_end; ++r) {
-    const int q = q0 + r;
-    const int n = num_blocks_of(q);
-    int kb, nexp;
-    budget(keep_bp, n, v.explore_bp, &kb, &nexp);
-    if (warm || kb >= n) {
-      for (int j = tid; j < n; j += kSelectThreads) s_flags[j] |= 1;
-      __syncthreads();
-      continue;
-    }
-    for (int j = tid; j < n; j += kSelectThreads) s_flags[j] &= 3;
-    __syncthreads();
+  const int r = per_row ? int(blockIdx.y) : 0;
+  const int n = num_blocks_of(q0 + r);
+  int kb, nexp;
+  budget(keep_bp, n, v.explore_bp, &kb, &nexp);
+  if (warm || kb >= n) {
+    for (int j = tid; j < n; j += kSelectThreads) s_flags[j] |= 1;
+  } else {
     const int pcount = kb - nexp;
-    const float* S_row = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
-    if (RESIDENT && pcount > 0) {
-      for (int j = tid; j < n; j += kSelectThreads) s_S[j] = S_row[j];
-      __syncthreads();
-    }
     if (pcount > 0) {
-      BlockScoreSrc src{RESIDENT ? s_S : S_row};
+      BlockScoreSrc src{v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks};
       uint32_t thr;
       int neq;
       radix_threshold<kSelectThreads, 4, uint32_t>(src, n, pcount, &thr, &neq, s_scr);
@@ -311,7 +443,7 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
             src, n, thr, neq, [&](int j, int) { s_flags[j] |= 5; }, s_scr);
     }
     if (nexp > 0) {
-      ExploreSrc src{u, s_flags};
+      ExploreSrc src{v.ukey + size_t(b) * v.max_blocks, s_flags};
       uint64_t thr;
       int neq;
       radix_threshold<kSelectThreads, 4, uint64_t>(src, n, nexp, &thr, &neq, s_scr);
@@ -321,17 +453,17 @@ k_select(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept, int32
         ordered_emit<kSelectThreads, 2, uint64_t>(
             src, n, thr, neq, [&](int j, int) { s_flags[j] |= 2; }, s_scr);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   if (per_row) {
-    uint8_t* rf = reinterpret_cast<uint8_t*>(v.bscore + (size_t(b) * v.max_rows + r_begin) *
+    uint8_t* rf = reinterpret_cast<uint8_t*>(v.bscore + (size_t(b) * v.max_rows + r) *
                                                             v.max_blocks);
     for (int j = tid; j < n_last; j += kSelectThreads) rf[j] = s_flags[j] & 3;
     return;
   }
   if (v.mask_row0)      // blocks only the later rows reach (the draft positions)
-    for (int j = num_blocks_of(q0) + tid; j < n_last; j += kSelectThreads) s_flags[j] |= 1;
+    for (int j = n + tid; j < n_last; j += kSelectThreads) s_flags[j] |= 1;
   __syncthreads();
   for (int j = tid; j < bt.max_blocks; j += kSelectThreads) {
     uint8_t f = 0;
@@ -418,22 +550,26 @@ hipError_t launch_predict(const SpinView& v, int layer, const spin_batch& bt, in
                            dim3(kScoreWaves * kWave), 0, s, v, layer, bt, keep_bp);
     }
   }
-  const size_t resident_lds = size_t(bt.max_blocks) * 13;
-  // Opt in to dynamic LDS beyond 64 KB for the resident variant (once).
-  static const hipError_t lds_opt_in = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&k_select<true>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      int(kResidentLdsMax));
-  if (resident_lds > 64 * 1024 && lds_opt_in != hipSuccess) return lds_opt_in;
   // Several rows building their own masks (the union policy) run as one
   // workgroup per (request, row), then one per request forms the union.
   const int per_row = (!v.mask_row0 && bt.R > 1) ? 1 : 0;
   const dim3 grid(unsigned(bt.B), per_row ? unsigned(bt.R) : 1u);
-  if (resident_lds <= kResidentLdsMax)
-    hipLaunchKernelGGL(k_select<true>, grid, dim3(kSelectThreads), resident_lds, s, v, layer, bt,
-                       keep_bp, kept, kept_count, flags, per_row);
+  const dim3 block(kSelectThreads);
+  if (bt.max_blocks <= 2 * kSelectThreads)
+    hipLaunchKernelGGL(k_select_regs<2>, grid, block, 0, s, v, layer, bt, keep_bp, kept,
+                       kept_count, flags, per_row);
+  else if (bt.max_blocks <= 4 * kSelectThreads)
+    hipLaunchKernelGGL(k_select_regs<4>, grid, block, 0, s, v, layer, bt, keep_bp, kept,
+                       kept_count, flags, per_row);
+  else if (bt.max_blocks <= 8 * kSelectThreads)
+    hipLaunchKernelGGL(k_select_regs<8>, grid, block, 0, s, v, layer, bt, keep_bp, kept,
+                       kept_count, flags, per_row);
+  else if (bt.max_blocks <= kSelectRegsMax)
+    hipLaunchKernelGGL(k_select_regs<16>, grid, block, 0, s, v, layer, bt, keep_bp, kept,
+                       kept_count, flags, per_row);
   else
-    hipLaunchKernelGGL(k_select<false>, grid, dim3(kSelectThreads), size_t(bt.max_blocks), s, v,
-                       layer, bt, keep_bp, kept, kept_count, flags, per_row);
+    hipLaunchKernelGGL(k_select, grid, block, size_t(bt.max_blocks), s, v, layer, bt, keep_bp,
+                       kept, kept_count, flags, per_row);
   if (per_row) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -216,3 +216,144 @@ __device__ int count_valid(const Src& src, int n, int* s_scratch) {
 }
 
 }  // namespace spin
+
+namespace spin {
+
+// ------------------------------------------------------------------------
+// Register-resident selection: a workgroup of NT threads holds NPL keys per
+// thread, element e(w, i, l) = w * (NPL * 64) + i * 64 + l (wave w owns a
+// contiguous segment, in lane order within each step i), with a validity bit
+// per element.  The `want` largest valid keys (ties to the lower element) are
+// keys > T, or == T for the first n_eq valid elements holding T.
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts within
+// each 16-lane row, then the row broadcasts of lanes 15 and 31).  Every lane
+// of the wave must be active.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+  int s = x;
+  s += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // x[l-1]
+  s += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // x[l-2]
+  s += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xF, 0xF, true);   // x[l-3]
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xF, 0xE, false);  // lanes 4..15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xF, 0xC, false);  // lanes 8..15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xA, 0xF, false);  // rows 1, 3: + lane 15
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xC, 0xF, false);  // rows 2, 3: + lane 31
+  return s;
+}
+
+// LDS of the register-resident threshold search: two histograms, used in turn
+// by successive passes, each held as kSelCopies copies (lane l adds to copy
+// l % kSelCopies; the copies of a digit are adjacent words in distinct
+// banks), so that lanes sharing a digit rarely hit one address; and two
+// broadcast words.
+constexpr int kSelCopies = 8;
+struct RegsSelectShared {
+  __attribute__((aligned(16))) int hist[2][kSelHist * kSelCopies];
+  int bc[2][4];
+};
+
+// Clears the first histogram; a barrier must follow before the first search.
+template <int NT>
+__device__ __forceinline__ void regs_select_init(RegsSelectShared& sh) {
+  for (int i = threadIdx.x; i < kSelHist * kSelCopies; i += NT) sh.hist[0][i] = 0;
+}
+
+// Threshold of the `want` largest valid keys, 0 < want < number valid: MSB
+// first 8-bit radix digits, stopping once the threshold bucket is taken whole
+// (then n_eq is unbounded, 0x7fffffff).  Pass p (counted over every search of
+// the workgroup in `pass`) fills hist[p & 1]; wave 0 then scans it while the
+// other waves clear hist[(p + 1) & 1] for the next pass.
+template <int NT, int NPL, typename K>
+__device__ void regs_threshold(const K (&key)[NPL], uint32_t valid, int want,
+                               RegsSelectShared& sh, int& pass, K* thr_out, int* neq_out) {
+  static_assert(NT > kWave, "one wave scans while the others clear");
+  const int tid = threadIdx.x, l = lane_id();
+  const int copy = l & (kSelCopies - 1);
+  K prefix = 0, mask = 0;
+  int remaining = want;
+  bool done = false;
+  for (int shift = int(sizeof(K)) * 8 - 8; shift >= 0 && !done; shift -= 8, ++pass) {
+    int* h = sh.hist[pass & 1];
+    int* bc = sh.bc[pass & 1];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if ((valid >> i & 1u) != 0 && (key[i] & mask) == prefix)
+        atomicAdd(&h[(int(key[i] >> shift) & 255) * kSelCopies + copy], 1);
+    __syncthreads();
+    if (tid < kWave) {
+      // lane l holds digits 255 - 4 l .. 252 - 4 l: a prefix sum over lanes is
+      // the count of keys at or above a digit
+      int c[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int4* hv = reinterpret_cast<const int4*>(h + (255 - 4 * l - k) * kSelCopies);
+        int t = 0;
+#pragma unroll
+        for (int q = 0; q < kSelCopies / 4; ++q) {
+          const int4 v4 = hv[q];
+          t += v4.x + v4.y + v4.z + v4.w;
+        }
+        c[k] = t;
+      }
+      const int tot = c[0] + c[1] + c[2] + c[3];
+      const int incl = wave_prefix_sum(tot);
+      const int above = incl - tot;
+      const uint64_t hit = __ballot(above < remaining && remaining <= incl);
+      const int at = __ffsll(static_cast<unsigned long long>(hit)) - 1;   // exactly one lane
+      const int a1 = above + c[0], a2 = a1 + c[1], a3 = a2 + c[2];
+      const int k = (a1 < remaining ? 1 : 0) + (a2 < remaining ? 1 : 0) + (a3 < remaining ? 1 : 0);
+      const int cum = k == 0 ? above : (k == 1 ? a1 : (k == 2 ? a2 : a3));
+      const int cnt = k == 0 ? c[0] : (k == 1 ? c[1] : (k == 2 ? c[2] : c[3]));
+      if (l == at) {
+        bc[0] = 255 - 4 * l - k;
+        bc[1] = cum;
+        bc[2] = cnt;
+      }
+    } else {
+      int* hn = sh.hist[(pass + 1) & 1];
+      for (int i = tid - kWave; i < kSelHist * kSelCopies; i += NT - kWave) hn[i] = 0;
+    }
+    __syncthreads();
+    remaining -= bc[1];
+    prefix |= K(bc[0]) << shift;
+    mask |= K(255) << shift;
+    done = bc[2] == remaining;
+  }
+  *thr_out = prefix;
+  *neq_out = done ? 0x7fffffff : remaining;
+}
+
+// Bits of the selected elements (key > thr, or == thr among the first n_eq
+// valid holders of thr in element order).  s_i: NT / 64 ints.
+template <int NT, int NPL, typename K>
+__device__ uint32_t regs_selected(const K (&key)[NPL], uint32_t valid, K thr, int n_eq, int* s_i) {
+  uint32_t sel = 0;
+  if (n_eq == 0x7fffffff) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if ((valid >> i & 1u) && key[i] >= thr) sel |= 1u << i;
+    return sel;
+  }
+  const int w = threadIdx.x / kWave, l = lane_id();
+  int eq = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) eq += ((valid >> i & 1u) && key[i] == thr) ? 1 : 0;
+  eq = wave_sum(eq);
+  __syncthreads();
+  if (l == 0) s_i[w] = eq;
+  __syncthreads();
+  int eq_base = 0;
+  for (int i = 0; i < w; ++i) eq_base += s_i[i];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool is_eq = (valid >> i & 1u) && key[i] == thr;
+    const uint64_t eqb = __ballot(is_eq);
+    if (((valid >> i & 1u) && key[i] > thr) || (is_eq && eq_base + ballot_rank(eqb) < n_eq))
+      sel |= 1u << i;
+    eq_base += __popcll(eqb);
+  }
+  __syncthreads();
+  return sel;
+}
+
+}  // namespace spin

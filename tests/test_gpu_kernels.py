@@ -271,18 +271,55 @@ POOL_NAMES = {spin.SPIN_POOL_MAX: O.POOL_MAX, spin.SPIN_POOL_MEAN: O.POOL_MEAN,
 @pytest.mark.parametrize("R,keep_bp,explore_bp,step,blocks,policy", [
     (1, 6000, 500, 3, 200, 0), (1, 5000, 0, 1, 200, 0), (1, 8000, 2500, 7, 200, 0),
     (4, 5000, 1000, 2, 200, 0), (4, 6000, 500, 0, 200, 0), (1, 10000, 500, 4, 200, 0),
-    (1, 0, 500, 4, 200, 0), (2, 9990, 500, 5, 200, 0),
-    # past the LDS-resident limit of the selection kernel: the workspace path
-    (1, 5000, 500, 3, 12000, 0), (4, 6000, 1000, 2, 12000, 0),
+    (1, 0, 500, 4, 200, 0), (2, 9990, 500, 5, 200, 0), (1, 5000, 10000, 3, 200, 0),
+    # register-resident selection at 4, 8 and 16 blocks per thread
+    (1, 5000, 500, 3, 12000, 0), (4, 6000, 1000, 2, 12000, 0), (1, 5000, 500, 3, 8192, 0),
     # the MTP shape: 4 rows over 4096 blocks, each row selected by its own workgroup
     (4, 5000, 1000, 2, 4096, 0),
+    # past the register-resident limit (16384 blocks): the selection from global memory
+    (1, 5000, 500, 3, 17000, 0), (4, 5000, 1000, 2, 17000, 0),
     # the pages' ablation variants: Mean / Top-4 pooling, row-0 mask
     (1, 6000, 500, 3, 200, spin.SPIN_POOL_MEAN), (1, 5000, 1000, 2, 200, spin.SPIN_POOL_TOP4),
     (4, 5000, 1000, 2, 200, spin.SPIN_MASK_ROW0),
     (4, 6000, 500, 3, 200, spin.SPIN_MASK_ROW0 | spin.SPIN_POOL_TOP4),
-    (2, 5000, 500, 1, 12000, spin.SPIN_POOL_MEAN)])
+    (2, 5000, 500, 1, 12000, spin.SPIN_POOL_MEAN), (2, 5000, 500, 1, 17000, spin.SPIN_MASK_ROW0)])
 def test_predict_exact(gpu_lib, R, keep_bp, explore_bp, step, blocks, policy):
-    rng = np.random.default_rng(keep_bp + R)
+    _predict_case(R, keep_bp, explore_bp, step, blocks, policy, "random")
+
+
+# score ties: V and D on four levels (block scores tie in long runs at the
+# threshold), almost never observed (most block scores -inf), or never
+# observed at all (every block score -inf, every key equal)
+@pytest.mark.parametrize("R,blocks,kind", [
+    (1, 200, "levels"), (1, 8192, "levels"), (1, 8192, "sparse"), (1, 8192, "empty"),
+    (4, 4096, "levels"), (1, 17000, "levels"), (4, 17000, "sparse"), (2, 12000, "empty")])
+def test_predict_exact_ties(gpu_lib, R, blocks, kind):
+    _predict_case(R, 5000, 1000, 3, blocks, 0, kind)
+
+
+def _states(kind, ctx, b):
+    if kind == "random":
+        V = np_(random_state(ctx, 0.15, seed=10 * b + 1)).astype(np.float64)
+        D = np_(random_state(ctx, 0.15, seed=10 * b + 2)).astype(np.float64)
+        return V, D
+    rng = np.random.default_rng(77 + b)
+    if kind == "levels":
+        V = np.floor(np.abs(rng.standard_normal(ctx)) * 1.5).clip(0, 3)
+        D = np.floor(np.abs(rng.standard_normal(ctx)) * 1.5).clip(0, 3)
+        V[rng.random(ctx) < 0.1] = NEG
+        D[rng.random(ctx) < 0.1] = NEG
+    elif kind == "sparse":
+        V = np.full(ctx, NEG)
+        D = np.full(ctx, NEG)
+        V[rng.integers(0, ctx, max(1, ctx // 20000))] = 2.0
+        D[rng.integers(0, ctx, max(1, ctx // 20000))] = 1.0
+    else:
+        V = np.full(ctx, NEG)
+        D = np.full(ctx, NEG)
+    return V, D
+
+
+def _predict_case(R, keep_bp, explore_bp, step, blocks, policy, kind):
     B, ctx = 4, 64 * blocks
     mb = nblocks(ctx - 1)
     qpos = np.array([ctx - R, 64 * (blocks * 3 // 4) + 63 - 1, 64 * 3 + 1, 40], dtype=np.int64)
@@ -296,13 +333,12 @@ def test_predict_exact(gpu_lib, R, keep_bp, explore_bp, step, blocks, policy):
     layer = 1
     states = []
     for b in range(B):
-        V = np_(random_state(ctx, 0.15, seed=10 * b + 1)).astype(np.float64)
-        D = np_(random_state(ctx, 0.15, seed=10 * b + 2)).astype(np.float64)
+        V, D = _states(kind, ctx, b)
         V[qpos[b] + 1:] = NEG
         rig.inject(layer, b, V.astype(np.float32), D.astype(np.float32), step)
         states.append((V.astype(np.float32).astype(np.float64), D.astype(np.float32).astype(np.float64)))
     rig.set_qpos(qpos)
-    _say("predict", R, keep_bp, explore_bp, step)
+    _say("predict", R, keep_bp, explore_bp, step, blocks, policy, kind)
     spin.spin_predict_blocks(rig.h, layer, rig.batch, keep_bp, rig.kept, rig.kept_count, rig.flags)
     torch.cuda.synchronize()
     for b in range(B):
