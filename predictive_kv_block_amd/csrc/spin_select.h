@@ -259,26 +259,44 @@ __device__ __forceinline__ void regs_select_init(RegsSelectShared& sh) {
 }
 
 // Threshold of the `want` largest valid keys, 0 < want < number valid: MSB
-// first 8-bit radix digits, stopping once the threshold bucket is taken whole
-// (then n_eq is unbounded, 0x7fffffff).  Pass p (counted over every search of
-// the workgroup in `pass`) fills hist[p & 1]; wave 0 then scans it while the
-// other waves clear hist[(p + 1) & 1] for the next pass.
+// first radix digits of up to 8 bits, stopping once the threshold bucket is
+// taken whole (then n_eq is unbounded, 0x7fffffff).  Given the smallest and
+// largest valid key, the digits start below the bits those two share (all
+// keys share them); all keys equal gives the first `want` valid elements.
+// Pass p (counted over every search of the workgroup in `pass`) fills
+// hist[p & 1]; wave 0 then scans it while the other waves clear
+// hist[(p + 1) & 1] for the next pass.
 template <int NT, int NPL, typename K>
 __device__ void regs_threshold(const K (&key)[NPL], uint32_t valid, int want,
-                               RegsSelectShared& sh, int& pass, K* thr_out, int* neq_out) {
+                               RegsSelectShared& sh, int& pass, K* thr_out, int* neq_out,
+                               K kmin = K(0), K kmax = ~K(0)) {
   static_assert(NT > kWave, "one wave scans while the others clear");
+  static_assert(NPL <= 32, "one validity bit per key");
+  constexpr int kBits = int(sizeof(K)) * 8;
   const int tid = threadIdx.x, l = lane_id();
   const int copy = l & (kSelCopies - 1);
-  K prefix = 0, mask = 0;
+  if (kmin == kmax) {
+    *thr_out = kmin;
+    *neq_out = want;
+    return;
+  }
+  const K diff = kmin ^ kmax;
+  const int hb = kBits - 1 - (kBits == 64 ? __clzll(static_cast<long long>(diff))
+                                          : __clz(static_cast<int>(diff)));
+  K mask = hb == kBits - 1 ? K(0) : ~((K(2) << hb) - K(1));   // the shared high bits
+  K prefix = kmin & mask;
   int remaining = want;
   bool done = false;
-  for (int shift = int(sizeof(K)) * 8 - 8; shift >= 0 && !done; shift -= 8, ++pass) {
+  for (int top = hb; top >= 0 && !done; ++pass) {
+    const int width = top + 1 < 8 ? top + 1 : 8;
+    const int shift = top + 1 - width;
+    const K dmask = (K(1) << width) - K(1);
     int* h = sh.hist[pass & 1];
     int* bc = sh.bc[pass & 1];
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if ((valid >> i & 1u) != 0 && (key[i] & mask) == prefix)
-        atomicAdd(&h[(int(key[i] >> shift) & 255) * kSelCopies + copy], 1);
+        atomicAdd(&h[int((key[i] >> shift) & dmask) * kSelCopies + copy], 1);
     __syncthreads();
     if (tid < kWave) {
       // lane l holds digits 255 - 4 l .. 252 - 4 l: a prefix sum over lanes is
@@ -316,8 +334,9 @@ __device__ void regs_threshold(const K (&key)[NPL], uint32_t valid, int want,
     __syncthreads();
     remaining -= bc[1];
     prefix |= K(bc[0]) << shift;
-    mask |= K(255) << shift;
+    mask |= dmask << shift;
     done = bc[2] == remaining;
+    top = shift - 1;
   }
   *thr_out = prefix;
   *neq_out = done ? 0x7fffffff : remaining;

@@ -30,13 +30,13 @@
 
 #include "spin_device.h"
 #include "spin_internal.h"
+#include "spin_select.h"
 
 namespace spin {
 namespace {
 
 constexpr int kTopkThreads = 512;
 constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kHistCopies = 4;                       // LDS histograms, shared by waves
 constexpr int kSeg = kChunk / kTopkWaves;            // 2048 keys per wave
 constexpr int kPerLane = kSeg / kWave;               // 32 keys per lane
 
@@ -63,7 +63,7 @@ struct LevelArgs {
 constexpr int kMaxWaves = 16;
 
 struct TopkShared {
-  int hist[kHistCopies][256];
+  RegsSelectShared sel;
   int wave_a[kMaxWaves], wave_b[kMaxWaves];
   uint32_t wave_min[kMaxWaves], wave_max[kMaxWaves];
   int bc[4];
@@ -111,83 +111,25 @@ __device__ void block_key_stats(const uint32_t* key, TopkShared& sh, int* total,
   *kmax = hi;
 }
 
-// Threshold of the `want` largest register-held keys (0 < want < total):
-// selected = key > thr, or key == thr for the first n_eq in index order.
-// Radix windows start below the bits common to kmin and kmax; the search stops
-// early when the whole threshold bucket is taken (then thr is the bucket's
-// lowest key and n_eq is unbounded).
+// Threshold of the `want` largest register-held keys (0 < want < total, key 0
+// = not a candidate): selected = key > thr, or key == thr for the first n_eq
+// in index order (n_eq unbounded when the whole threshold bucket is taken).
+// kmin and kmax are the smallest and largest candidate keys.
 template <int NT, int NPL>
 __device__ void radix_select_regs(const uint32_t* key, int want, uint32_t kmin, uint32_t kmax,
                                   TopkShared& sh, uint32_t* thr_out, int* n_eq_out) {
-  const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
-  if (kmin == kmax) {
-    *thr_out = kmin;                       // all equal: the lowest-index `want`
-    *n_eq_out = want;
-    return;
+  uint32_t k[NPL];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    k[i] = key[i];
+    valid |= (key[i] != 0u) ? (1u << i) : 0u;
   }
-  const int hb = 31 - __clz(int(kmin ^ kmax));
-  uint32_t mask = (hb == 31) ? 0u : ~((2u << hb) - 1u);
-  uint32_t prefix = kmin & mask;
-  int remaining = want;
-  int top = hb;                            // highest bit of the current window
-  bool done = false;
-  while (top >= 0 && !done) {
-    const int width = min(8, top + 1);
-    const int shift = top + 1 - width;
-    const uint32_t dmask = (1u << width) - 1u;
-    __syncthreads();
-    for (int i = tid; i < kHistCopies * 256; i += NT) (&sh.hist[0][0])[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NPL; ++i)
-      hist_add(sh.hist[w % kHistCopies], int((key[i] >> shift) & dmask),
-               key[i] != 0u && (key[i] & mask) == prefix);
-    __syncthreads();
-    if (w == 0) {
-      int c4[4], tot = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        int sum = 0;
-#pragma unroll
-        for (int hc = 0; hc < kHistCopies; ++hc) sum += sh.hist[hc][4 * l + k];
-        c4[k] = sum;
-        tot += sum;
-      }
-      int sfx = tot;  // inclusive suffix sum over lanes l..63
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_down(sfx, o, kWave);
-        if (l + o < kWave) sfx += t;
-      }
-      const int above = sfx - tot;
-      if (l == 0) {
-        sh.bc[0] = 0;
-        sh.bc[1] = 0;
-        sh.bc[2] = 0;
-      }
-      if (above < remaining && remaining <= sfx) {
-        int cum = above;
-        for (int k = 3; k >= 0; --k) {
-          if (cum + c4[k] >= remaining) {
-            sh.bc[0] = 4 * l + k;
-            sh.bc[1] = cum;
-            sh.bc[2] = c4[k];
-            break;
-          }
-          cum += c4[k];
-        }
-      }
-    }
-    __syncthreads();
-    const int digit = sh.bc[0];
-    remaining -= sh.bc[1];
-    prefix |= uint32_t(digit) << shift;
-    mask |= dmask << shift;
-    done = sh.bc[2] == remaining;
-    top = shift - 1;
-  }
-  *thr_out = prefix;
-  *n_eq_out = done ? 0x7fffffff : remaining;
+  int pass = 0;
+  __syncthreads();                       // earlier readers of the histograms are done
+  regs_select_init<NT>(sh.sel);
+  __syncthreads();
+  regs_threshold<NT, NPL, uint32_t>(k, valid, want, sh.sel, pass, thr_out, n_eq_out, kmin, kmax);
 }
 
 // ---------------------------------------------------------------- fused row
@@ -382,25 +324,31 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
     // distinct slots, so at least K slots score >= t1.
     int lm = 0;
     while (lm < 2 && (cnt << lm) < 2 * K && (cnt << (lm + 1)) <= kFusedMaxPages) ++lm;
+    // (every lane loads, page 0 past the count, so that the loads are issued
+    // together rather than one branch and wait each)
+    float4 xq[kFusedPageLanes];
+#pragma unroll
+    for (int i = 0; i < kFusedPageLanes; ++i) {
+      const int p = (w * (kFusedPageLanes * kWave) + i * kWave + l) >> lm;
+      xq[i] = *reinterpret_cast<const float4*>(pq + size_t(p < cnt ? p : 0) * 4);
+    }
     uint32_t pk[kFusedPageLanes];
 #pragma unroll
     for (int i = 0; i < kFusedPageLanes; ++i) {
       const int e = w * (kFusedPageLanes * kWave) + i * kWave + l;
       const int p = e >> lm, t = e & ((1 << lm) - 1);
-      float v = -INFINITY;
-      if (p < cnt) {
-        const float4 x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
-        if (lm == 2) {
-          v = t == 0 ? x.x : t == 1 ? x.y : t == 2 ? x.z : x.w;
-        } else {
-          const float a = fmaxf(x.x, x.y), b2 = fminf(x.x, x.y);
-          const float c = fmaxf(x.z, x.w), d = fminf(x.z, x.w);
-          const float top1 = fmaxf(a, c);
-          const float top2 = fmaxf(fminf(a, c), fmaxf(b2, d));
-          v = (lm == 1 && t == 1) ? top2 : top1;
-        }
+      const float4 x = xq[i];
+      float v;
+      if (lm == 2) {
+        v = t == 0 ? x.x : t == 1 ? x.y : t == 2 ? x.z : x.w;
+      } else {
+        const float a = fmaxf(x.x, x.y), b2 = fminf(x.x, x.y);
+        const float c = fmaxf(x.z, x.w), d = fminf(x.z, x.w);
+        const float top1 = fmaxf(a, c);
+        const float top2 = fmaxf(fminf(a, c), fmaxf(b2, d));
+        v = (lm == 1 && t == 1) ? top2 : top1;
       }
-      pk[i] = (v > -INFINITY) ? ord_key(v) : 0u;
+      pk[i] = (p < cnt && v > -INFINITY) ? ord_key(v) : 0u;
     }
     int nvals;
     uint32_t kmin, kmax;
@@ -425,10 +373,14 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
 #pragma unroll
       for (int i = 0; i < kFusedPageLanes; ++i) {
         const int p = p_first + i;
-        float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (p < cnt) x = *reinterpret_cast<const float4*>(pq + size_t(p) * 4);
-        qbits[i] = int(x.x >= f1) | (int(x.y >= f1) << 1) | (int(x.z >= f1) << 2) |
-                   (int(x.w >= f1) << 3);
+        xq[i] = *reinterpret_cast<const float4*>(pq + size_t(p < cnt ? p : 0) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < kFusedPageLanes; ++i) {
+        const float4 x = xq[i];
+        qbits[i] = p_first + i < cnt ? int(x.x >= f1) | (int(x.y >= f1) << 1) |
+                                           (int(x.z >= f1) << 2) | (int(x.w >= f1) << 3)
+                                     : 0;
         mine += __popc(qbits[i]);
       }
       const int incl = wave_inclusive_sum(mine);
