@@ -224,7 +224,10 @@ __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
 // index.  With `out`, their positions are written to out[0..K) ascending and
 // padded with -1; without, they are compacted in place into
 // sh.skey/spos[0..min(K, live)).  n <= kFusedCap.  Returns min(K, live).
-__device__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out) {
+// Bounds lo <= hi on the live keys, when known (lo > 0), save the workgroup
+// reduction that finds them.
+__device__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out,
+                        uint32_t lo = 0u, uint32_t hi = 0u) {
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   uint32_t key[kFusedPerLane];
   int pos[kFusedPerLane];
@@ -237,9 +240,11 @@ __device__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out) {
   uint32_t thr = 0;                              // live <= K: every entry
   int n_eq = 0;
   if (live > K) {
-    uint32_t smin, smax;
-    int tot;
-    block_key_stats<kFusedThreads, kFusedPerLane>(key, sh.t, &tot, &smin, &smax);
+    uint32_t smin = lo, smax = hi;
+    if (lo == 0u) {
+      int tot;
+      block_key_stats<kFusedThreads, kFusedPerLane>(key, sh.t, &tot, &smin, &smax);
+    }
     radix_select_regs<kFusedThreads, kFusedPerLane>(key, K, smin, smax, sh.t, &thr, &n_eq);
   }
   int gt = 0, eq = 0;
@@ -452,10 +457,6 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
             int c, slot;
             const int f = survivors(c0, i, v[i], jv[i], &c, &slot);
             const int n = __popc(f);
-            // survivors of the quarter: sum over its 4 lanes (quad DPP)
-            int q = n + __builtin_amdgcn_update_dpp(0, n, kDppXor1, 0xF, 0xF, false);
-            q += __builtin_amdgcn_update_dpp(0, q, kDppXor2, 0xF, 0xF, false);
-            if ((l & 3) == 3 && c < c_hi) sh.qcount[c] = q;
             const int incl = wave_inclusive_sum(n);
             int o = wave_n + incl - n;
             const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -489,11 +490,27 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
               sh.spos[kSlice * w + x] = 0;
             }
             __syncthreads();
-            lds_topk(sh, kFusedCap, nsurv, K, out);
+            lds_topk(sh, kFusedCap, nsurv, K, out, lowest, max(kmax, lowest));
             return;
           }
-          // 4'. a wave found more than its slice holds: offsets from the
-          // per-quarter counts, and a second read collects the survivors packed
+          // 4'. a wave found more than its slice holds: a second read counts
+          // each quarter's survivors, and after a scan of those counts a third
+          // collects the survivors packed
+          for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
+            float4 v[kLoads];
+            int jv[kLoads];
+            load_batch(c0, v, jv);
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+              int c, slot;
+              const int n = __popc(survivors(c0, i, v[i], jv[i], &c, &slot));
+              // survivors of the quarter: sum over its 4 lanes (quad DPP)
+              int q = n + __builtin_amdgcn_update_dpp(0, n, kDppXor1, 0xF, 0xF, false);
+              q += __builtin_amdgcn_update_dpp(0, q, kDppXor2, 0xF, 0xF, false);
+              if ((l & 3) == 3 && c < c_hi) sh.qcount[c] = q;
+            }
+          }
+          __syncthreads();
           block_exclusive_scan(sh.qcount, ncand, sh.scan);
           for (int c0 = c_lo; c0 < c_hi; c0 += kFusedBatch) {
             float4 v[kLoads];
@@ -525,7 +542,7 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
           }
           __syncthreads();
           // 5. exact top-K of the survivors, written ascending
-          lds_topk(sh, nsurv, nsurv, K, out);
+          lds_topk(sh, nsurv, nsurv, K, out, lowest, max(kmax, lowest));
           return;
         }
       }
