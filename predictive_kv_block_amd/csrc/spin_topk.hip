@@ -400,11 +400,16 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
       }
       if (ncand <= kFusedCandQ) {
         int o = before + incl - mine;
+        // the lane's flags as one 64-bit mask (bit 4 i + c: quarter c of page
+        // p_first + i), walked set bit by set bit: entry 4 p_first + bit
+        uint64_t fm = 0;
 #pragma unroll
-        for (int i = 0; i < kFusedPageLanes; ++i)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (qbits[i] & (1 << c)) sh.cq[o++] = 4 * (p_first + i) + c;
+        for (int i = 0; i < kFusedPageLanes; ++i) fm |= uint64_t(qbits[i]) << (4 * i);
+        while (fm != 0) {
+          const int bit = __ffsll(static_cast<unsigned long long>(fm)) - 1;
+          sh.cq[o++] = 4 * p_first + bit;
+          fm &= fm - 1;
+        }
         __syncthreads();
 
         // 3. survivors per candidate quarter.  Wave w scans the contiguous
@@ -452,25 +457,31 @@ __device__ __forceinline__ void topk_row(FusedShared& sh, int row, const spin_ba
           float4 v[kLoads];
           int jv[kLoads];
           load_batch(c0, v, jv);
+          // loads of 16 quarters wholly past the wave's range hold nothing: their
+          // processing is skipped (a wave-uniform test; the loads themselves are
+          // issued regardless, so that they go out together)
+          const int live_loads = __builtin_amdgcn_readfirstlane((c_hi - c0 + 15) / 16);
 #pragma unroll
           for (int i = 0; i < kLoads; ++i) {
-            int c, slot;
-            const int f = survivors(c0, i, v[i], jv[i], &c, &slot);
-            const int n = __popc(f);
-            const int incl = wave_inclusive_sum(n);
-            int o = wave_n + incl - n;
-            const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            if (i < live_loads) {
+              int c, slot;
+              const int f = survivors(c0, i, v[i], jv[i], &c, &slot);
+              const int n = __popc(f);
+              const int incl = wave_inclusive_sum(n);
+              int o = wave_n + incl - n;
+              const float vals[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              if (f & (1 << k)) {
-                if (o < kSlice) {
-                  sh.skey[kSlice * w + o] = ord_key(vals[k]);
-                  sh.spos[kSlice * w + o] = slot + k;
+              for (int k = 0; k < 4; ++k) {
+                if (f & (1 << k)) {
+                  if (o < kSlice) {
+                    sh.skey[kSlice * w + o] = ord_key(vals[k]);
+                    sh.spos[kSlice * w + o] = slot + k;
+                  }
+                  ++o;
                 }
-                ++o;
               }
+              wave_n += __builtin_amdgcn_readlane(incl, kWave - 1);
             }
-            wave_n += __builtin_amdgcn_readlane(incl, kWave - 1);
           }
         }
         if (l == 0) sh.wcount[w] = wave_n;
