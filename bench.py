@@ -156,15 +156,23 @@ def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_end, ev=None, accepte
     ev = ev or [None] * 8
     rec = lambda e, s: e.record(s) if e is not None else None
     rec(ev[0], main)
+    # quantiser on the side stream, ordered after the previous round.  It is
+    # enqueued before the predictor: the block-score kernel fills every wave
+    # slot of the chip, and a quantiser enqueued after it would wait for the
+    # slots it frees
+    qs = side if QUANTIZE_ON_SIDE else main
+    if QUANTIZE_ON_SIDE:
+        if prev_end is not None:
+            side.wait_event(prev_end)
+        rec(ev[5], qs)
+        spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
+        rec(ev[6], qs)
     spin.spin_predict_blocks(st.handle, 0, b["batch"], keep_bp, b["kept"], b["cnt"], b["flags"])
     rec(ev[1], main)
-    # quantiser on the side stream, ordered after the previous round
-    qs = side if QUANTIZE_ON_SIDE else main
-    if QUANTIZE_ON_SIDE and prev_end is not None:
-        side.wait_event(prev_end)
-    rec(ev[5], qs)
-    spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
-    rec(ev[6], qs)
+    if not QUANTIZE_ON_SIDE:
+        rec(ev[5], qs)
+        spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
+        rec(ev[6], qs)
     if QUANTIZE_ON_SIDE:
         q_done = torch.cuda.Event()
         q_done.record(side)

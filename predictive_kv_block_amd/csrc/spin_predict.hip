@@ -76,10 +76,9 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int b = blockIdx.y, r = blockIdx.z;
   const int s = bt.slot[b];
   const int q0 = bt.qpos[b];
-  if (!request_ok(v, bt, s, q0)) return;
+  if (!request_ok(v, bt, s, q0) || keep_bp >= 10000) return;
   const size_t row = size_t(layer) * v.S + s;
-  const int step = v.step[row];
-  if (step < v.warmup || keep_bp >= 10000) return;
+  const int step = v.step[row];             // waited for only after the first loads
   const int q = q0 + r;
   const int n = num_blocks_of(q);
   const int n_last = num_blocks_of(q0 + bt.R - 1);
@@ -89,7 +88,7 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
   const int jw = (blockIdx.x * kScoreWaves + wave) * kScoreBlocksPerWave;
   const bool words = r == 0 && v.explore_bp > 0 && jw < n_last;
   if (kb >= n || jw >= n) {
-    if (words) explore_words(v, layer, b, s, step, jw, kScoreBlocksPerWave, n_last);
+    if (words && step >= v.warmup) explore_words(v, layer, b, s, step, jw, kScoreBlocksPerWave, n_last);
     return;
   }
 
@@ -139,7 +138,10 @@ k_block_scores(SpinView v, int layer, spin_batch bt, int keep_bp) {
       if ((l & 15) == 15 && j < nfull) out[j] = fmaxf(m, vbuf[u][gq]);
     }
   };
+  // the first batch's loads go out before the step count is known: a request
+  // still warming up (its selection keeps every block) drops them unused
   issue(0, 0);
+  if (step < v.warmup) return;
 #pragma unroll
   for (int t = 0; t < kScoreBatchesPerWave; t += 2) {
     issue(1, t + 1);
@@ -301,16 +303,32 @@ k_select_regs(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept,
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int w = tid / kWave, l = lane_id();
+  const int r = per_row ? int(blockIdx.y) : 0;
+  const int e0 = w * (NPL * kWave) + l;        // block of step i: e0 + 64 i
+  // The row's block scores and exploration words are loaded first, every
+  // lane from block 0 past max_blocks: their addresses need neither the
+  // request's slot, position nor step count, so the loads go out together at
+  // once, and a request that turns out to be invalid or still warming up
+  // leaves them unused.  (A conditional load per element had made the
+  // compiler put each one behind its own branch and wait.)
+  const uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
+  const float* S_row = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
+  float xs[NPL];
+  uint64_t xu[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int j = e0 + kWave * i < bt.max_blocks ? e0 + kWave * i : 0;
+    xu[i] = u[j];
+    xs[i] = S_row[j];
+  }
   const int s = bt.slot[b];
   const int q0 = bt.qpos[b];
   uint8_t* fo = flags_out + size_t(b) * bt.max_blocks;
   if (reject_request(v, bt, s, q0, per_row, fo, kept_count, b)) return;
   const size_t row = size_t(layer) * v.S + s;
   const int step = v.step[row];
-  const int r = per_row ? int(blockIdx.y) : 0;
   const int n = num_blocks_of(q0 + r);
   const int n_last = num_blocks_of(q0 + bt.R - 1);
-  const int e0 = w * (NPL * kWave) + l;        // block of step i: e0 + 64 i
   uint32_t in_row = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) in_row |= (e0 + kWave * i < n) ? (1u << i) : 0u;
@@ -318,23 +336,7 @@ k_select_regs(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept,
   budget(keep_bp, n, v.explore_bp, &kb, &nexp);
   const int pcount = kb - nexp;
   const bool budgeted = keep_bp < 10000 && kb < n;
-
-  // scores and exploration words are loaded beside the step count (a request
-  // still warming up selects every block and leaves them unused)
-  // (every lane loads, from block 0 when past the row or when the values go
-  // unused, so that all loads are issued together rather than one branch and
-  // wait each)
   const bool load_s = budgeted && pcount > 0, load_u = budgeted && nexp > 0;
-  const uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
-  const float* S_row = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
-  float xs[NPL];
-  uint64_t xu[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int j = (in_row >> i & 1u) ? e0 + kWave * i : 0;
-    xu[i] = u[j];
-    xs[i] = S_row[j];
-  }
   uint32_t key[NPL];
   uint64_t ukey[NPL];
 #pragma unroll
