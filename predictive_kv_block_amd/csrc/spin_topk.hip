@@ -137,7 +137,8 @@ constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
 constexpr int kFusedPageLanes = 16;                          // page maxima per lane
 constexpr int kFusedMaxPages = kFusedThreads * kFusedPageLanes;   // 16384
-constexpr int kFusedCandQ = 8192;                            // listed candidate quarters
+constexpr int kFusedCandQ = 8192;
+                            // listed candidate quarters
 constexpr int kFusedCap = 8192;                              // survivors held in LDS
 constexpr int kFusedPerLane = kFusedCap / kFusedThreads;     // 8
 
@@ -639,6 +640,12 @@ __global__ void __launch_bounds__(kFusedThreads)
 k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
              const int32_t* kept, const int32_t* kept_count, int32_t* topk_out,
              unsigned long long* arrivals) {
+  // An empty asm that clobbers v127 makes the kernel allocate 128 registers per
+  // thread: its 16 waves then fill the CU's register files (4 waves x 128 of
+  // 512 per SIMD), so no workgroup of the kernel beside the top-k (the EMA
+  // update, 44 registers) lands on a top-k CU and takes its issue slots; the
+  // two then share only HBM.
+  asm volatile("" ::: "v127");
   __shared__ FusedShared sh;
   if (arrivals && threadIdx.x == 0)
     __hip_atomic_fetch_add(arrivals, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
