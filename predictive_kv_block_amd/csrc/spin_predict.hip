@@ -310,21 +310,31 @@ k_select_regs(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept,
   // request's slot, position nor step count, so the loads go out together at
   // once, and a request that turns out to be invalid or still warming up
   // leaves them unused.  (A conditional load per element had made the
-  // compiler put each one behind its own branch and wait.)
+  // compiler put each one behind its own branch and wait.)  With 16 blocks per
+  // thread, registers allow neither that nor holding the words through the
+  // top-P search: the scores are loaded after the request checks and the words
+  // after the top-P search.
+  constexpr bool kEarly = NPL <= 8;
   const uint64_t* u = v.ukey + size_t(b) * v.max_blocks;
   const float* S_row = v.bscore + (size_t(b) * v.max_rows + r) * v.max_blocks;
+  auto block_of = [&](int i) { return e0 + kWave * i < bt.max_blocks ? e0 + kWave * i : 0; };
   float xs[NPL];
   uint64_t xu[NPL];
+  if (kEarly) {
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int j = e0 + kWave * i < bt.max_blocks ? e0 + kWave * i : 0;
-    xu[i] = u[j];
-    xs[i] = S_row[j];
+    for (int i = 0; i < NPL; ++i) {
+      xu[i] = u[block_of(i)];
+      xs[i] = S_row[block_of(i)];
+    }
   }
   const int s = bt.slot[b];
   const int q0 = bt.qpos[b];
   uint8_t* fo = flags_out + size_t(b) * bt.max_blocks;
   if (reject_request(v, bt, s, q0, per_row, fo, kept_count, b)) return;
+  if (!kEarly) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) xs[i] = S_row[block_of(i)];
+  }
   const size_t row = size_t(layer) * v.S + s;
   const int step = v.step[row];
   const int n = num_blocks_of(q0 + r);
@@ -336,15 +346,6 @@ k_select_regs(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept,
   budget(keep_bp, n, v.explore_bp, &kb, &nexp);
   const int pcount = kb - nexp;
   const bool budgeted = keep_bp < 10000 && kb < n;
-  const bool load_s = budgeted && pcount > 0, load_u = budgeted && nexp > 0;
-  uint32_t key[NPL];
-  uint64_t ukey[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const uint32_t m = 0u - (in_row >> i & 1u);
-    key[i] = load_s ? ord_key(xs[i]) & m : 0u;
-    ukey[i] = load_u ? ~xu[i] & (uint64_t(0) - uint64_t(m & 1u)) : 0ull;
-  }
   regs_select_init<kSelectThreads>(sh);
   __syncthreads();
 
@@ -353,9 +354,23 @@ k_select_regs(SpinView v, int layer, spin_batch bt, int keep_bp, int32_t* kept,
     pred = in_row;
   } else {
     int pass = 0;
-    if (pcount > 0) pred = select_largest<NPL, uint32_t>(key, in_row, pcount, sh, pass, s_i);
-    if (nexp > 0)      // smallest word first among the blocks not predicted (nexp < their count)
-      expl = select_largest<NPL, uint64_t>(ukey, in_row & ~pred, nexp, sh, pass, s_i);
+    if (pcount > 0) {
+      uint32_t key[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) key[i] = ord_key(xs[i]) & (0u - (in_row >> i & 1u));
+      pred = select_largest<NPL, uint32_t>(key, in_row, pcount, sh, pass, s_i);
+    }
+    if (nexp > 0) {    // smallest word first among the blocks not predicted (nexp < their count)
+      if (!kEarly) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) xu[i] = u[block_of(i)];
+      }
+      const uint32_t cand = in_row & ~pred;
+      uint64_t ukey[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) ukey[i] = ~xu[i] & (uint64_t(0) - uint64_t(cand >> i & 1u));
+      expl = select_largest<NPL, uint64_t>(ukey, cand, nexp, sh, pass, s_i);
+    }
   }
 
   if (per_row) {

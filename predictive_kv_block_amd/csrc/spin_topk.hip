@@ -184,7 +184,7 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 }
 
 // Exclusive prefix sum over n <= kFusedCandQ ints in LDS; returns the total.
-__device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
+__device__ __forceinline__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
   constexpr int per = kFusedCandQ / kFusedThreads;             // 8
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   int loc[per], sum = 0;
@@ -227,7 +227,7 @@ __device__ int block_exclusive_scan(int* v, int n, int* wave_tot) {
 // sh.skey/spos[0..min(K, live)).  n <= kFusedCap.  Returns min(K, live).
 // Bounds lo <= hi on the live keys, when known (lo > 0), save the workgroup
 // reduction that finds them.
-__device__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out,
+__device__ __forceinline__ int lds_topk(FusedShared& sh, int n, int live, int K, int32_t* out,
                         uint32_t lo = 0u, uint32_t hi = 0u) {
   const int tid = threadIdx.x, w = tid / kWave, l = lane_id();
   uint32_t key[kFusedPerLane];
