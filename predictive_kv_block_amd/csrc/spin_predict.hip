@@ -1,9 +1,10 @@
 // SPIN block predictor: z = max(V, D), block max-pool, budgeted top-P block
 // selection, Philox exploration and the MTP row union.
 //
-// Two kernels per call:
+// Two kernels per call (three when several rows build their own masks):
 //   k_block_scores  (B x R x block-chunks workgroups, streams D and VB, 128
-//                    blocks per wave with one batch of loads in flight)
+//                    blocks per wave, the next batch's loads in flight while
+//                    the current one is reduced)
 //       S_j = max over existing slots i of block j of max(V_i, D_{q-i}).
 //       For a block wholly at or before q this equals max(VB_j, max of the
 //       D window), where VB_j (the block max of V) is kept exact by the update
@@ -17,6 +18,8 @@
 //       blocks with the smallest Philox words among the rest, ballot
 //       compaction of the kept list.  k_select does the same from global
 //       memory for longer contexts.
+//   k_select_union  (union policy only: one workgroup per request) ORs the
+//                    rows' flags and compacts the kept list.
 #include "spin_device.h"
 #include "spin_internal.h"
 #include "spin_select.h"
