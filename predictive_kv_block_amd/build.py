@@ -45,16 +45,15 @@ def _compile(src, build_dir=BUILD, extra=()):
     return obj, errs.strip()
 
 
-def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, defines=(), sources=SOURCES):
+def build(jobs=None, verbose=False, out=LIB, build_dir=BUILD, sources=SOURCES):
     """Compile every HIP source and link the library (default: libspin.so next to
-    this file); `defines` are extra -D macros for tuning experiments."""
+    this file)."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(build_dir, exist_ok=True)
-    extra = [f"-D{d}" for d in defines]
     jobs = jobs or min(len(sources), os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(lambda src: _compile(src, build_dir, extra), sources))
+        results = list(ex.map(lambda src: _compile(src, build_dir), sources))
     for obj, msg in results:
         if msg and verbose:
             print(msg, file=sys.stderr)

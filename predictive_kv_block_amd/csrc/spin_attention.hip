@@ -42,15 +42,9 @@ constexpr int kChunks = kAttnDim / 8;                 // 16-byte chunks per cach
 constexpr int kItems = (kAT / 4) * kChunks;           // (token quad, chunk) staging items
 constexpr int kItemsPerThread = (kItems + 255) / 256;
 constexpr int kQChunks = kAttnDim / 16;               // Q^T operand chunks (k-steps) per lane
-#ifndef SPIN_ATT_QREG
-#define SPIN_ATT_QREG 28
-#endif
-constexpr int kQReg = SPIN_ATT_QREG;                  // chunks held in registers, the rest in LDS
+constexpr int kQReg = 28;                  // chunks held in registers, the rest in LDS
 constexpr int kQLds = kQChunks - kQReg;
-#ifndef SPIN_ATT_MFMA_GROUP
-#define SPIN_ATT_MFMA_GROUP 6
-#endif
-constexpr int kMfmaGroup = SPIN_ATT_MFMA_GROUP;       // MFMAs between scheduling fences
+constexpr int kMfmaGroup = 6;       // MFMAs between scheduling fences
 constexpr int kMaxShare = 4096;                       // top-k entries per share (<= topk)
 constexpr int kMaxShares = 16;                        // shares per row at most
 constexpr double kMergeCostPerShare = 0.008;          // merge cost of one share-row, in tile-times

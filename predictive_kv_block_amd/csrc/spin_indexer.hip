@@ -26,64 +26,22 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
-#ifndef SPIN_IDX_PAGES_PER_WAVE
-#define SPIN_IDX_PAGES_PER_WAVE 32
-#endif
-#ifndef SPIN_IDX_WAVES
-#define SPIN_IDX_WAVES 4
-#endif
-#ifndef SPIN_IDX_NONTEMPORAL
-#define SPIN_IDX_NONTEMPORAL 0
-#endif
-#ifndef SPIN_IDX_STAGES
-#define SPIN_IDX_STAGES 2              // key ring depth: pages in flight + the one on the MFMAs
-#endif
-#ifndef SPIN_IDX_NT_STORE
-#define SPIN_IDX_NT_STORE 1            // streaming (non-temporal) score stores
-#endif
-#ifndef SPIN_IDX_WAVES_PER_EU
-#define SPIN_IDX_WAVES_PER_EU 3        // occupancy target for the register allocator (0: none)
-#endif
-#if SPIN_IDX_WAVES_PER_EU > 0
-#define SPIN_IDX_OCCUPANCY __attribute__((amdgpu_waves_per_eu(SPIN_IDX_WAVES_PER_EU)))
-#else
-#define SPIN_IDX_OCCUPANCY
-#endif
-constexpr int kIdxWaves = SPIN_IDX_WAVES;
-constexpr int kPagesPerWave = SPIN_IDX_PAGES_PER_WAVE;
-#ifndef SPIN_IDX_PAGES_PER_WAVE_MR
-#define SPIN_IDX_PAGES_PER_WAVE_MR 16  // the same with several query rows (more workgroups)
-#endif
+constexpr int kPagesPerWave = 32;    // pages each wave takes in turn, one query row
+constexpr int kPagesPerWaveMR = 16;  // the same with several query rows (more workgroups)
+constexpr int kIdxWaves = 4;         // waves per workgroup
+constexpr int kStages1 = 2;          // key ring depth: pages in flight + the one on the MFMAs
+constexpr int kStagesMR = 2;         // the same with several rows (more compute per page)
+// LDS row stride of the staged queries: 16 bytes of padding after each head
+// row move the 16 head rows that one operand read touches onto different banks.
+constexpr int kQStride = kDim + 16;
+constexpr int kFlushRows = 32;       // page-rows of scores staged per wave before a burst write
+constexpr int kFlushRowsMR = 8;      // the same with several rows (small: 3 workgroups per CU)
+constexpr int kIdxMinPagesPerWg = 16;  // smallest share of the batch's pages a workgroup takes
+constexpr int kIdxRounds = 4;        // dispatch rounds of resident workgroups per launch
 template <int R>
-constexpr int pages_per_wave() { return R == 1 ? kPagesPerWave : SPIN_IDX_PAGES_PER_WAVE_MR; }
-constexpr int kStages1 = SPIN_IDX_STAGES;     // ring depth for one query row
-#ifndef SPIN_IDX_STAGES_MR
-#define SPIN_IDX_STAGES_MR 2           // ring depth with several rows (more compute per page)
-#endif
-#ifndef SPIN_IDX_QPAD
-#define SPIN_IDX_QPAD 16               // bytes of LDS padding after each staged head row
-#endif
-// LDS row stride of the staged queries: the pad moves the 16 head rows that
-// one operand read touches onto different banks.
-constexpr int kQStride = kDim + SPIN_IDX_QPAD;
-#ifndef SPIN_IDX_FLUSH_ROWS
-#define SPIN_IDX_FLUSH_ROWS 32         // page-rows of scores staged per wave before a burst write
-#endif
-constexpr int kFlushRows = SPIN_IDX_FLUSH_ROWS;
-#ifndef SPIN_IDX_FLUSH_ROWS_MR
-#define SPIN_IDX_FLUSH_ROWS_MR 8       // the same with several query rows (small: 3 workgroups per CU)
-#endif
-constexpr int kFlushRowsMR = SPIN_IDX_FLUSH_ROWS_MR;
-#ifndef SPIN_IDX_MIN_PAGES_PER_WG
-#define SPIN_IDX_MIN_PAGES_PER_WG 16   // smallest share of the batch's pages a workgroup takes
-#endif
-constexpr int kIdxMinPagesPerWg = SPIN_IDX_MIN_PAGES_PER_WG;
-#ifndef SPIN_IDX_ROUNDS
-#define SPIN_IDX_ROUNDS 4              // dispatch rounds of resident workgroups per launch
-#endif
-constexpr int kIdxRounds = SPIN_IDX_ROUNDS;
-static_assert(kStages1 >= 2 && SPIN_IDX_STAGES_MR >= 2 && kPagesPerWave + kStages1 <= kWave &&
-                  SPIN_IDX_PAGES_PER_WAVE_MR + SPIN_IDX_STAGES_MR <= kWave,
+constexpr int pages_per_wave() { return R == 1 ? kPagesPerWave : kPagesPerWaveMR; }
+static_assert(kStages1 >= 2 && kStagesMR >= 2 && kPagesPerWave + kStages1 <= kWave &&
+                  kPagesPerWaveMR + kStagesMR <= kWave,
               "indexer pipeline shape");
 static_assert(kQStride % 16 == 0, "16-byte aligned query rows");
 
@@ -124,13 +82,9 @@ k_quantize(SpinView v, spin_batch bt, const uint16_t* q, const float* w) {
   }
 }
 
-// 32 contiguous key bytes; keys are streamed once, so optionally non-temporal.
+// 32 contiguous key bytes.
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
-#if SPIN_IDX_NONTEMPORAL
-  return __builtin_nontemporal_load(reinterpret_cast<const v8i*>(p));
-#else
   return *reinterpret_cast<const v8i*>(p);
-#endif
 }
 
 // One page of keys in MFMA B-operand layout: tile tt holds tokens 16tt..16tt+15,
@@ -286,7 +240,8 @@ __device__ __forceinline__ int64_t readlane64(int64_t x, int src) {
 // neighbours, reach HBM as scattered partial-row writes that stall the key
 // stream far more than their share of the bytes.
 template <int R>
-__global__ void __launch_bounds__(kIdxWaves * kWave) SPIN_IDX_OCCUPANCY
+__global__ void __launch_bounds__(kIdxWaves * kWave)
+    __attribute__((amdgpu_waves_per_eu(3)))   // register budget for 3 waves per SIMD
 k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
           const float* __restrict__ k_scale, int64_t pool_pages, const int32_t* table,
           const int32_t* kept, const int32_t* kept_count, float* scores, float* page_qmax,
@@ -294,7 +249,7 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
   constexpr int kPagesPerWaveR = pages_per_wave<R>();
   constexpr int F = (R == 1 ? kFlushRows : kFlushRowsMR) / R > 0
                         ? (R == 1 ? kFlushRows : kFlushRowsMR) / R : 1;   // pages per flush
-  constexpr int kStages = R == 1 ? kStages1 : SPIN_IDX_STAGES_MR;
+  constexpr int kStages = R == 1 ? kStages1 : kStagesMR;
   __shared__ __attribute__((aligned(16))) uint8_t s_q[R * kHeads * kQStride];
   __shared__ float s_w[R * kHeads];
   __shared__ __attribute__((aligned(16))) float s_out[kIdxWaves * R * F * kBlock];
@@ -466,11 +421,7 @@ k_indexer(SpinView v, spin_batch bt, const uint8_t* __restrict__ k_pool,
                 for (int i0 = 0; i0 < F * (kBlock / 4); i0 += kWave) {
                   const int x = i0 + l;
                   if (x < n4) {
-#if SPIN_IDX_NT_STORE
-                    __builtin_nontemporal_store(src[x], dst + x);
-#else
-                    dst[x] = src[x];
-#endif
+                    __builtin_nontemporal_store(src[x], dst + x);   // streaming
                   }
                 }
                 if (R == 1 && page_qmax && l <= mf) {

@@ -29,10 +29,7 @@ namespace {
 
 constexpr int kScoreWaves = 4;        // waves per workgroup in k_block_scores
 constexpr int kScoreBatch = 16;       // blocks per load batch (one D load per lane per block)
-#ifndef SPIN_SCORE_BATCHES
-#define SPIN_SCORE_BATCHES 8
-#endif
-constexpr int kScoreBatchesPerWave = SPIN_SCORE_BATCHES;
+constexpr int kScoreBatchesPerWave = 8;
 constexpr int kScoreBlocksPerWave = kScoreBatch * kScoreBatchesPerWave;   // 128
 static_assert(kScoreBatchesPerWave % 2 == 0, "double-buffered batches");
 constexpr int kSelectThreads = 1024;

@@ -142,11 +142,8 @@ constexpr int kFusedCandQ = 8192;
 constexpr int kFusedCap = 8192;                              // survivors held in LDS
 constexpr int kFusedPerLane = kFusedCap / kFusedThreads;     // 8
 
-#ifndef SPIN_TOPK_BATCH
-#define SPIN_TOPK_BATCH 256
-#endif
-static_assert(SPIN_TOPK_BATCH % 16 == 0 && SPIN_TOPK_BATCH <= 256, "16 quarters per load");
-constexpr int kFusedBatch = SPIN_TOPK_BATCH;                 // quarters per wave step
+constexpr int kFusedBatch = 256;                             // quarters per wave step
+static_assert(kFusedBatch % 16 == 0 && kFusedBatch <= 256, "16 quarters per load");
 
 struct FusedShared {
   TopkShared t;
