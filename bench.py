@@ -691,13 +691,37 @@ def _fidelity(mode, wl, device, targets):
 
         runs.append((f"per_layer_{source}",
                      _fidelity_trace(wl, inputs, device, "union", "prefix", keep_of), plan))
+    # the same v3 passage read through each layer's miss curve: W calibration
+    # rounds at every keep of a grid (each grid keep on its own fresh state, the
+    # mean's from the uniform run), then spin_allocate_budgets_curve
+    step = max(mean_keep // 4, 1)
+    grid = sorted({min(10000, mean_keep // 2 + i * step) for i in range(10000 // step + 3)})
+    curve = np.zeros((wl.layers, len(grid)))
+    for gi, g in enumerate(grid):
+        if g == 10000:
+            continue                  # every block kept: nothing can be missed
+        m = uni[0][:W] if g == mean_keep else _fidelity_trace(
+            wl, inputs, device, "union", "prefix", lambda t, l, m, e, g=g: g, rounds=W)[0]
+        s = _fidelity_summary(m, np.ones((W, wl.layers, wl.batch)), np.full((W, wl.layers), g),
+                              qpos, wl.rows, warm)
+        curve[:, gi] = [p["mean_miss"] or 0.0 for p in s["per_layer"]]
+        print(f"[fidelity] calibration at keep {g}: per-layer mean miss "
+              f"{[round(float(x), 4) for x in curve[:, gi]]}", file=sys.stderr, flush=True)
+    cplan = {"calib_grid_bp": grid, "calib_miss_curve": curve.tolist(),
+             "keep": spin.spin_allocate_budgets_curve(curve.tolist(), grid, mean_keep)}
+    runs.append(("per_layer_curve", _fidelity_trace(
+        wl, inputs, device, "union", "prefix",
+        lambda t, l, m, e: mean_keep if t < W else cplan["keep"][l]), cplan))
     for name, (miss, kept_n, keeps, est), plan in runs:
         s = _fidelity_summary(miss, kept_n, keeps, qpos, wl.rows, warm, first_round=W, est=est)
         rec = {"fidelity": "layer_budgets", "workload": wl.name, "mean_keep_bp": mean_keep,
                "calibration_rounds": W, "budgets": name,
                "keep_bp": [int(k) for k in keeps[-1]], **s}
-        if plan:
+        if plan and "calib_miss" in plan:
             rec["calibration_mean_miss"] = plan["calib_miss"]
+        if plan and "calib_miss_curve" in plan:
+            rec["calibration_grid_bp"] = plan["calib_grid_bp"]
+            rec["calibration_miss_curve"] = plan["calib_miss_curve"]
         print(json.dumps(rec), flush=True)
         out.append(rec)
     return out

@@ -17,7 +17,7 @@
  * Measurement calls beside the round: spin_measure_miss (against an all-keep
  * top-k), spin_estimate_miss (from exploration hits alone), spin_slot_scores
  * and spin_predictor_fidelity (a slot predictor against the indexer), and the
- * host allocator spin_allocate_budgets.
+ * host allocators spin_allocate_budgets and spin_allocate_budgets_curve.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked [host].
@@ -416,6 +416,21 @@ int spin_sparse_attention(const spin_batch* batch, int topk, const int32_t* topk
  * integer basis points by largest remainder (ties to the lower layer).
  * miss: [host] double [L]; keep_bp_out: [host] int32 [L]. */
 int spin_allocate_budgets(int L, const double* miss, int mean_keep_bp, int32_t* keep_bp_out);
+
+/* [host] Per-layer keep budgets from each layer's miss measured at several
+ * keeps (the same v3 abstract passage, read the other way: the measured miss
+ * at more than one budget gives each layer's slope).
+ * READING: every layer starts at grid_bp[0]; while L * mean_keep_bp has room
+ * for some layer's next grid step, that step goes to the layer whose measured
+ * miss falls most per basis point of the step (ties to the lower layer); the
+ * result is the grid keep each layer reached.  For curves convex in the keep
+ * this is the least summed miss over grid points within the total.
+ * miss_curve: [host] double [L][G], miss_curve[l][g] = layer l's mean miss with
+ * every layer at keep grid_bp[g], each in [0, 1]; grid_bp: [host] int32 [G],
+ * strictly ascending in [0, 10000], grid_bp[0] <= mean_keep_bp; keep_bp_out:
+ * [host] int32 [L].  1 <= L <= 4096, 1 <= G <= 64; SPIN_EINVAL otherwise. */
+int spin_allocate_budgets_curve(int L, int G, const double* miss_curve, const int32_t* grid_bp,
+                                int mean_keep_bp, int32_t* keep_bp_out);
 
 /* [host] Static text for a status code (and the last HIP error, if any). */
 const char* spin_status_string(int status);

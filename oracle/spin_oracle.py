@@ -558,6 +558,40 @@ def allocate_budgets(miss, mean_keep_bp, eps=1e-3):
     return out
 
 
+def allocate_budgets_curve(miss_curve, grid_bp, mean_keep_bp):
+    """Per-layer keep budgets from each layer's miss measured at several keeps.
+
+    READING (an alternative to allocate_budgets) of the v3 abstract, where the
+    layers' block budget follows their measured miss rates: miss_curve[l][g] is
+    layer l's mean miss measured with every layer at keep grid_bp[g] (grid
+    ascending).  Every layer starts at grid_bp[0]; while the total
+    L * mean_keep_bp still has room for some layer's next grid step, that step
+    goes to the layer whose measured miss falls the most per basis point of the
+    step (a rise counts as a negative fall), ties to the lower layer.  This is
+    marginal allocation: for curves convex in the keep it gives the least summed
+    miss over grid points within the total.
+    """
+    m = np.asarray(miss_curve, dtype=np.float64)
+    g = [int(x) for x in grid_bp]
+    L = m.shape[0]
+    room = L * int(mean_keep_bp) - L * g[0]
+    pos = [0] * L
+    while True:
+        best, best_gain = -1, None
+        for l in range(L):
+            i = pos[l]
+            if i + 1 >= len(g) or g[i + 1] - g[i] > room:
+                continue
+            gain = (m[l, i] - m[l, i + 1]) / (g[i + 1] - g[i])
+            if best < 0 or gain > best_gain:
+                best, best_gain = l, gain
+        if best < 0:
+            break
+        room -= g[pos[best] + 1] - g[pos[best]]
+        pos[best] += 1
+    return np.array([g[i] for i in pos], dtype=np.int64)
+
+
 # ---------------------------------------------------------------------------
 # One decode round for one request and one layer.
 # ---------------------------------------------------------------------------

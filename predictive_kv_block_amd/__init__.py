@@ -14,7 +14,8 @@ __all__ = [
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_topk_update", "spin_measure_miss", "spin_allocate_budgets",
-    "spin_status_string", "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
+    "spin_allocate_budgets_curve", "spin_status_string", "spin_slot_scores", "spin_estimate_miss",
+    "spin_predictor_fidelity",
     "spin_attention_workspace_bytes", "spin_sparse_attention", "spin_topk_scores_noalloc",
     "EXPORTS",
 ]
@@ -26,7 +27,8 @@ EXPORTS = [
     "spin_reset_slots", "spin_predict_blocks", "spin_quantize_q", "spin_indexer_scores",
     "spin_topk_scores", "spin_topk_workspace_bytes", "spin_indexer_topk", "spin_update",
     "spin_mtp_replay", "spin_topk_update", "spin_measure_miss", "spin_allocate_budgets",
-    "spin_status_string", "spin_slot_scores", "spin_estimate_miss", "spin_predictor_fidelity",
+    "spin_allocate_budgets_curve", "spin_status_string", "spin_slot_scores", "spin_estimate_miss",
+    "spin_predictor_fidelity",
     "spin_attention_workspace_bytes", "spin_sparse_attention", "spin_topk_scores_noalloc",
 ]
 
@@ -89,6 +91,9 @@ _SIGS = {
     "spin_measure_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp],
     "spin_allocate_budgets": [_i32, ctypes.POINTER(ctypes.c_double), _i32,
                               ctypes.POINTER(ctypes.c_int32)],
+    "spin_allocate_budgets_curve": [_i32, _i32, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int32), _i32,
+                                    ctypes.POINTER(ctypes.c_int32)],
     "spin_status_string": [_i32],
     "spin_slot_scores": [_vp, _i32, ctypes.POINTER(SpinBatch), _vp, _vp],
     "spin_estimate_miss": [ctypes.POINTER(SpinBatch), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -299,6 +304,19 @@ def spin_allocate_budgets(miss, mean_keep_bp):
     arr = (ctypes.c_double * L)(*[float(m) for m in miss])
     out = (ctypes.c_int32 * L)()
     _check(load().spin_allocate_budgets(L, arr, int(mean_keep_bp), out))
+    return [int(x) for x in out]
+
+
+def spin_allocate_budgets_curve(miss_curve, grid_bp, mean_keep_bp):
+    """miss_curve: L rows of G mean miss rates, one per keep of grid_bp."""
+    L, G = len(miss_curve), len(grid_bp)
+    flat = [float(m) for row in miss_curve for m in row]
+    if len(flat) != L * G:
+        raise SpinError(SPIN_EINVAL, "miss_curve rows must have one value per grid keep")
+    arr = (ctypes.c_double * (L * G))(*flat)
+    grid = (ctypes.c_int32 * G)(*[int(g) for g in grid_bp])
+    out = (ctypes.c_int32 * L)()
+    _check(load().spin_allocate_budgets_curve(L, G, arr, grid, int(mean_keep_bp), out))
     return [int(x) for x in out]
 
 

@@ -481,6 +481,48 @@ int spin_allocate_budgets(int L, const double* miss, int mean_keep_bp, int32_t* 
   return SPIN_OK;
 }
 
+int spin_allocate_budgets_curve(int L, int G, const double* miss_curve, const int32_t* grid_bp,
+                                int mean_keep_bp, int32_t* keep_bp_out) {
+  if (L < 1 || L > 4096 || G < 1 || G > 64 || !miss_curve || !grid_bp || !keep_bp_out ||
+      mean_keep_bp < 0 || mean_keep_bp > 10000)
+    return SPIN_EINVAL;
+  for (int g = 0; g < G; ++g)
+    if (grid_bp[g] < 0 || grid_bp[g] > 10000 || (g > 0 && grid_bp[g] <= grid_bp[g - 1]))
+      return SPIN_EINVAL;
+  if (grid_bp[0] > mean_keep_bp) return SPIN_EINVAL;
+  for (long i = 0; i < long(L) * G; ++i)
+    if (!(miss_curve[i] >= 0.0 && miss_curve[i] <= 1.0)) return SPIN_EINVAL;
+  // every layer starts at the lowest grid keep; each pass hands the next grid
+  // step to the layer whose miss falls most per basis point, among the steps
+  // that still fit in the total (ties to the lower layer)
+  int* pos = new (std::nothrow) int[L];
+  if (!pos) return SPIN_EINVAL;
+  for (int l = 0; l < L; ++l) pos[l] = 0;
+  long room = long(L) * mean_keep_bp - long(L) * grid_bp[0];
+  for (;;) {
+    int best = -1;
+    double best_gain = 0.0;
+    for (int l = 0; l < L; ++l) {
+      const int i = pos[l];
+      if (i + 1 >= G) continue;
+      const int step = grid_bp[i + 1] - grid_bp[i];
+      if (step > room) continue;
+      const double gain =
+          (miss_curve[long(l) * G + i] - miss_curve[long(l) * G + i + 1]) / double(step);
+      if (best < 0 || gain > best_gain) {
+        best = l;
+        best_gain = gain;
+      }
+    }
+    if (best < 0) break;
+    room -= grid_bp[pos[best] + 1] - grid_bp[pos[best]];
+    ++pos[best];
+  }
+  for (int l = 0; l < L; ++l) keep_bp_out[l] = grid_bp[pos[l]];
+  delete[] pos;
+  return SPIN_OK;
+}
+
 const char* spin_status_string(int status) {
   switch (status) {
     case SPIN_OK: return "ok";

@@ -102,6 +102,31 @@ def test_allocate_budgets_matches_oracle(L, mean):
         spin.spin_allocate_budgets([0.1, 1.5], 5000)
 
 
+@pytest.mark.parametrize("L,G", [(1, 1), (4, 7), (9, 5), (61, 12)])
+def test_allocate_budgets_curve_matches_oracle(L, G):
+    rng = np.random.default_rng(L * 97 + G)
+    for trial in range(25):
+        steps = rng.integers(1, 2500, size=G)
+        grid = np.cumsum(steps) - steps[0] + int(rng.integers(0, 2500))
+        grid = np.minimum(grid, 10000 - (G - 1 - np.arange(G)))     # ascending, <= 10000
+        if trial % 3 == 0:
+            curve = np.sort(rng.random((L, G)), axis=1)[:, ::-1]   # falling with the keep
+        else:
+            curve = rng.random((L, G))
+        if trial == 1:
+            curve = np.round(curve * 4) / 4                           # many equal gains
+        mean = int(rng.integers(grid[0], 10001))
+        got = spin.spin_allocate_budgets_curve(curve.tolist(), grid.tolist(), mean)
+        exp = O.allocate_budgets_curve(curve, grid, mean)
+        assert got == [int(x) for x in exp]
+    with pytest.raises(spin.SpinError):
+        spin.spin_allocate_budgets_curve([[0.1, 0.2]], [5000, 4000], 5000)    # not ascending
+    with pytest.raises(spin.SpinError):
+        spin.spin_allocate_budgets_curve([[0.1, 0.2]], [6000, 8000], 5000)    # floor above mean
+    with pytest.raises(spin.SpinError):
+        spin.spin_allocate_budgets_curve([[0.1, 1.5]], [4000, 8000], 5000)    # miss outside [0, 1]
+
+
 def test_header_is_plain_c_and_links():
     """include/spin.h compiles as C11, and a C program that takes the address
     of every entry point links against libspin.so (the boundary is a C ABI)."""

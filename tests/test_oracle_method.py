@@ -375,3 +375,65 @@ def test_allocate_budgets_clamped_closed_forms():
     rest = Fraction(3 * 6500 - 10000)
     assert out[2] == 10000
     assert list(out[:2]) == _largest_remainder([rest * w[0] / sum(w), rest * w[1] / sum(w)])
+
+
+def _convex_curve(rng, G):
+    """A non-increasing curve, convex in the grid index, with distinct steps."""
+    drops = np.sort(rng.random(G - 1))[::-1] * rng.uniform(0.05, 0.3)
+    return np.concatenate([[drops.sum()], drops.sum() - np.cumsum(drops)])
+
+
+@pytest.mark.parametrize("L,G,seed", [(2, 3, 1), (2, 5, 2), (3, 4, 3), (3, 5, 4), (4, 4, 5)])
+def test_allocate_budgets_curve_is_least_summed_miss_on_convex_curves(L, G, seed):
+    """Brute force over every grid assignment within the total: on curves convex
+    in the keep (equal grid steps) marginal allocation reaches the least sum."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    grid = [2500 + 1250 * i for i in range(G)]
+    for trial in range(30):
+        curve = np.stack([_convex_curve(rng, G) for _ in range(L)])
+        mean = grid[int(rng.integers(0, G))]
+        out = O.allocate_budgets_curve(curve, grid, mean)
+        best = min(sum(curve[l, c[l]] for l in range(L))
+                   for c in itertools.product(range(G), repeat=L)
+                   if sum(grid[i] for i in c) <= L * mean)
+        got = sum(curve[l, grid.index(int(out[l]))] for l in range(L))
+        assert got == pytest.approx(best, abs=1e-12)
+        assert out.sum() == L * mean                     # equal steps: the total is spent
+
+
+def test_allocate_budgets_curve_closed_forms():
+    grid = [2500, 5000, 7500, 10000]
+    # identical curves: every layer stays at the mean
+    flat = [[0.4, 0.2, 0.1, 0.0]] * 3
+    assert list(O.allocate_budgets_curve(flat, grid, 5000)) == [5000] * 3
+    # a layer whose miss does not move gives its steps to one that falls steeply
+    curve = [[0.05, 0.05, 0.05, 0.05], [0.6, 0.3, 0.1, 0.0]]
+    assert list(O.allocate_budgets_curve(curve, grid, 5000)) == [2500, 7500]
+    assert list(O.allocate_budgets_curve(curve, grid, 6250)) == [2500, 10000]
+    # equal gains go to the lower layer first
+    tie = [[0.5, 0.25, 0.0, 0.0], [0.5, 0.25, 0.0, 0.0]]
+    assert list(O.allocate_budgets_curve(tie, grid, 6250)) == [7500, 5000]
+    # uneven grid: the gain is per basis point of the step
+    g2 = [4000, 5000, 8000]
+    c2 = [[0.30, 0.20, 0.10], [0.30, 0.26, 0.00]]      # 1e-4/bp, then 3.3e-5/bp; 4e-5/bp, then 8.7e-5/bp
+    assert list(O.allocate_budgets_curve(c2, g2, 5000)) == [5000, 5000]
+    assert list(O.allocate_budgets_curve(c2, g2, 6500)) == [5000, 8000]
+    # the mean at the lowest grid point: nothing to hand out
+    assert list(O.allocate_budgets_curve(curve, grid, 2500)) == [2500, 2500]
+
+
+def test_allocate_budgets_curve_invariants():
+    rng = np.random.default_rng(11)
+    grid = [2000, 3000, 4500, 5000, 7000, 10000]
+    for trial in range(200):
+        L = int(rng.integers(1, 9))
+        curve = rng.random((L, len(grid)))              # not monotone, not convex
+        mean = int(rng.integers(2000, 10001))
+        out = O.allocate_budgets_curve(curve, grid, mean)
+        assert all(int(k) in grid for k in out)
+        assert out.sum() <= L * mean
+        room = L * mean - out.sum()
+        for l in range(L):                              # no further step fits
+            i = grid.index(int(out[l]))
+            assert i + 1 == len(grid) or grid[i + 1] - grid[i] > room
