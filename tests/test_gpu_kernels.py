@@ -68,7 +68,7 @@ def _rand_pool(rng, pages, d=128):
     return codes, sc.float()
 
 
-@pytest.mark.parametrize("R", [1, 2, 4])
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
 def test_indexer_scores_parity(gpu_lib, R):
     rng = np.random.default_rng(R)
     B, mb, pages = 3, 40, 150
@@ -282,7 +282,9 @@ POOL_NAMES = {spin.SPIN_POOL_MAX: O.POOL_MAX, spin.SPIN_POOL_MEAN: O.POOL_MEAN,
     (1, 6000, 500, 3, 200, spin.SPIN_POOL_MEAN), (1, 5000, 1000, 2, 200, spin.SPIN_POOL_TOP4),
     (4, 5000, 1000, 2, 200, spin.SPIN_MASK_ROW0),
     (4, 6000, 500, 3, 200, spin.SPIN_MASK_ROW0 | spin.SPIN_POOL_TOP4),
-    (2, 5000, 500, 1, 12000, spin.SPIN_POOL_MEAN), (2, 5000, 500, 1, 17000, spin.SPIN_MASK_ROW0)])
+    (2, 5000, 500, 1, 12000, spin.SPIN_POOL_MEAN), (2, 5000, 500, 1, 17000, spin.SPIN_MASK_ROW0),
+    # three verification rows (draft length 2)
+    (3, 5000, 1000, 2, 200, 0), (3, 6000, 500, 3, 4096, 0), (3, 5000, 1000, 2, 300, spin.SPIN_MASK_ROW0)])
 def test_predict_exact(gpu_lib, R, keep_bp, explore_bp, step, blocks, policy):
     _predict_case(R, keep_bp, explore_bp, step, blocks, policy, "random")
 
@@ -367,7 +369,7 @@ def _predict_case(R, keep_bp, explore_bp, step, blocks, policy, kind):
 
 
 # ------------------------------------------------------ update and replay
-@pytest.mark.parametrize("R", [1, 4])
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
 def test_update_and_replay_parity(gpu_lib, R):
     rng = np.random.default_rng(40 + R)
     B, ctx = 5, 64 * 60
