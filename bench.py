@@ -79,8 +79,6 @@ def _args():
     ap.add_argument("--sparsity-bp", type=int, default=5000)
     ap.add_argument("--sweep", default="0,4000", help="extra sparsities (bp) timed for scaling")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quantize-on-main", action="store_true",
-                    help="run the query quantiser on the main stream after the predictor")
     ap.add_argument("--cpu-requests", type=int, default=64)
     ap.add_argument("--pools", type=int, default=1,
                     help="independently drawn key pools, round t reading pool t mod N, so that "
@@ -113,9 +111,12 @@ def _setup(wl, device):
     st = spin.SpinState(cfg, device=device)
     slot = torch.arange(B, dtype=torch.int32, device=device)
     spin.spin_reset_slots(st.handle, slot, torch.arange(B, dtype=torch.int64, device=device) + 1000)
-    qpos = torch.zeros(B, dtype=torch.int32, device=device)
+    # two position buffers (and batches over them): round t writes buffer
+    # t % 2 while round t - 1's update may still read the other
+    qpos_ring = [torch.zeros(B, dtype=torch.int32, device=device) for _ in range(2)]
+    batches = [spin.make_batch(slot, qp, wl.rows, nb) for qp in qpos_ring]
     bufs = dict(
-        slot=slot, qpos=qpos, batch=spin.make_batch(slot, qpos, wl.rows, nb),
+        slot=slot, qpos=qpos_ring[0], batch=batches[0], qpos_ring=qpos_ring, batches=batches,
         kept=torch.zeros(B, nb, dtype=torch.int32, device=device),
         cnt=torch.zeros(B, dtype=torch.int32, device=device),
         flags=torch.zeros(B, nb, dtype=torch.uint8, device=device),
@@ -128,93 +129,95 @@ def _setup(wl, device):
     return spin, pool, cfg, st, bufs, make_queries
 
 
-QUANTIZE_ON_SIDE = True
+def _round(spin, st, bufs, pool, qpos, q, w, keep_bp, streams, t, prev=None, ev=None,
+           accepted=None, tail="beside"):
+    """Round t of a run, enqueued without host waits.
 
-
-def _round(spin, st, bufs, pool, q, w, keep_bp, side, prev_end, ev=None, accepted=None,
-           tail="beside"):
-    """One SPIN round.
-
-    Main stream: predict -> indexer -> the round's tail (spin_topk_update).
-    `side` runs the query quantisation beside the predictor (both start once
-    the previous round is done; they touch disjoint memory) and, with
-    tail="beside", the EMA update beside the top-k, behind the library's gate
-    (it opens once every top-k workgroup has started).  tail="behind" runs the
-    update on the main stream after the top-k.  `ev` = 8 timing events (0-4
-    on the main stream around predict, the wait for the quantiser, indexer and
-    top-k; 5-6 on the quantiser's stream around it; 7 at the update's end), or
-    None.  `accepted` (int32 [B], device): MTP acceptances, whose
-    prefix-valid replay replaces the single-row update.  Returns the event
-    that marks the round's end.
+    Both schedules keep the round's critical chain (predict -> indexer ->
+    top-k -> EMA update -> next predict) free of waits between streams, and
+    write the next round's inputs ahead on the other stream: the query
+    positions go into buffer t % 2 (round t - 2's, long done) and the query
+    quantisation follows, beside the previous round's top-k and update, which
+    touch neither.  The round's main stream waits for them before the
+    predictor.
+    tail="behind": the chain runs on streams[0]: the top-k, then the update
+    (spin_topk_scores, then spin_update or spin_mtp_replay).  The inputs go on
+    streams[1] once the previous round's indexer (the last reader of the
+    quantised queries) is done.
+    tail="beside": the streams take turns.  Round t's chain up to the top-k
+    runs on streams[t % 2]; its update runs on the other stream beside the
+    top-k, behind the library's gate (spin_topk_update: it opens once every
+    top-k workgroup has started); round t + 1 runs on the stream of round t's
+    update.  The inputs go on the stream of round t - 1's top-k, after it.
+    `qpos`: int32 [B] device positions of round t; `prev`: what the previous
+    call returned (None for the first round); `ev` = 8 timing events (0-4 on
+    main around the predictor, the indexer and the top-k; 5-6 around the
+    quantiser; 7 at the update's end), or None; `accepted` (int32 [B],
+    device): MTP acceptances, whose prefix-valid replay replaces the
+    single-row update.  Returns (the batch used, the event after the indexer).
     """
     import torch
 
     b = bufs
-    main = torch.cuda.current_stream()
-    if prev_end is not None:
-        main.wait_event(prev_end)
+    beside = tail == "beside"
+    main = streams[t % 2] if beside else streams[0]
+    side = streams[(t + 1) % 2] if beside else streams[1]
     ev = ev or [None] * 8
     rec = lambda e, s: e.record(s) if e is not None else None
+    batch = b["batches"][t % 2]
+    if prev is not None:
+        side.wait_event(prev[1])            # (beside: already in order on this stream)
+    with torch.cuda.stream(side):
+        b["qpos_ring"][t % 2].copy_(qpos)
+    rec(ev[5], side)
+    spin.spin_quantize_q(st.handle, batch, q, w, stream=side)
+    rec(ev[6], side)
+    ahead = torch.cuda.Event()
+    ahead.record(side)
+    main.wait_event(ahead)
     rec(ev[0], main)
-    # quantiser on the side stream, ordered after the previous round.  It is
-    # enqueued before the predictor: the block-score kernel fills every wave
-    # slot of the chip, and a quantiser enqueued after it would wait for the
-    # slots it frees
-    qs = side if QUANTIZE_ON_SIDE else main
-    if QUANTIZE_ON_SIDE:
-        if prev_end is not None:
-            side.wait_event(prev_end)
-        rec(ev[5], qs)
-        spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
-        rec(ev[6], qs)
-    spin.spin_predict_blocks(st.handle, 0, b["batch"], keep_bp, b["kept"], b["cnt"], b["flags"])
+    spin.spin_predict_blocks(st.handle, 0, batch, keep_bp, b["kept"], b["cnt"], b["flags"],
+                             stream=main)
     rec(ev[1], main)
-    if not QUANTIZE_ON_SIDE:
-        rec(ev[5], qs)
-        spin.spin_quantize_q(st.handle, b["batch"], q, w, stream=qs)
-        rec(ev[6], qs)
-    if QUANTIZE_ON_SIDE:
-        q_done = torch.cuda.Event()
-        q_done.record(side)
-        main.wait_event(q_done)
     rec(ev[2], main)
-    spin.spin_indexer_scores(st.handle, b["batch"], pool.key_codes, pool.key_scale,
-                             pool.block_table, b["kept"], b["cnt"], b["scores"], b["pq"])
+    spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale, pool.block_table,
+                             b["kept"], b["cnt"], b["scores"], b["pq"], stream=main)
     rec(ev[3], main)
-    # the library's tail: the top-k on the main stream, the EMA update (or
-    # the replay) beside it on `side` (tail="beside", gated by the library so
-    # that it never takes the top-k's CUs) or behind it on main ("behind")
-    spin.spin_topk_update(st.handle, 0, b["batch"], b["scores"], b["pq"], b["kept"], b["cnt"],
-                          b["topk"], accepted, update_stream=side if tail == "beside" else None)
-    rec(ev[4], main)                      # the top-k's end (with "behind", the update's)
-    us = side if tail == "beside" else main
-    rec(ev[7], us)
-    end = torch.cuda.Event()
-    end.record(us)
-    if tail == "beside":
-        # the round ends when the top-k (main) and the update (side) are done
-        main_done = torch.cuda.Event()
-        main_done.record(main)
-        side.wait_event(main_done)
-        end = torch.cuda.Event()
-        end.record(side)
-    return end
+    indexed = torch.cuda.Event()
+    indexed.record(main)
+    if beside:
+        spin.spin_topk_update(st.handle, 0, batch, b["scores"], b["pq"], b["kept"], b["cnt"],
+                              b["topk"], accepted, stream=main, update_stream=side)
+        rec(ev[4], main)
+        rec(ev[7], side)
+    else:
+        spin.spin_topk_scores(batch, st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
+                              None, b["pq"], stream=main)
+        rec(ev[4], main)
+        if accepted is None:
+            spin.spin_update(st.handle, 0, batch, b["scores"], b["kept"], b["cnt"], stream=main)
+        else:
+            spin.spin_mtp_replay(st.handle, 0, batch, accepted, b["scores"], b["kept"], b["cnt"],
+                                 stream=main)
+        rec(ev[7], main)
+    return batch, indexed
 
 
 # timing passes: (name, tail, events recorded per round)
-PASSES = (("lean", "beside", (0, 4, 7)), ("serial", "behind", (0, 7)),
+PASSES = (("lean", "beside", (0, 4, 7)), ("behind", "behind", (0, 4, 7)),
           ("detailed", "beside", tuple(range(8))))
 
 
 def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
     """Per keep and per timing pass of PASSES, `warmup` untimed rounds then
     `steps` timed rounds, all from the same state reset and inputs:
-      lean      the library's round with the update beside the top-k, 3
-                events per round (its start, the top-k's end, the update's
-                end): value, ms_per_step, the predict + index + top-k latency
-                and the whole step.
-      serial    the same round with the update behind the top-k on one stream
-                (2 events): the whole step without the overlap.
+      lean      the round with the update beside the top-k on the other
+                stream, behind the library's gate, 3 events per round (its
+                start, the top-k's end, the update's end): value,
+                ms_per_step, the predict + index + top-k latency and the
+                whole step.
+      behind    the round with the update behind the top-k on one stream
+                (3 events): the same figures without the overlap.
       detailed  the lean round with events around every stage (8 per round):
                 the stage times, the sweep's indexer times and the roofline.
     Returns {keep: {pass name: {...}}}."""
@@ -242,18 +245,18 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
     qpos_all = qpos_all.to(torch.int32).to(device)
     torch.cuda.synchronize()
     results = {}
-    side = torch.cuda.Stream(device=device)          # default priority
+    streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device))  # default priority
     acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
     for keep_bp in keep_bps:
         results[keep_bp] = {}
         for name, tail, recorded in PASSES:
             spin.spin_reset_slots(st.handle, bufs["slot"],
                                   torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
-            done = None
+            torch.cuda.synchronize()
+            prev = None
             for t in range(warmup):
-                bufs["qpos"].copy_(qpos_all[t])
-                done = _round(spin, st, bufs, pools[t % n_pools], qs[t][0], qs[t][1], keep_bp,
-                              side, done, accepted=acc_of(t), tail=tail)
+                prev = _round(spin, st, bufs, pools[t % n_pools], qpos_all[t], qs[t][0],
+                              qs[t][1], keep_bp, streams, t, prev, accepted=acc_of(t), tail=tail)
             torch.cuda.synchronize()
             evs = []
             for _ in range(steps):
@@ -263,12 +266,12 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
                 evs.append(e)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            done = None
+            prev = None
             for t in range(steps):
-                bufs["qpos"].copy_(qpos_all[warmup + t])
                 q, w = qs[warmup + t]
-                done = _round(spin, st, bufs, pools[(warmup + t) % n_pools], q, w, keep_bp, side,
-                              done, evs[t], accepted=acc_of(warmup + t), tail=tail)
+                prev = _round(spin, st, bufs, pools[(warmup + t) % n_pools], qpos_all[warmup + t],
+                              q, w, keep_bp, streams, warmup + t, prev, evs[t],
+                              accepted=acc_of(warmup + t), tail=tail)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
             per = {"step": [e[0].elapsed_time(e[7]) * 1e3 for e in evs]}      # us
@@ -281,11 +284,13 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
                                for e in evs]
             if name == "detailed":
                 per["predict"] = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-                per["quantize"] = [e[5].elapsed_time(e[6]) * 1e3 for e in evs]  # beside predict
+                per["quantize"] = [e[5].elapsed_time(e[6]) * 1e3 for e in evs]  # ahead, on the side stream
                 per["indexer"] = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
                 per["topk"] = [e[3].elapsed_time(e[4]) * 1e3 for e in evs]
-                # the update beside the top-k: from the indexer's end to its own
-                per["update"] = [e[3].elapsed_time(e[7]) * 1e3 for e in evs]
+                # the update: from the top-k's end (behind it) or the indexer's
+                # end (beside it) to its own
+                u0 = 4 if tail == "behind" else 3
+                per["update"] = [e[u0].elapsed_time(e[7]) * 1e3 for e in evs]
             cnt = bufs["cnt"].cpu()
             kept_pages = int(cnt.sum())
             if st.error() != 0:
@@ -741,13 +746,17 @@ def _attention_bench(wl, device, steps, warmup, keep_bp):
     spin, pool, cfg, st, bufs, make_queries = _setup(wl, device)
     from workload import positions
 
-    side = torch.cuda.Stream(device=device)
+    streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device))
     qp = positions(wl)
-    done = None
+    rounds = []
     for t, keep in enumerate((10000, keep_bp)):
-        bufs["qpos"].copy_(qp[t].to(torch.int32))
         q, w = make_queries(wl, pool, 0, t, qp[t].tolist(), device=device)
-        done = _round(spin, st, bufs, pool, q, w, keep, side, done)
+        rounds.append((qp[t].to(device=device, dtype=torch.int32), q, w, keep))
+    torch.cuda.synchronize()
+    prev = None
+    for t, (qpos, q, w, keep) in enumerate(rounds):
+        prev = _round(spin, st, bufs, pool, qpos, q, w, keep, streams, t, prev)
+    batch = prev[0]
     torch.cuda.synchronize()
     H, D, DV = 128, 576, 512
     g = torch.Generator(device=device)
@@ -757,12 +766,12 @@ def _attention_bench(wl, device, steps, warmup, keep_bp):
         kv[i:i + 8192].copy_(torch.randn(min(8192, wl.pool_pages - i), 64, D, device=device,
                                          generator=g))
     qa = torch.randn(wl.batch, wl.rows, H, D, device=device, generator=g).to(torch.bfloat16)
-    n = spin.spin_attention_workspace_bytes(bufs["batch"], wl.topk)
+    n = spin.spin_attention_workspace_bytes(batch, wl.topk)
     ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
     out = torch.empty(wl.batch, wl.rows, H, DV, dtype=torch.bfloat16, device=device)
     lse = torch.empty(wl.batch, wl.rows, H, device=device)
     scale = 1.0 / 192 ** 0.5
-    args = (bufs["batch"], wl.topk, bufs["topk"], qa, kv, pool.block_table, scale, out, lse, ws)
+    args = (batch, wl.topk, bufs["topk"], qa, kv, pool.block_table, scale, out, lse, ws)
     for _ in range(warmup):
         spin.spin_sparse_attention(*args)
     torch.cuda.synchronize()
@@ -851,8 +860,6 @@ def main():
     wl = WORKLOADS[a.workload]
     device = "cuda:0"
     torch.cuda.set_device(0)
-    global QUANTIZE_ON_SIDE
-    QUANTIZE_ON_SIDE = not a.quantize_on_main
     if a.fidelity:
         _fidelity(a.fidelity, wl, device, [int(x) for x in a.fid_targets.split(",")])
         return
@@ -870,8 +877,8 @@ def main():
         _copy_calibration(device)
     both = _run_gpu(wl, keeps, a.steps, a.warmup, device, max(1, a.pools))
     res = {k: v["detailed"] for k, v in both.items()}    # per-stage times
-    lean = both[keep_main]["lean"]                       # library round: latency, step, wall
-    ser = both[keep_main]["serial"]                      # the update behind the top-k
+    lean = both[keep_main]["lean"]                       # the round: latency, step, wall
+    beh = both[keep_main]["behind"]                      # the update behind the top-k
 
     main_r = res[keep_main]
     per = main_r["per_us"]
@@ -927,7 +934,7 @@ def main():
         "indexer_roofline_tokens_per_s": HBM_PEAK_GBS * 1e9 / (
             IDX_BYTES_PER_PAGE / 64 + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW / 64),
         "per_step_us": {
-            # lean pass: the library's round, the update beside the top-k
+            # lean pass: the update beside the top-k
             "predict_index_topk_median": round(_median(pit), 2),
             "predict_index_topk_p10": round(_pct(pit, 10), 2),
             "predict_index_topk_p90": round(_pct(pit, 90), 2),
@@ -935,13 +942,16 @@ def main():
             "update_median": round(_median(per["update"]), 2),
             **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items()
                if n not in ("step", "to_topk")},
-            "quantize_overlaps_predict": QUANTIZE_ON_SIDE,
-            "tail": "spin_topk_update: top-k on the main stream, EMA update beside it behind "
-                    "the library's gate",
-            # the same round with the update behind the top-k on one stream
-            "serial_pass": {
-                "ms_per_step": round(ser["wall_s"] * 1e3 / a.steps, 4),
-                "whole_step_median": round(_median(ser["per_us"]["step"]), 2),
+            "schedule": "two streams taking turns: predict, indexer and top-k on one, the "
+                        "EMA update beside the top-k on the other behind the library's gate "
+                        "(spin_topk_update); the next round's chain follows the update on its "
+                        "stream; the next round's positions and query quantisation written "
+                        "ahead, after the top-k, beside the update",
+            # the same rounds with the update behind the top-k on one stream
+            "behind_pass": {
+                "ms_per_step": round(beh["wall_s"] * 1e3 / a.steps, 4),
+                "whole_step_median": round(_median(beh["per_us"]["step"]), 2),
+                "predict_index_topk_median": round(_median(beh["per_us"]["to_topk"]), 2),
             },
             # every stage bracketed by events (8 per round): the stage means,
             # the sweep's indexer times and the roofline

@@ -26,10 +26,12 @@
  *     caller owns every buffer, including the state buffer.
  *   - A state is used from one stream at a time: calls that overlap on one
  *     state race on its workspace.  The exceptions, which touch disjoint
- *     state regions: spin_quantize_q (q8, wq, qexp) may run beside
- *     spin_predict_blocks (V, D, VB, step, bscore, ukey) once both are
- *     ordered after the previous round's update, and spin_topk_scores (no
- *     state) may run beside spin_update / spin_mtp_replay.
+ *     state regions: spin_quantize_q (writes q8, wq, qexp; ordered after the
+ *     previous round's indexer, which reads them) may run beside
+ *     spin_predict_blocks (V, D, VB, step, bscore, ukey) and beside the
+ *     previous round's EMA update (spin_update, spin_mtp_replay or the update
+ *     half of spin_topk_update: V, D, VB, step, tail_gate); spin_topk_scores
+ *     (no state) may run beside spin_update / spin_mtp_replay.
  *   - Return value: SPIN_OK (0) or a negative SPIN_E* code; no C++ exception
  *     crosses this boundary.  Arguments that live in host memory are checked
  *     before anything is enqueued.  Values that live in device arrays (slot,

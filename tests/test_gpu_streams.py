@@ -1,7 +1,8 @@
-"""The benchmark's round (quantiser beside the predictor on a second stream,
-the library's spin_topk_update tail with the EMA update beside the top-k on
-that stream, behind the library's gate) against the same calls issued one
-after another on one stream: every output and the whole state must be
+"""The benchmark's two round schedules (the EMA update beside the top-k on a
+second stream behind the library's gate, the streams taking turns from round
+to round; or the update behind the top-k on one stream; in both, positions
+and quantised queries written ahead on the other stream) against the same
+calls issued one after another on one stream: every output and the whole state must be
 bit-identical, round after round, with a host synchronisation after every
 round and without any (the rounds' outputs then copied on the stream).  A
 missing dependency between the streams or between rounds would show up here
@@ -68,33 +69,44 @@ def test_benchmark_round_equals_serial(gpu_lib):
     wl = dataclasses.replace(WORKLOADS["ctx94k-b8"], steps=6)
     qp = np_(positions(wl))
     runs = {}
-    for mode in ("serial", "bench-synced", "bench-unsynced"):
+    modes = ("serial", "beside-synced", "beside-unsynced", "behind-synced", "behind-unsynced")
+    for mode in modes:
         print("[case] stream plan", mode, flush=True)
         spin_, pool, cfg, st, bufs, _ = bench._setup(wl, DEV)
-        side = torch.cuda.Stream(device=DEV)
+        streams = (torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV))
         qs = [make_queries(wl, pool, 0, t, qp[t].tolist(), device=DEV) for t in range(wl.steps)]
         qpos = [torch.as_tensor(qp[t].astype(np.int32), device=DEV) for t in range(wl.steps)]
         torch.cuda.synchronize()
-        done = None
         snaps = []
+        prev = None
+        tail = mode.split("-")[0]
         for t in range(wl.steps):
             keep = 10000 if t == 0 else 5000
-            bufs["qpos"].copy_(qpos[t])
             if mode == "serial":
+                bufs["qpos"].copy_(qpos[t])
                 _serial_round(st, bufs, pool, qs[t][0], qs[t][1], keep)
             else:
-                done = bench._round(spin, st, bufs, pool, qs[t][0], qs[t][1], keep, side, done)
-            if mode == "bench-unsynced":
-                snaps.append(_snapshot_dev(st, bufs))     # on the stream, no host wait
+                prev = bench._round(spin, st, bufs, pool, qpos[t], qs[t][0], qs[t][1], keep,
+                                    streams, t, prev, tail=tail)
+            if mode.endswith("unsynced"):
+                # on the stream the next round's predictor runs on, once the
+                # round's top-k and update are both done
+                main = streams[t % 2] if tail == "beside" else streams[0]
+                nxt = streams[(t + 1) % 2] if tail == "beside" else streams[0]
+                done = torch.cuda.Event()
+                done.record(main)
+                nxt.wait_event(done)
+                with torch.cuda.stream(nxt):
+                    snaps.append(_snapshot_dev(st, bufs))
             else:
                 torch.cuda.synchronize()
                 snaps.append(_host(_snapshot_dev(st, bufs)))
         torch.cuda.synchronize()
-        if mode == "bench-unsynced":
+        if mode.endswith("unsynced"):
             snaps = [_host(d) for d in snaps]
         assert st.error() == 0
         runs[mode] = snaps
-    for mode in ("bench-synced", "bench-unsynced"):
+    for mode in modes[1:]:
         for t, (a, b) in enumerate(zip(runs["serial"], runs[mode])):
             _same(a, b, (mode, t))
 
