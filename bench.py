@@ -111,96 +111,84 @@ def _setup(wl, device):
     st = spin.SpinState(cfg, device=device)
     slot = torch.arange(B, dtype=torch.int32, device=device)
     spin.spin_reset_slots(st.handle, slot, torch.arange(B, dtype=torch.int64, device=device) + 1000)
-    # two position buffers (and batches over them): round t writes buffer
-    # t % 2 while round t - 1's update may still read the other
-    qpos_ring = [torch.zeros(B, dtype=torch.int32, device=device) for _ in range(2)]
-    batches = [spin.make_batch(slot, qp, wl.rows, nb) for qp in qpos_ring]
-    bufs = dict(
-        slot=slot, qpos=qpos_ring[0], batch=batches[0], qpos_ring=qpos_ring, batches=batches,
-        kept=torch.zeros(B, nb, dtype=torch.int32, device=device),
-        cnt=torch.zeros(B, dtype=torch.int32, device=device),
-        flags=torch.zeros(B, nb, dtype=torch.uint8, device=device),
-        scores=torch.empty(B, wl.rows, nb * 64, dtype=torch.float32, device=device),
-        topk=torch.empty(B, wl.rows, wl.topk, dtype=torch.int32, device=device),
-    )
-    bufs["pq"] = torch.empty(B, wl.rows, nb, 4, dtype=torch.float32, device=device)
+    qpos = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def outputs():
+        return dict(kept=torch.zeros(B, nb, dtype=torch.int32, device=device),
+                    cnt=torch.zeros(B, dtype=torch.int32, device=device),
+                    flags=torch.zeros(B, nb, dtype=torch.uint8, device=device),
+                    scores=torch.empty(B, wl.rows, nb * 64, dtype=torch.float32, device=device),
+                    pq=torch.empty(B, wl.rows, nb, 4, dtype=torch.float32, device=device),
+                    topk=torch.empty(B, wl.rows, wl.topk, dtype=torch.int32, device=device))
+
+    # two sets of round outputs: round t writes set t % 2 while round t - 1's
+    # top-k and update may still read the other (set 0 also under the plain keys)
+    sets = [outputs(), outputs()]
+    bufs = dict(slot=slot, qpos=qpos, batch=spin.make_batch(slot, qpos, wl.rows, nb), sets=sets,
+                **sets[0])
     bufs["topk_ws"] = torch.empty(max(256, spin.spin_topk_workspace_bytes(bufs["batch"], wl.topk)),
                                   dtype=torch.uint8, device=device)
     return spin, pool, cfg, st, bufs, make_queries
 
 
-def _round(spin, st, bufs, pool, qpos, q, w, keep_bp, streams, t, prev=None, ev=None,
-           accepted=None, tail="beside"):
-    """Round t of a run, enqueued without host waits.
+def _round(spin, st, bufs, pool, batch, q, w, keep_bp, streams, t, ev=None, accepted=None,
+           tail="beside", start=True):
+    """Round t of a run, enqueued without host waits; returns its output set.
 
-    Both schedules keep the round's critical chain (predict -> indexer ->
-    top-k -> EMA update -> next predict) free of waits between streams, and
-    write the next round's inputs ahead on the other stream: the query
-    positions go into buffer t % 2 (round t - 2's, long done) and the query
-    quantisation follows, beside the previous round's top-k and update, which
-    touch neither.  The round's main stream waits for them before the
-    predictor.
-    tail="behind": the chain runs on streams[0]: the top-k, then the update
-    (spin_topk_scores, then spin_update or spin_mtp_replay).  The inputs go on
-    streams[1] once the previous round's indexer (the last reader of the
-    quantised queries) is done.
-    tail="beside": the streams take turns.  Round t's chain up to the top-k
-    runs on streams[t % 2]; its update runs on the other stream beside the
-    top-k, behind the library's gate (spin_topk_update: it opens once every
-    top-k workgroup has started); round t + 1 runs on the stream of round t's
-    update.  The inputs go on the stream of round t - 1's top-k, after it.
-    `qpos`: int32 [B] device positions of round t; `prev`: what the previous
-    call returned (None for the first round); `ev` = 8 timing events (0-4 on
-    main around the predictor, the indexer and the top-k; 5-6 around the
-    quantiser; 7 at the update's end), or None; `accepted` (int32 [B],
+    The round's chain (quantise, predict, indexer, top-k, EMA update, then the
+    next round's chain) runs without a wait between streams: a wait, like any
+    event, is a packet between two kernels, and costs the chain several µs
+    where consecutive kernels follow each other directly.  Round t writes
+    output set t % 2 (kept list, counts, flags, scores, quarter maxima,
+    top-k), so it needs nothing from round t - 1 but the state, and reads its
+    positions through its own `batch` (a spin_batch over that round's row of
+    positions, written before the run).
+    tail="beside": the two streams take turns.  Round t's chain up to the
+    top-k runs on streams[t % 2]; its update runs on the other stream beside
+    the top-k, behind the library's gate (spin_topk_update: it opens once
+    every top-k workgroup has started), and round t + 1's chain follows that
+    update on its stream.
+    tail="behind": everything on streams[0], the update after the top-k.
+    `ev` = 8 timing events (0 at the start, 5-6 around the quantiser, 1 after
+    the predictor, 2-3 around the indexer, 4 after the top-k, 7 after the
+    update), or None; `start` = False leaves event 0 to the caller (the
+    previous round's event 7 marks the same point).  `accepted` (int32 [B],
     device): MTP acceptances, whose prefix-valid replay replaces the
-    single-row update.  Returns (the batch used, the event after the indexer).
+    single-row update.
     """
-    import torch
-
-    b = bufs
     beside = tail == "beside"
     main = streams[t % 2] if beside else streams[0]
-    side = streams[(t + 1) % 2] if beside else streams[1]
+    side = streams[(t + 1) % 2] if beside else main
     ev = ev or [None] * 8
     rec = lambda e, s: e.record(s) if e is not None else None
-    batch = b["batches"][t % 2]
-    if prev is not None:
-        side.wait_event(prev[1])            # (beside: already in order on this stream)
-    with torch.cuda.stream(side):
-        b["qpos_ring"][t % 2].copy_(qpos)
-    rec(ev[5], side)
-    spin.spin_quantize_q(st.handle, batch, q, w, stream=side)
-    rec(ev[6], side)
-    ahead = torch.cuda.Event()
-    ahead.record(side)
-    main.wait_event(ahead)
-    rec(ev[0], main)
-    spin.spin_predict_blocks(st.handle, 0, batch, keep_bp, b["kept"], b["cnt"], b["flags"],
+    o = bufs["sets"][t % 2]
+    if start:
+        rec(ev[0], main)
+    rec(ev[5], main)
+    spin.spin_quantize_q(st.handle, batch, q, w, stream=main)
+    rec(ev[6], main)
+    spin.spin_predict_blocks(st.handle, 0, batch, keep_bp, o["kept"], o["cnt"], o["flags"],
                              stream=main)
     rec(ev[1], main)
     rec(ev[2], main)
     spin.spin_indexer_scores(st.handle, batch, pool.key_codes, pool.key_scale, pool.block_table,
-                             b["kept"], b["cnt"], b["scores"], b["pq"], stream=main)
+                             o["kept"], o["cnt"], o["scores"], o["pq"], stream=main)
     rec(ev[3], main)
-    indexed = torch.cuda.Event()
-    indexed.record(main)
     if beside:
-        spin.spin_topk_update(st.handle, 0, batch, b["scores"], b["pq"], b["kept"], b["cnt"],
-                              b["topk"], accepted, stream=main, update_stream=side)
+        spin.spin_topk_update(st.handle, 0, batch, o["scores"], o["pq"], o["kept"], o["cnt"],
+                              o["topk"], accepted, stream=main, update_stream=side)
         rec(ev[4], main)
-        rec(ev[7], side)
     else:
-        spin.spin_topk_scores(batch, st.cfg.topk, b["scores"], b["kept"], b["cnt"], b["topk"],
-                              None, b["pq"], stream=main)
+        spin.spin_topk_scores(batch, st.cfg.topk, o["scores"], o["kept"], o["cnt"], o["topk"],
+                              None, o["pq"], stream=main)
         rec(ev[4], main)
         if accepted is None:
-            spin.spin_update(st.handle, 0, batch, b["scores"], b["kept"], b["cnt"], stream=main)
+            spin.spin_update(st.handle, 0, batch, o["scores"], o["kept"], o["cnt"], stream=main)
         else:
-            spin.spin_mtp_replay(st.handle, 0, batch, accepted, b["scores"], b["kept"], b["cnt"],
+            spin.spin_mtp_replay(st.handle, 0, batch, accepted, o["scores"], o["kept"], o["cnt"],
                                  stream=main)
-        rec(ev[7], main)
-    return batch, indexed
+    rec(ev[7], side)
+    return o
 
 
 # timing passes: (name, tail, events recorded per round)
@@ -211,13 +199,16 @@ PASSES = (("lean", "beside", (0, 4, 7)), ("behind", "behind", (0, 4, 7)),
 def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
     """Per keep and per timing pass of PASSES, `warmup` untimed rounds then
     `steps` timed rounds, all from the same state reset and inputs:
-      lean      the round with the update beside the top-k on the other
-                stream, behind the library's gate, 3 events per round (its
-                start, the top-k's end, the update's end): value,
-                ms_per_step, the predict + index + top-k latency and the
-                whole step.
-      behind    the round with the update behind the top-k on one stream
-                (3 events): the same figures without the overlap.
+      lean      the round with the update beside the top-k on a second
+                stream, behind the library's gate, the streams taking turns,
+                3 events per round (its start, the top-k's end, the update's
+                end): value, ms_per_step, the predict + index + top-k latency
+                and the whole step.
+      behind    the round on one stream, the update behind the top-k (3
+                events): the same figures without the overlap.
+    Before the first timed pass, untimed cycles of the run's rounds in the
+    lean schedule (at least 100 ms of them) settle the part: the first pass
+    after the inputs are drawn ran 1-10% slower than the same pass repeated.
       detailed  the lean round with events around every stage (8 per round):
                 the stage times, the sweep's indexer times and the roofline.
     Returns {keep: {pass name: {...}}}."""
@@ -242,57 +233,69 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
         acc_all = acc[:T].to(torch.int32).to(device)
     qs = [make_queries(wl, pools[t % n_pools], 0, t, qpos_all[t].tolist(), device=device)
           for t in range(T)]
-    qpos_all = qpos_all.to(torch.int32).to(device)
+    qpos_all = qpos_all.to(torch.int32).to(device).contiguous()
+    # one batch per round, over that round's row of positions
+    batches = [spin.make_batch(bufs["slot"], qpos_all[t], wl.rows, wl.blocks) for t in range(T)]
     torch.cuda.synchronize()
     results = {}
     streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device))  # default priority
     acc_of = (lambda t: acc_all[t]) if acc_all is not None else (lambda t: None)
+    spin.spin_reset_slots(st.handle, bufs["slot"],
+                          torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
+    torch.cuda.synchronize()
+    # untimed: settles the part before the first pass (cycles of the run's
+    # rounds for at least 100 ms)
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.1:
+        for t in range(T):
+            _round(spin, st, bufs, pools[t % n_pools], batches[t], qs[t][0], qs[t][1],
+                   keep_bps[0], streams, t, accepted=acc_of(t), tail=PASSES[0][1])
+        torch.cuda.synchronize()
     for keep_bp in keep_bps:
         results[keep_bp] = {}
         for name, tail, recorded in PASSES:
             spin.spin_reset_slots(st.handle, bufs["slot"],
                                   torch.arange(wl.batch, dtype=torch.int64, device=device) + 1000)
             torch.cuda.synchronize()
-            prev = None
             for t in range(warmup):
-                prev = _round(spin, st, bufs, pools[t % n_pools], qpos_all[t], qs[t][0],
-                              qs[t][1], keep_bp, streams, t, prev, accepted=acc_of(t), tail=tail)
+                _round(spin, st, bufs, pools[t % n_pools], batches[t], qs[t][0], qs[t][1], keep_bp,
+                       streams, t, accepted=acc_of(t), tail=tail)
             torch.cuda.synchronize()
             evs = []
-            for _ in range(steps):
+            for i in range(steps):
                 e = [None] * 8
                 for k in recorded:
                     e[k] = torch.cuda.Event(enable_timing=True)
+                if i > 0:
+                    e[0] = evs[-1][7]     # the previous update's end starts this round
                 evs.append(e)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            prev = None
-            for t in range(steps):
-                q, w = qs[warmup + t]
-                prev = _round(spin, st, bufs, pools[(warmup + t) % n_pools], qpos_all[warmup + t],
-                              q, w, keep_bp, streams, warmup + t, prev, evs[t],
-                              accepted=acc_of(warmup + t), tail=tail)
+            for i in range(steps):
+                t = warmup + i
+                q, w = qs[t]
+                last = _round(spin, st, bufs, pools[t % n_pools], batches[t], q, w, keep_bp,
+                              streams, t, evs[i], accepted=acc_of(t), tail=tail, start=i == 0)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
             per = {"step": [e[0].elapsed_time(e[7]) * 1e3 for e in evs]}      # us
             if 4 in recorded:
-                # critical path to the top-k: predict, the wait for the quantiser, indexer, top-k
+                # critical path to the top-k: quantise, predict, indexer, top-k
                 per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
             if 4 in recorded:
                 # a round ends when both the top-k and the update are done
                 per["step"] = [max(e[0].elapsed_time(e[4]), e[0].elapsed_time(e[7])) * 1e3
                                for e in evs]
             if name == "detailed":
-                per["predict"] = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-                per["quantize"] = [e[5].elapsed_time(e[6]) * 1e3 for e in evs]  # ahead, on the side stream
+                per["quantize"] = [e[5].elapsed_time(e[6]) * 1e3 for e in evs]
+                per["predict"] = [e[6].elapsed_time(e[1]) * 1e3 for e in evs]
                 per["indexer"] = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
                 per["topk"] = [e[3].elapsed_time(e[4]) * 1e3 for e in evs]
                 # the update: from the top-k's end (behind it) or the indexer's
                 # end (beside it) to its own
                 u0 = 4 if tail == "behind" else 3
                 per["update"] = [e[u0].elapsed_time(e[7]) * 1e3 for e in evs]
-            cnt = bufs["cnt"].cpu()
-            kept_pages = int(cnt.sum())
+            kept_pages = int(last["cnt"].sum().item())
             if st.error() != 0:
                 raise RuntimeError(f"device error word {st.error()}")
             results[keep_bp][name] = dict(wall_s=wall, per_us=per, kept_pages=kept_pages,
@@ -747,16 +750,13 @@ def _attention_bench(wl, device, steps, warmup, keep_bp):
     from workload import positions
 
     streams = (torch.cuda.Stream(device=device), torch.cuda.Stream(device=device))
-    qp = positions(wl)
-    rounds = []
-    for t, keep in enumerate((10000, keep_bp)):
-        q, w = make_queries(wl, pool, 0, t, qp[t].tolist(), device=device)
-        rounds.append((qp[t].to(device=device, dtype=torch.int32), q, w, keep))
+    qp = positions(wl)[:2].to(device=device, dtype=torch.int32).contiguous()
+    batches = [spin.make_batch(bufs["slot"], qp[t], wl.rows, wl.blocks) for t in range(2)]
+    qws = [make_queries(wl, pool, 0, t, qp[t].tolist(), device=device) for t in range(2)]
     torch.cuda.synchronize()
-    prev = None
-    for t, (qpos, q, w, keep) in enumerate(rounds):
-        prev = _round(spin, st, bufs, pool, qpos, q, w, keep, streams, t, prev)
-    batch = prev[0]
+    for t, keep in enumerate((10000, keep_bp)):
+        out = _round(spin, st, bufs, pool, batches[t], qws[t][0], qws[t][1], keep, streams, t)
+    batch, topk = batches[1], out["topk"]
     torch.cuda.synchronize()
     H, D, DV = 128, 576, 512
     g = torch.Generator(device=device)
@@ -771,7 +771,7 @@ def _attention_bench(wl, device, steps, warmup, keep_bp):
     out = torch.empty(wl.batch, wl.rows, H, DV, dtype=torch.bfloat16, device=device)
     lse = torch.empty(wl.batch, wl.rows, H, device=device)
     scale = 1.0 / 192 ** 0.5
-    args = (batch, wl.topk, bufs["topk"], qa, kv, pool.block_table, scale, out, lse, ws)
+    args = (batch, wl.topk, topk, qa, kv, pool.block_table, scale, out, lse, ws)
     for _ in range(warmup):
         spin.spin_sparse_attention(*args)
     torch.cuda.synchronize()
@@ -782,7 +782,7 @@ def _attention_bench(wl, device, steps, warmup, keep_bp):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    tok = int((bufs["topk"] >= 0).sum())
+    tok = int((topk >= 0).sum())
     rows = wl.batch * wl.rows
     byts = tok * D * 2 + rows * (H * D * 2 + H * DV * 2 + H * 4 + wl.topk * 4)
     flops = 2 * H * tok * (D + DV)
@@ -942,12 +942,12 @@ def main():
             "update_median": round(_median(per["update"]), 2),
             **{f"{n}_mean": round(sum(v) / len(v), 2) for n, v in per.items()
                if n not in ("step", "to_topk")},
-            "schedule": "two streams taking turns: predict, indexer and top-k on one, the "
-                        "EMA update beside the top-k on the other behind the library's gate "
-                        "(spin_topk_update); the next round's chain follows the update on its "
-                        "stream; the next round's positions and query quantisation written "
-                        "ahead, after the top-k, beside the update",
-            # the same rounds with the update behind the top-k on one stream
+            "schedule": "two streams taking turns: quantise, predict, indexer and top-k on "
+                        "one, the EMA update beside the top-k on the other behind the library's "
+                        "gate (spin_topk_update), the next round's chain after that update on "
+                        "its stream; two sets of round outputs, so that no round waits on "
+                        "another stream",
+            # the same rounds on one stream, the update behind the top-k
             "behind_pass": {
                 "ms_per_step": round(beh["wall_s"] * 1e3 / a.steps, 4),
                 "whole_step_median": round(_median(beh["per_us"]["step"]), 2),

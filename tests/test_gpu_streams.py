@@ -1,8 +1,8 @@
 """The benchmark's two round schedules (the EMA update beside the top-k on a
 second stream behind the library's gate, the streams taking turns from round
-to round; or the update behind the top-k on one stream; in both, positions
-and quantised queries written ahead on the other stream) against the same
-calls issued one after another on one stream: every output and the whole state must be
+to round; or the update behind the top-k on one stream; in both, two sets of
+round outputs and one position row per round) against the same calls issued
+one after another on one stream: every output and the whole state must be
 bit-identical, round after round, with a host synchronisation after every
 round and without any (the rounds' outputs then copied on the stream).  A
 missing dependency between the streams or between rounds would show up here
@@ -57,7 +57,9 @@ def _masked_scores(s, cnt):
 
 def _same(a, b, t):
     assert np.array_equal(a["cnt"], b["cnt"]), t
-    for k in ("kept", "flags", "topk", "V", "D", "VB", "step"):
+    for bi, c in enumerate(a["cnt"]):          # entries past the count are not written
+        assert np.array_equal(a["kept"][bi, : int(c)], b["kept"][bi, : int(c)]), (t, "kept", bi)
+    for k in ("flags", "topk", "V", "D", "VB", "step"):
         assert np.array_equal(a[k], b[k]), (t, k)
     assert np.array_equal(_masked_scores(a["scores"], a["cnt"]),
                           _masked_scores(b["scores"], b["cnt"])), (t, "scores")
@@ -75,21 +77,23 @@ def test_benchmark_round_equals_serial(gpu_lib):
         spin_, pool, cfg, st, bufs, _ = bench._setup(wl, DEV)
         streams = (torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV))
         qs = [make_queries(wl, pool, 0, t, qp[t].tolist(), device=DEV) for t in range(wl.steps)]
-        qpos = [torch.as_tensor(qp[t].astype(np.int32), device=DEV) for t in range(wl.steps)]
+        qpos = torch.as_tensor(qp.astype(np.int32), device=DEV).contiguous()
+        batches = [spin.make_batch(bufs["slot"], qpos[t], wl.rows, wl.blocks)
+                   for t in range(wl.steps)]
         torch.cuda.synchronize()
         snaps = []
-        prev = None
         tail = mode.split("-")[0]
         for t in range(wl.steps):
             keep = 10000 if t == 0 else 5000
             if mode == "serial":
                 bufs["qpos"].copy_(qpos[t])
                 _serial_round(st, bufs, pool, qs[t][0], qs[t][1], keep)
+                out = bufs
             else:
-                prev = bench._round(spin, st, bufs, pool, qpos[t], qs[t][0], qs[t][1], keep,
-                                    streams, t, prev, tail=tail)
+                out = bench._round(spin, st, bufs, pool, batches[t], qs[t][0], qs[t][1], keep,
+                                   streams, t, tail=tail)
             if mode.endswith("unsynced"):
-                # on the stream the next round's predictor runs on, once the
+                # on the stream the next round's chain runs on, once the
                 # round's top-k and update are both done
                 main = streams[t % 2] if tail == "beside" else streams[0]
                 nxt = streams[(t + 1) % 2] if tail == "beside" else streams[0]
@@ -97,10 +101,10 @@ def test_benchmark_round_equals_serial(gpu_lib):
                 done.record(main)
                 nxt.wait_event(done)
                 with torch.cuda.stream(nxt):
-                    snaps.append(_snapshot_dev(st, bufs))
+                    snaps.append(_snapshot_dev(st, out))
             else:
                 torch.cuda.synchronize()
-                snaps.append(_host(_snapshot_dev(st, bufs)))
+                snaps.append(_host(_snapshot_dev(st, out)))
         torch.cuda.synchronize()
         if mode.endswith("unsynced"):
             snaps = [_host(d) for d in snaps]
