@@ -192,25 +192,28 @@ def _round(spin, st, bufs, pool, batch, q, w, keep_bp, streams, t, ev=None, acce
 
 
 # timing passes: (name, tail, events recorded per round)
-PASSES = (("lean", "beside", (0, 4, 7)), ("behind", "behind", (0, 4, 7)),
-          ("detailed", "beside", tuple(range(8))))
+PASSES = (("plain", "beside", ()), ("lean", "beside", (0, 4, 7)),
+          ("behind", "behind", (0, 4, 7)), ("detailed", "beside", tuple(range(8))))
 
 
 def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
     """Per keep and per timing pass of PASSES, `warmup` untimed rounds then
     `steps` timed rounds, all from the same state reset and inputs:
-      lean      the round with the update beside the top-k on a second
+      plain     the round with the update beside the top-k on a second
                 stream, behind the library's gate, the streams taking turns,
-                3 events per round (its start, the top-k's end, the update's
-                end): value, ms_per_step, the predict + index + top-k latency
-                and the whole step.
+                with no event inside the timed rounds (an event between two
+                kernels delays the second): value and ms_per_step, from the
+                wall clock.
+      lean      the same round with 3 events per round (its start, the
+                top-k's end, the update's end): the predict + index + top-k
+                latency and the whole step.
       behind    the round on one stream, the update behind the top-k (3
                 events): the same figures without the overlap.
+      detailed  the lean round with events around every stage (8 per round):
+                the stage times, the sweep's indexer times and the roofline.
     Before the first timed pass, untimed cycles of the run's rounds in the
     lean schedule (at least 100 ms of them) settle the part: the first pass
     after the inputs are drawn ran 1-10% slower than the same pass repeated.
-      detailed  the lean round with events around every stage (8 per round):
-                the stage times, the sweep's indexer times and the roofline.
     Returns {keep: {pass name: {...}}}."""
     import torch
 
@@ -266,7 +269,7 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
                 e = [None] * 8
                 for k in recorded:
                     e[k] = torch.cuda.Event(enable_timing=True)
-                if i > 0:
+                if i > 0 and recorded:
                     e[0] = evs[-1][7]     # the previous update's end starts this round
                 evs.append(e)
             torch.cuda.synchronize()
@@ -278,7 +281,7 @@ def _run_gpu(wl, keep_bps, steps, warmup, device, n_pools=1):
                               streams, t, evs[i], accepted=acc_of(t), tail=tail, start=i == 0)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
-            per = {"step": [e[0].elapsed_time(e[7]) * 1e3 for e in evs]}      # us
+            per = {"step": [e[0].elapsed_time(e[7]) * 1e3 for e in evs]} if recorded else {}
             if 4 in recorded:
                 # critical path to the top-k: quantise, predict, indexer, top-k
                 per["to_topk"] = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
@@ -877,15 +880,16 @@ def main():
         _copy_calibration(device)
     both = _run_gpu(wl, keeps, a.steps, a.warmup, device, max(1, a.pools))
     res = {k: v["detailed"] for k, v in both.items()}    # per-stage times
-    lean = both[keep_main]["lean"]                       # the round: latency, step, wall
+    plain = both[keep_main]["plain"]                     # the round: wall clock only
+    lean = both[keep_main]["lean"]                       # the round: latency, step
     beh = both[keep_main]["behind"]                      # the update behind the top-k
 
     main_r = res[keep_main]
     per = main_r["per_us"]
     step_us = lean["per_us"]["step"]
     pit = lean["per_us"]["to_topk"]
-    ms_per_step = lean["wall_s"] * 1e3 / a.steps
-    tokens_per_step = lean["kept_pages"] * 64
+    ms_per_step = plain["wall_s"] * 1e3 / a.steps
+    tokens_per_step = plain["kept_pages"] * 64
     value = tokens_per_step / (ms_per_step / 1e3)
     idx_us = sum(per["indexer"]) / a.steps
     idx_flops = main_r["kept_pages"] * 64 * wl.rows * wl.heads * wl.head_dim * 2
@@ -934,7 +938,8 @@ def main():
         "indexer_roofline_tokens_per_s": HBM_PEAK_GBS * 1e9 / (
             IDX_BYTES_PER_PAGE / 64 + wl.rows * IDX_SCORE_BYTES_PER_PAGE_ROW / 64),
         "per_step_us": {
-            # lean pass: the update beside the top-k
+            # lean pass: the update beside the top-k, 3 events per round
+            "lean_pass_ms_per_step": round(lean["wall_s"] * 1e3 / a.steps, 4),
             "predict_index_topk_median": round(_median(pit), 2),
             "predict_index_topk_p10": round(_pct(pit, 10), 2),
             "predict_index_topk_p90": round(_pct(pit, 90), 2),
