@@ -313,3 +313,84 @@ def test_mtp_union_and_replay_rounds(gpu_lib):
 def test_mtp_union_and_replay_lockstep(gpu_lib):
     n, ties = _mtp_rounds(lockstep=True)
     assert n == 36 and ties == 0
+
+
+# ------------------------------------------------------ start of a sequence
+@pytest.mark.parametrize("R", [1, 4])
+def test_sequence_start_lockstep(gpu_lib, R):
+    """The first positions of a sequence, in lockstep with the oracle: a
+    one-slot context, a first block with one slot left, a full first block,
+    the first two-block context (the first real selection), and with four
+    rows, rows that cross the first block boundary.  Every round runs the
+    whole path (quantise, predict, indexer, top-k with fewer valid slots than
+    K, update or prefix-valid replay)."""
+    base = WORKLOADS["ctx9k-b1"] if R == 1 else WORKLOADS["mtp-ctx256k-b32"]
+    starts = [0, 1, 62, 63, 64, 126] if R == 1 else [0, 1, 58, 60, 61, 62]
+    steps = 5
+    wl = dataclasses.replace(base, batch=len(starts), ctx=64 * 4, layers=1, steps=steps,
+                             heavy=(4,))
+    acc = (np.random.default_rng(3).integers(0, R, size=(steps, wl.batch))
+           if R > 1 else np.zeros((steps, wl.batch), dtype=np.int64))
+    qp = np.zeros((steps, wl.batch), dtype=np.int64)
+    qp[0] = starts
+    for t in range(1, steps):
+        qp[t] = qp[t - 1] + acc[t - 1] + 1
+    assert int((qp[-1] + R - 1).max()) < wl.ctx
+    cfg = spin.make_config(1, wl.batch, wl.ctx, wl.topk, max_rows=R, explore_bp=wl.explore_bp,
+                           alpha=wl.alpha)
+    rig = Rig(cfg, wl.batch, R, wl.blocks)
+    rids = [700 + b for b in range(wl.batch)]
+    rig.reset(rids)
+    pool = make_pool(wl, 0, device=DEV)
+    kv = O.e4m3fn_decode(np_(pool.key_codes))
+    scv = np_(pool.key_scale).astype(np.float64)
+    tables = np_(pool.block_table)
+    osts = [O.RequestState(wl.ctx, request_id=rids[b]) for b in range(wl.batch)]
+    keep = [10000, 5000, 3000, 6000, 5000]
+    for t in range(steps):
+        _say("sequence start R", R, "round", t, "positions", qp[t].tolist())
+        rig.set_qpos(qp[t])
+        if t > 0:
+            for b in range(wl.batch):
+                sync_from_oracle(rig, 0, b, osts[b], lockstep=True)
+        qb, w = make_queries(wl, pool, 0, t, qp[t].tolist(), device=DEV)
+        spin.spin_predict_blocks(rig.h, 0, rig.batch, keep[t], rig.kept, rig.kept_count,
+                                 rig.flags)
+        spin.spin_indexer_topk(rig.h, rig.batch, qb, w, pool.key_codes, pool.key_scale,
+                               pool.block_table, rig.kept, rig.kept_count, rig.scores, rig.topk)
+        torch.cuda.synchronize()
+        g_scores, g_topk = np_(rig.scores), np_(rig.topk)
+        if R == 1:
+            spin.spin_update(rig.h, 0, rig.batch, rig.scores, rig.kept, rig.kept_count)
+        else:
+            spin.spin_mtp_replay(rig.h, 0, rig.batch,
+                                 torch.as_tensor(acc[t].astype(np.int32), device=DEV),
+                                 rig.scores, rig.kept, rig.kept_count)
+        torch.cuda.synchronize()
+        for b in range(wl.batch):
+            q = int(qp[t, b])
+            qv, wv, _, _ = oracle_fp8_operands(qb[b], w[b])
+            ref = O.decode_round(osts[b], q, R, keep[t], wl.explore_bp, cfg.seed, 0, qv, wv, kv,
+                                 scv, tables[b], wl.topk, wl.alpha, accepted=int(acc[t, b]))
+            gk = rig.kept_list(b)
+            assert np.array_equal(gk, ref["kept"]), f"t{t} b{b}: kept blocks"
+            assert np.array_equal(np_(rig.flags[b])[: len(ref["flags"])], ref["flags"]), \
+                f"t{t} b{b}: flags"
+            n = len(gk) * 64
+            mag = score_mag(qv, wv, kv, scv, tables[b], gk)
+            assert_scores_close(g_scores[b, :, :n], ref["scores"], mag, f"t{t} b{b}")
+            slots = (gk[:, None] * 64 + np.arange(64)).reshape(-1)
+            for r in range(R):
+                valid = int(np.sum(slots <= q + r))
+                assert valid < wl.topk                      # fewer valid slots than K
+                assert np.all(g_topk[b, r, valid:] == -1), f"t{t} b{b} r{r}: padding"
+                rs = dict(zip(slots.tolist(), ref["scores"][r].tolist()))
+                mg = dict(zip(slots.tolist(), mag[r].tolist()))
+                assert_topk_tie_aware(g_topk[b, r], ref["topk"][r], lambda x: rs[x],
+                                      lambda x: score_tol(rs[x], mg[x]), f"t{t} b{b} r{r}")
+            gV, gD, _, gstep = rig.read_state(0, b)
+            scale = float(np.max(mag))
+            _state_close(gV, osts[b].V, scale, f"V t{t} b{b}")
+            _state_close(gD, osts[b].D, scale, f"D t{t} b{b}")
+            assert gstep == osts[b].step
+    assert rig.state.error() == 0
