@@ -501,3 +501,80 @@ def test_device_errors_flagged_without_faults(gpu_lib):
     torch.cuda.synchronize()
     assert rig.state.error() & spin.ERR_QPOS
     assert int(rig.kept_count[1]) == 0
+
+
+def test_device_errors_indexer_update_replay(gpu_lib):
+    """Bad device-side values the host cannot check: a kept entry past
+    max_blocks, a block-table entry past the pool, a kept count past
+    max_blocks, an accepted count past the rows.  Each is flagged in the
+    state's error word; the offending page, entry or request is skipped (its
+    scores -inf, its state untouched) and everything else is computed as
+    usual.  Every kernel checks these values before it reads through them."""
+    rng = np.random.default_rng(21)
+    B, mb, pages = 2, 8, 16
+    codes, sc = _rand_pool(rng, pages)
+    table = np.stack([rng.permutation(pages)[:mb] for _ in range(B)]).astype(np.int32)
+    table[0, 2] = pages + 83                                    # past the pool
+    qpos = np.array([64 * mb - 1, 64 * mb - 1], dtype=np.int64)
+    cfg = spin.make_config(1, B, 64 * mb, 256, max_rows=2, alpha=0.9)
+    rig = Rig(cfg, B, 1, mb)
+    rig.reset([31, 32])
+    rig.set_qpos(qpos)
+    kt = np.full((B, mb), -1, dtype=np.int32)
+    kt[0, :4] = [0, 1, mb + 1, 2]                               # entry 2 past max_blocks
+    kt[1, :] = np.arange(mb)
+    rig.kept.copy_(torch.as_tensor(kt))
+    rig.kept_count.copy_(torch.as_tensor([4, 100], dtype=torch.int32))   # 100 > max_blocks
+    q = (torch.randn(B, 1, 64, 128) * 2).to(torch.bfloat16)
+    w = torch.rand(B, 1, 64) + 0.5
+    _say("indexer with bad kept entries, a page past the pool, a count past max_blocks")
+    spin.spin_quantize_q(rig.h, rig.batch, q.to(DEV), w.to(DEV))
+    spin.spin_indexer_scores(rig.h, rig.batch, codes.to(DEV), sc.to(DEV),
+                             torch.as_tensor(table).to(DEV), rig.kept, rig.kept_count, rig.scores)
+    torch.cuda.synchronize()
+    err = rig.state.error()
+    assert err & spin.ERR_KEPT and err & spin.ERR_PAGE
+    got = np_(rig.scores)
+    kv = O.e4m3fn_decode(np_(codes))
+    scv = np_(sc).astype(np.float64)
+    for b, good in ((0, [(0, 0), (1, 1)]), (1, [(i, i) for i in range(mb)])):
+        qv, wv, _, _ = oracle_fp8_operands(q[b], w[b])
+        for pos, j in good:
+            ref = O.indexer_scores(qv, wv, kv, scv, table[b], np.array([j]), int(qpos[b]))
+            mag = score_mag(qv, wv, kv, scv, table[b], np.array([j]))
+            assert_scores_close(got[b, :, 64 * pos: 64 * pos + 64], ref, mag, f"b{b} page {pos}")
+    assert np.all(got[0, 0, 128:256] == -np.inf)                 # the two skipped pages
+
+    # the update over the same lists: the bad entry is skipped and flagged,
+    # the clamped count covers every block of request 1
+    V0, D0 = [np_(x).copy() for x in (rig.state.V(), rig.state.D())]
+    s_fin = np.where(np.isfinite(got), got, 0.0).astype(np.float32)
+    rig.scores.copy_(torch.as_tensor(s_fin))
+    rig.kept_count.copy_(torch.as_tensor([4, mb], dtype=torch.int32))
+    _say("update with a bad kept entry")
+    spin.spin_update(rig.h, 0, rig.batch, rig.scores, rig.kept, rig.kept_count)
+    torch.cuda.synchronize()
+    V1 = np_(rig.state.V())
+    for j in (0, 1, 2):                                          # kept blocks observed
+        assert np.all(np.isfinite(V1[0, 0, 64 * j: 64 * j + 64]))
+    assert np.array_equal(V1[0, 0, 64 * 3: 64 * mb], V0[0, 0, 64 * 3: 64 * mb])   # untouched
+    assert int(rig.state.step()[0, 0]) == 1 and int(rig.state.step()[0, 1]) == 1
+
+    # a replay whose accepted count is past the rows: that request is skipped
+    cfg2 = spin.make_config(1, B, 64 * mb, 256, max_rows=2, alpha=0.9)
+    rig2 = Rig(cfg2, B, 2, mb)
+    rig2.reset([41, 42])
+    rig2.set_qpos([64 * 4, 64 * 4])
+    kt2 = np.tile(np.arange(mb, dtype=np.int32), (B, 1))
+    rig2.kept.copy_(torch.as_tensor(kt2))
+    rig2.kept_count.copy_(torch.as_tensor([5, 5], dtype=torch.int32))
+    rig2.scores.copy_(torch.as_tensor(rng.random((B, 2, mb * 64)).astype(np.float32)))
+    Vb = np_(rig2.state.V()).copy()
+    _say("replay with accepted past the rows")
+    spin.spin_mtp_replay(rig2.h, 0, rig2.batch, torch.tensor([1, 2], dtype=torch.int32, device=DEV),
+                         rig2.scores, rig2.kept, rig2.kept_count)
+    torch.cuda.synchronize()
+    assert rig2.state.error() & spin.ERR_ACCEPT
+    Va = np_(rig2.state.V())
+    assert np.array_equal(Va[0, 1], Vb[0, 1]) and int(rig2.state.step()[0, 1]) == 0
+    assert np.all(np.isfinite(Va[0, 0, : 64 * 4 + 2])) and int(rig2.state.step()[0, 0]) == 1
