@@ -1,5 +1,5 @@
 // EMA update from the observed slots, with prefix-valid MTP replay: the work
-// of one wave, shared by k_update and the top-k + update launch.
+// of one wave of k_update.
 //
 // A wave takes NB consecutive entries of the kept list.  With a accepted
 // drafts, rows 0..a are applied in row order; row r observes kept slots
@@ -12,7 +12,10 @@
 //      kept).  When block j - 1 is not kept, block j's owner also takes the
 //      offsets with i0 in 64j - a .. 64j - 1, whose later rows land in block j.
 //      Each offset therefore has exactly one writer and sees its rows in order.
-// All loads of a wave's blocks are issued before any is used.
+// Every load of a wave (V, D and each row's scores of all its blocks) is
+// issued before the first EMA step, so a replay over several rows costs one
+// memory latency, not one per row.  The single-row update (kReplay false) has
+// no row-1..3 loads.
 #pragma once
 
 #include "spin_device.h"
@@ -20,9 +23,11 @@
 
 namespace spin {
 
+constexpr int kMaxRows = 4;       // query rows a batch may carry (1 + draft length)
+
 // Request b's kept entries k0 .. k0 + NB - 1.  `lead` (one thread per request
 // and call) reports bad request arguments and advances the round counter.
-template <int NB>
+template <int NB, bool kReplay>
 __device__ __forceinline__ void update_wave(const SpinView& v, int layer, const spin_batch& bt,
                                             const int32_t* accepted, const float* scores,
                                             const int32_t* kept, const int32_t* kept_count,
@@ -37,7 +42,7 @@ __device__ __forceinline__ void update_wave(const SpinView& v, int layer, const 
     if (lead) flag_error(v.err, SPIN_ERR_QPOS);
     return;
   }
-  const int a = accepted ? accepted[b] : 0;
+  const int a = kReplay && accepted ? __builtin_amdgcn_readfirstlane(accepted[b]) : 0;
   if (a < 0 || a >= bt.R) {
     if (lead) flag_error(v.err, SPIN_ERR_ACCEPT);
     return;
@@ -71,19 +76,55 @@ __device__ __forceinline__ void update_wave(const SpinView& v, int layer, const 
   float* VB = v.VB + row * v.max_blocks;
   const size_t rstride = mb * kBlock;
   const float* sc = scores + size_t(b) * bt.R * rstride;
+  constexpr int RM = kReplay ? kMaxRows : 1;
 
   // Issue the loads of every block first.
-  float x[NB], y[NB], s0[NB];
-  bool okb[NB];
+  //   x, y      V_i and D_{q-i} of slot i = 64j + lane
+  //   sv[r]     row r's score of slot i (the V chain)
+  //   sd[r]     row r's score of slot i + r (the D chain of offset q - i), r >= 1
+  //   yb, sb[r] the offset q - i0 of i0 = 64j - 1 - lane in a block not kept
+  //             (lanes < a) and row r's score of slot i0 + r when in block j
+  // With replay rows every load is unconditional (one whose value is not
+  // needed reads element 0; a conditional load would make the join after it
+  // wait for every load in flight), and each value is used only under the
+  // condition it was loaded under.  The single-row update keeps conditional
+  // loads: measured in the round, its faster unconditional form left more of
+  // its written lines to reach HBM during the next round's indexer, which
+  // then took about as much longer as the update saved.
+  auto ld = [](const float* p, bool ok, size_t idx, float none) {
+    if (kReplay) return p[ok ? idx : 0];
+    return ok ? p[idx] : none;
+  };
+  float x[NB], y[NB], sv[NB][RM], sd[NB][RM], yb[NB], sb[NB][RM];
+  bool okb[NB], nxt[NB], prv[NB];
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
     const int j = jj[m + 1];
     const int k = k0 + m;
     okb[m] = k < cnt && j >= 0 && j < bt.max_blocks;
+    nxt[m] = jj[m + 2] == j + 1 && k + 1 < cnt;
+    prv[m] = jj[m] == j - 1 && k > 0;
     const int i = j * kBlock + l;
-    x[m] = (okb[m] && i < v.max_ctx) ? V[i] : -INFINITY;
-    y[m] = (okb[m] && i <= q) ? D[q - i] : 0.0f;
-    s0[m] = okb[m] ? sc[size_t(k) * kBlock + l] : 0.0f;
+    const size_t here = size_t(k) * kBlock;
+    x[m] = ld(V, okb[m] && i < v.max_ctx, size_t(i), -INFINITY);
+    y[m] = ld(D, okb[m] && i <= q, size_t(q - i), 0.0f);
+    sv[m][0] = ld(sc, okb[m], here + l, 0.0f);
+    if (kReplay) {
+      const int i0 = j * kBlock - 1 - l;
+      const bool edge = okb[m] && !prv[m] && l < a && i0 <= q;
+      yb[m] = ld(D, edge, size_t(q - i0), 0.0f);
+#pragma unroll
+      for (int r = 1; r < RM; ++r) {
+        if (r <= a) {
+          const size_t rb = size_t(r) * rstride + here;
+          sv[m][r] = ld(sc, okb[m] && i <= q + r, rb + l, 0.0f);
+          const int t = l + r;
+          sd[m][r] = ld(sc, okb[m] && i <= q && (t < kBlock || nxt[m]), rb + t, 0.0f);
+          const int tb = i0 + r - j * kBlock;
+          sb[m][r] = ld(sc, edge && tb >= 0, rb + tb, 0.0f);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
@@ -95,22 +136,19 @@ __device__ __forceinline__ void update_wave(const SpinView& v, int layer, const 
   for (int m = 0; m < NB; ++m) {
     if (!okb[m]) continue;
     const int j = jj[m + 1];
-    const int k = k0 + m;
-    const bool next_kept = jj[m + 2] == j + 1 && k + 1 < cnt;
-    const bool prev_kept = jj[m] == j - 1 && k > 0;
-    const size_t here = size_t(k) * kBlock;
     const int i = j * kBlock + l;
 
-    // V of slot i, rows 0..a in order (row 0's score is already loaded)
+    // V of slot i, rows 0..a in order
     float xv = x[m];
     bool changed = false;
     if (i <= q) {
-      xv = ema_observe(xv, s0[m], alpha, beta);
+      xv = ema_observe(xv, sv[m][0], alpha, beta);
       changed = true;
     }
-    for (int r = 1; r <= a; ++r) {
-      if (i <= q + r) {
-        xv = ema_observe(xv, sc[r * rstride + here + l], alpha, beta);
+#pragma unroll
+    for (int r = 1; r < RM; ++r) {
+      if (r <= a && i <= q + r) {
+        xv = ema_observe(xv, sv[m][r], alpha, beta);
         changed = true;
       }
     }
@@ -120,27 +158,21 @@ __device__ __forceinline__ void update_wave(const SpinView& v, int layer, const 
 
     // D at offset q - i for row-0 slot i (rows reach i + r)
     if (i <= q) {
-      float yv = ema_observe(y[m], s0[m], alpha, beta);
-      for (int r = 1; r <= a; ++r) {
-        const int t = l + r;
-        if (t < kBlock)
-          yv = ema_observe(yv, sc[r * rstride + here + t], alpha, beta);
-        else if (next_kept)
-          yv = ema_observe(yv, sc[r * rstride + here + t], alpha, beta);
-      }
+      float yv = ema_observe(y[m], sv[m][0], alpha, beta);
+#pragma unroll
+      for (int r = 1; r < RM; ++r)
+        if (r <= a && (l + r < kBlock || nxt[m])) yv = ema_observe(yv, sd[m][r], alpha, beta);
       D[q - i] = yv;
     }
     // offsets whose row-0 slot lies just before block j, in a block not kept
-    if (!prev_kept && l < a) {
+    if (kReplay && !prv[m] && l < a) {
       const int i0 = j * kBlock - 1 - l;
       if (i0 <= q) {
-        const int o = q - i0;
-        float yv = D[o];
-        for (int r = 0; r <= a; ++r) {
-          const int t = i0 + r - j * kBlock;
-          if (t >= 0) yv = ema_observe(yv, sc[r * rstride + here + t], alpha, beta);
-        }
-        D[o] = yv;
+        float yv = yb[m];
+#pragma unroll
+        for (int r = 1; r < RM; ++r)
+          if (r <= a && i0 + r - j * kBlock >= 0) yv = ema_observe(yv, sb[m][r], alpha, beta);
+        D[q - i0] = yv;
       }
     }
   }
