@@ -88,9 +88,10 @@ __device__ __forceinline__ void update_wave(const SpinView& v, int layer, const 
   // needed reads element 0; a conditional load would make the join after it
   // wait for every load in flight), and each value is used only under the
   // condition it was loaded under.  The single-row update keeps conditional
-  // loads: measured in the round, its faster unconditional form left more of
-  // its written lines to reach HBM during the next round's indexer, which
-  // then took about as much longer as the update saved.
+  // loads: measured in the decode round, its unconditional form ran faster
+  // alone, but the next round's indexer then took about as much longer as the
+  // update saved (more of the update's written lines still on their way to
+  // HBM when the key stream starts, by the look of it).
   auto ld = [](const float* p, bool ok, size_t idx, float none) {
     if (kReplay) return p[ok ? idx : 0];
     return ok ? p[idx] : none;
