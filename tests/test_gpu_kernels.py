@@ -439,6 +439,83 @@ def test_update_and_replay_parity(gpu_lib, R):
     assert rig.state.error() == 0
 
 
+
+@pytest.mark.parametrize("R", [2, 4])
+def test_replay_every_acceptance_and_kept_pattern(gpu_lib, R):
+    """Prefix-valid replay with every acceptance 0..R-1 against kept lists that
+    put every neighbour case at every position of a wave's four entries:
+    alternate blocks (each kept block's predecessor skipped, so its owner also
+    takes the offsets just before it), runs of two and three, all blocks, and
+    a random half; positions at, just past and just before block boundaries."""
+    rng = np.random.default_rng(70 + R)
+    B, ctx = 8, 64 * 48
+    mb = nblocks(ctx - 1)
+    cfg = spin.make_config(1, B, ctx, 256, max_rows=R, alpha=0.75)
+    rig = Rig(cfg, B, R, mb)
+    qpos = np.array([64 * 40, 64 * 40 + 1, 64 * 41 - 1, 64 * 41 - 2, 64 * 33 + 31,
+                     64 * 44 + 7, 64 * 45 - R, 64 * 30 + 62], dtype=np.int64)
+    qpos = np.minimum(qpos, ctx - R)
+    acc = np.array([b % R for b in range(B)], dtype=np.int32)
+    states, kept = [], []
+    for b in range(B):
+        V = np_(random_state(ctx, 0.3, seed=b + 300)).astype(np.float32).astype(np.float64)
+        D = np_(random_state(ctx, 0.3, seed=b + 400)).astype(np.float32).astype(np.float64)
+        V[qpos[b] + 1:] = NEG
+        rig.inject(0, b, V, D, 2)
+        n = nblocks(qpos[b] + R - 1)
+        kind = b % 4
+        if kind == 0:
+            k = np.arange(0, n, 2)                               # alternate blocks
+        elif kind == 1:
+            k = np.array([j for j in range(n) if j % 5 in (0, 1, 3)])   # runs of 2 and 1
+        elif kind == 2:
+            k = np.arange(n)                                     # every block
+        else:
+            k = np.sort(rng.choice(n, size=max(1, n // 2), replace=False))
+        k = np.union1d(k, [n - 1])
+        kept.append(k)
+        states.append((V, D))
+    kt = np.full((B, mb), -1, dtype=np.int32)
+    for b in range(B):
+        kt[b, : len(kept[b])] = kept[b]
+    rig.kept.copy_(torch.as_tensor(kt))
+    rig.kept_count.copy_(torch.as_tensor([len(k) for k in kept], dtype=torch.int32))
+    sc = (rng.random((B, R, mb * 64)) * 20).astype(np.float32)
+    for b in range(B):
+        slot = (kept[b][:, None] * 64 + np.arange(64)).reshape(-1)
+        for r in range(R):
+            row = sc[b, r, : len(slot)]
+            row[slot > qpos[b] + r] = NEG
+    rig.scores.copy_(torch.as_tensor(sc))
+    rig.set_qpos(qpos)
+    _say("replay R", R, "accepted", acc.tolist())
+    spin.spin_mtp_replay(rig.h, 0, rig.batch, torch.as_tensor(acc, device=DEV), rig.scores,
+                         rig.kept, rig.kept_count)
+    torch.cuda.synchronize()
+    for b in range(B):
+        V, D = states[b][0].copy(), states[b][1].copy()
+        O.ema_update(V, D, sc[b, :, : len(kept[b]) * 64].astype(np.float64), kept[b], int(qpos[b]),
+                     int(acc[b]), 0.75)
+        gV, gD, gVB, gstep = rig.read_state(0, b)
+        for name, g, r in (("V", gV, V), ("D", gD, D)):
+            fin = np.isfinite(r)
+            assert np.array_equal(fin, np.isfinite(g)), (name, b)
+            tol = 1e-3 * np.abs(r[fin]) + 1e-6
+            assert np.all(np.abs(g[fin] - r[fin]) <= tol), (name, b)
+        slot = (kept[b][:, None] * 64 + np.arange(64)).reshape(-1)
+        obs_v = np.zeros(ctx, dtype=bool)
+        obs_d = np.zeros(ctx, dtype=bool)
+        for r in range(int(acc[b]) + 1):
+            i = slot[slot <= qpos[b] + r]
+            obs_v[i] = True
+            obs_d[qpos[b] + r - i] = True
+        assert np.array_equal(gV[~obs_v], states[b][0][~obs_v]), b
+        assert np.array_equal(gD[~obs_d], states[b][1][~obs_d]), b
+        vb = np.concatenate([gV, np.full(mb * 64 - len(gV), NEG)]).reshape(mb, 64).max(1)
+        assert np.array_equal(gVB[kept[b]], vb[kept[b]]), b
+        assert gstep == 3
+    assert rig.state.error() == 0
+
 def test_measure_miss_parity(gpu_lib):
     rng = np.random.default_rng(7)
     B, R, mb, K = 3, 2, 50, 300
