@@ -640,8 +640,10 @@ k_topk_fused(spin_batch bt, int K, const float* scores, const float* page_qmax,
   // An empty asm that clobbers v127 makes the kernel allocate 128 registers per
   // thread: its 16 waves then fill the CU's register files (4 waves x 128 of
   // 512 per SIMD), so no workgroup of the kernel beside the top-k (the EMA
-  // update, 44 registers) lands on a top-k CU and takes its issue slots; the
-  // two then share only HBM.
+  // update: 34 registers, 104 replaying) lands on a top-k CU and takes its
+  // issue slots; the two then share only HBM.  (Without it the kernel
+  // allocates 123 as compiled now; the clobber keeps the bound whatever the
+  // compiler does.)
   asm volatile("" ::: "v127");
   __shared__ FusedShared sh;
   if (arrivals && threadIdx.x == 0)
